@@ -1,0 +1,339 @@
+/*
+ * uzip_oracle.c -- plain, slow, obviously-correct CPU oracle for the
+ * split-exponent lossless BF16 codec.
+ *
+ * THIS IS TEST INFRASTRUCTURE. Only the test suite, the package's smoke check
+ * and the benchmark's CPU-baseline leg may load it. The product path (the HIP
+ * library) never calls, links or includes anything from this directory, and
+ * this file includes nothing from the product.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [SZ]  "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+ *         Serving" (xllm-io paper review), section 3.2 (split/merge formulas,
+ *         4-bit Top-16 codes two per byte, escapes as a 16-bit in-chunk position
+ *         plus the raw 8-bit exponent, size B = N + N/2 + 3M), section 3.3
+ *         (offline calibration: histogram, Top-16, three lookup tables),
+ *         section 3.4 (all 16 codes are real exponents; escapes carry a dummy
+ *         code and are overwritten from the position list).
+ *   [UZ]  "UCCL-Zip: Lossless Compression Supercharged GPU Communication",
+ *         section 3.4 / Figure 6: a receiver decompresses a slice, reduces it
+ *         with its own slice, and recompresses the result.
+ *
+ * Readings where the pages leave a point open (each is the plainest reading;
+ * the same list stands in the design notes):
+ *   - code k is the k-th most frequent exponent, ties to the smaller exponent;
+ *     fewer than 16 non-zero bins are filled with zero-count exponents in
+ *     ascending order;
+ *   - the dummy code of an escape is 0;
+ *   - element 2j sits in the low nibble of code byte j, 2j+1 in the high one;
+ *     an odd N leaves the last high nibble 0;
+ *   - escapes are stored as two arrays (all u16 positions, then all u8 raw
+ *     exponents), chunk by chunk, ascending position inside a chunk, with a
+ *     u32 exclusive offset per chunk plus the total at the end;
+ *   - stream = 256-byte header, then the sign-mantissa, code, offset, position
+ *     and value sections, each starting at a multiple of 256 bytes, padding 0;
+ *   - reduce: one IEEE binary32 add of the two decoded values (round to
+ *     nearest even, subnormals kept), then round-half-to-even to BF16; a NaN
+ *     sum becomes 0x7FC0 (this last choice is ours: parity unpinned by the
+ *     pages).
+ *
+ * Everything here is scalar C on 16-bit words; floats appear only in the
+ * reduce's binary32 add. Build: gcc -O2 -std=c99 -ffp-contract=off (no
+ * -ffast-math: the add must be IEEE).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+#define ORC_HEADER 256u
+
+/* ---------------------------------------------------------------- split -- */
+/* [SZ] section 3.2: exponent e = (x >> 7) & 0xff, sign-mantissa byte
+ * a = ((x >> 8) & 0x80) | (x & 0x7f). */
+uint8_t orc_exponent(uint16_t x) { return (uint8_t)((x >> 7) & 0xffu); }
+uint8_t orc_signmant(uint16_t x) { return (uint8_t)(((x >> 8) & 0x80u) | (x & 0x7fu)); }
+
+/* [SZ] section 3.2: x = ((a & 0x80) << 8) | (e << 7) | (a & 0x7f). */
+uint16_t orc_merge(uint8_t a, uint8_t e)
+{
+    return (uint16_t)((((unsigned)a & 0x80u) << 8) | ((unsigned)e << 7) | ((unsigned)a & 0x7fu));
+}
+
+/* ------------------------------------------------------------ histogram -- */
+/* [SZ] section 3.3: count every exponent of the calibration set. Adds into
+ * hist (the caller zeroes it), so two sets can be pooled. */
+void orc_histogram(const uint16_t *x, uint64_t n, uint64_t *hist)
+{
+    for (uint64_t i = 0; i < n; i++)
+        hist[orc_exponent(x[i])] += 1;
+}
+
+/* --------------------------------------------------------------- Top-16 -- */
+/* [SZ] section 3.3: pick the 16 most frequent exponents and build the three
+ * tables. Order: count descending, then exponent ascending, over all 256
+ * values (zero counts included). Plain selection: 16 rounds, each taking the
+ * best exponent not yet taken. */
+void orc_top16(const uint64_t *hist, uint8_t *dec, uint8_t *enc, uint8_t *member)
+{
+    int taken[256];
+    for (int e = 0; e < 256; e++) { taken[e] = 0; enc[e] = 0; member[e] = 0; }
+    for (int k = 0; k < 16; k++) {
+        int best = -1;
+        for (int e = 0; e < 256; e++) {
+            if (taken[e]) continue;
+            if (best < 0 || hist[e] > hist[best]) best = e;   /* strict: ties keep smaller e */
+        }
+        taken[best] = 1;
+        dec[k] = (uint8_t)best;
+        enc[best] = (uint8_t)k;
+        member[best] = 1;
+    }
+}
+
+/* code of exponent e under dec[], or -1 if e is not in the codebook
+ * (linear search: independent of any lookup table). */
+static int orc_code_of(const uint8_t *dec, uint8_t e)
+{
+    for (int k = 0; k < 16; k++)
+        if (dec[k] == e) return k;
+    return -1;
+}
+
+/* ---------------------------------------------------------------- sizes -- */
+static uint64_t orc_align(uint64_t v) { return (v + 255u) & ~(uint64_t)255u; }
+
+typedef struct {
+    uint64_t sm, codes, offs, pos, val, total;
+} orc_layout;
+
+static uint64_t orc_nchunks(uint64_t n, uint32_t C) { return (n + C - 1) / C; }
+
+static orc_layout orc_layout_of(uint64_t n, uint32_t C, uint64_t m)
+{
+    orc_layout L;
+    uint64_t nch = orc_nchunks(n, C);
+    L.sm = ORC_HEADER;
+    L.codes = L.sm + orc_align(n);
+    L.offs = L.codes + orc_align((n + 1) / 2);
+    L.pos = L.offs + orc_align(4 * (nch + 1));
+    L.val = L.pos + orc_align(2 * m);
+    L.total = L.val + m;
+    return L;
+}
+
+/* Worst-case stream size: every element an escape. */
+uint64_t orc_max_bytes(uint64_t n, uint32_t C)
+{
+    if (n == 0 || C == 0) return 0;
+    return orc_layout_of(n, C, n).total;
+}
+
+/* [SZ] section 3.2: payload bytes N + N/2 + 3M (N/2 rounded up for odd N). */
+uint64_t orc_payload_bytes(uint64_t n, uint64_t m) { return n + (n + 1) / 2 + 3 * m; }
+
+static void put_u16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static void put_u32(uint8_t *p, uint32_t v) { for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static void put_u64(uint8_t *p, uint64_t v) { for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i)); }
+static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static uint32_t get_u32(const uint8_t *p) { uint32_t v = 0; for (int i = 3; i >= 0; i--) v = (v << 8) | p[i]; return v; }
+static uint64_t get_u64(const uint8_t *p) { uint64_t v = 0; for (int i = 7; i >= 0; i--) v = (v << 8) | p[i]; return v; }
+
+/* --------------------------------------------------------------- encode -- */
+/* [SZ] section 3.2, the two encode stages in the page's order:
+ *  (1) dense transform: keep every sign-mantissa byte, look each exponent up
+ *      in the codebook and pack two 4-bit codes per byte (escapes: dummy 0);
+ *  (2) scan the raw exponents chunk by chunk and append every exponent that
+ *      is not in the codebook to the escape arrays (in-chunk position, raw
+ *      exponent).
+ * Returns the stream size, or 0 if an argument is bad or cap is too small
+ * for the worst case. */
+uint64_t orc_encode(const uint16_t *x, uint64_t n, uint32_t C, const uint8_t *dec,
+                    uint8_t *out, uint64_t cap)
+{
+    if (n == 0 || C == 0 || C > 65536u || n >= ((uint64_t)1 << 32)) return 0;
+    if (cap < orc_max_bytes(n, C)) return 0;
+
+    /* count escapes first so the section offsets are known */
+    uint64_t m = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if (orc_code_of(dec, orc_exponent(x[i])) < 0) m++;
+    orc_layout L = orc_layout_of(n, C, m);
+    memset(out, 0, L.total);
+
+    /* stage (1): dense sections */
+    for (uint64_t i = 0; i < n; i++) {
+        out[L.sm + i] = orc_signmant(x[i]);
+        int k = orc_code_of(dec, orc_exponent(x[i]));
+        unsigned code = (k < 0) ? 0u : (unsigned)k;
+        if (i % 2 == 0) out[L.codes + i / 2] |= (uint8_t)code;
+        else            out[L.codes + i / 2] |= (uint8_t)(code << 4);
+    }
+
+    /* stage (2): escapes, chunk by chunk, ascending position */
+    uint64_t nch = orc_nchunks(n, C);
+    uint64_t j = 0;
+    for (uint64_t c = 0; c < nch; c++) {
+        put_u32(out + L.offs + 4 * c, (uint32_t)j);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t e = orc_exponent(x[i]);
+            if (orc_code_of(dec, e) < 0) {
+                put_u16(out + L.pos + 2 * j, (uint16_t)(i - lo));
+                out[L.val + j] = e;
+                j++;
+            }
+        }
+    }
+    put_u32(out + L.offs + 4 * nch, (uint32_t)j);
+
+    /* header */
+    out[0] = 0x55; out[1] = 0x5A; out[2] = 0x42; out[3] = 0x31;   /* "UZB1" */
+    put_u16(out + 4, 1);
+    put_u16(out + 6, 0);
+    put_u32(out + 8, C);
+    put_u32(out + 12, 0);
+    put_u64(out + 16, n);
+    put_u64(out + 24, m);
+    put_u64(out + 32, L.total);
+    memcpy(out + 40, dec, 16);
+    return L.total;
+}
+
+/* --------------------------------------------------------------- decode -- */
+/* [SZ] section 3.2: unpack both nibbles of every code byte, look the code up
+ * in the 16-entry table and rebuild each word with its sign-mantissa byte;
+ * then overwrite each escape's exponent with the recorded raw exponent.
+ * Returns 0, or -1 on a bad argument or a stream that does not match. */
+int orc_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint32_t C,
+               const uint8_t *dec, uint16_t *y)
+{
+    if (in_bytes < ORC_HEADER || n == 0 || C == 0) return -1;
+    if (get_u64(in + 16) != n || get_u32(in + 8) != C) return -1;
+    if (memcmp(in + 40, dec, 16) != 0) return -1;
+    uint64_t m = get_u64(in + 24);
+    orc_layout L = orc_layout_of(n, C, m);
+    if (in_bytes < L.total) return -1;
+
+    for (uint64_t i = 0; i < n; i++) {
+        uint8_t byte = in[L.codes + i / 2];
+        unsigned code = (i % 2 == 0) ? (byte & 0x0fu) : (byte >> 4);
+        y[i] = orc_merge(in[L.sm + i], dec[code]);
+    }
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        if (j1 < j0 || j1 > m) return -1;
+        for (uint32_t j = j0; j < j1; j++) {
+            uint64_t i = c * C + get_u16(in + L.pos + 2 * (uint64_t)j);
+            if (i >= n) return -1;
+            y[i] = orc_merge(in[L.sm + i], in[L.val + j]);
+        }
+    }
+    return 0;
+}
+
+/* --------------------------------------------------------------- reduce -- */
+/* BF16 word -> binary32: the 16 bits become the high half. */
+static float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* binary32 bits -> BF16, round half to even on the 16 dropped bits.
+ * NaN -> 0x7FC0. A carry out of the mantissa moves into the exponent, which
+ * turns the largest finite values into infinity when they round up. */
+uint16_t orc_bf16_rne(uint32_t u)
+{
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0) return 0x7FC0;
+    uint32_t hi = u >> 16, lo = u & 0xffffu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;
+    return (uint16_t)hi;
+}
+
+/* One element of the reduce: binary32 sum of the two values, then BF16. */
+uint16_t orc_add_bf16(uint16_t a, uint16_t b)
+{
+    volatile float s = orc_bf16_to_f32(a) + orc_bf16_to_f32(b);
+    float sv = s;
+    uint32_t u;
+    memcpy(&u, &sv, 4);
+    return orc_bf16_rne(u);
+}
+
+/* [UZ] section 3.4: decode both compressed inputs, add element-wise, and
+ * encode the result with the same codebook and chunk size. tmp must hold 3n
+ * words of scratch. Returns the output stream size or 0. */
+uint64_t orc_reduce_add(const uint8_t *a, uint64_t a_bytes, const uint8_t *b, uint64_t b_bytes,
+                        uint64_t n, uint32_t C, const uint8_t *dec,
+                        uint8_t *out, uint64_t cap, uint16_t *tmp)
+{
+    uint16_t *ya = tmp, *yb = tmp + n, *r = tmp + 2 * n;
+    if (orc_decode(a, a_bytes, n, C, dec, ya) != 0) return 0;
+    if (orc_decode(b, b_bytes, n, C, dec, yb) != 0) return 0;
+    for (uint64_t i = 0; i < n; i++) r[i] = orc_add_bf16(ya[i], yb[i]);
+    return orc_encode(r, n, C, dec, out, cap);
+}
+
+/* ------------------------------------------------------------- validate -- */
+/* Full structural check of a stream against the caller's codebook.
+ * 0 = ok, -3 = malformed, -4 = codebook differs. */
+int orc_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
+{
+    if (in_bytes < ORC_HEADER) return -3;
+    if (!(in[0] == 0x55 && in[1] == 0x5A && in[2] == 0x42 && in[3] == 0x31)) return -3;
+    if (get_u16(in + 4) != 1 || get_u16(in + 6) != 0 || get_u32(in + 12) != 0) return -3;
+    uint32_t C = get_u32(in + 8);
+    uint64_t n = get_u64(in + 16), m = get_u64(in + 24), total = get_u64(in + 32);
+    if (C == 0 || C > 65536u || n == 0 || n >= ((uint64_t)1 << 32) || m > n) return -3;
+    for (int i = 56; i < 256; i++) if (in[i] != 0) return -3;
+    orc_layout L = orc_layout_of(n, C, m);
+    if (total != L.total || in_bytes < L.total) return -3;
+    if (memcmp(in + 40, dec, 16) != 0) return -4;
+    /* codebook entries must be 16 distinct exponents */
+    for (int k = 0; k < 16; k++)
+        for (int q = k + 1; q < 16; q++)
+            if (dec[k] == dec[q]) return -3;
+    /* padding bytes are zero */
+    for (uint64_t p = L.sm + n; p < L.codes; p++) if (in[p]) return -3;
+    if (n % 2 == 1 && (in[L.codes + n / 2] >> 4) != 0) return -3;
+    for (uint64_t p = L.codes + (n + 1) / 2; p < L.offs; p++) if (in[p]) return -3;
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t p = L.offs + 4 * (nch + 1); p < L.pos; p++) if (in[p]) return -3;
+    for (uint64_t p = L.pos + 2 * m; p < L.val; p++) if (in[p]) return -3;
+    /* offsets: start at 0, never decrease, end at m, fit their chunk */
+    if (get_u32(in + L.offs) != 0 || get_u32(in + L.offs + 4 * nch) != m) return -3;
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        uint64_t len = (c + 1) * C <= n ? C : n - c * C;
+        if (j1 < j0 || (uint64_t)(j1 - j0) > len) return -3;
+        for (uint32_t j = j0; j < j1; j++) {
+            uint16_t p = get_u16(in + L.pos + 2 * (uint64_t)j);
+            if (p >= len) return -3;
+            if (j > j0 && p <= get_u16(in + L.pos + 2 * (uint64_t)(j - 1))) return -3;
+            if (orc_code_of(dec, in[L.val + j]) >= 0) return -3;   /* escape must be outside the codebook */
+            uint64_t i = c * C + p;
+            uint8_t byte = in[L.codes + i / 2];
+            unsigned code = (i % 2 == 0) ? (byte & 0x0fu) : (byte >> 4);
+            if (code != 0) return -3;                               /* dummy code is 0 */
+        }
+    }
+    return 0;
+}
+
+/* Header reads, for tests. */
+uint64_t orc_stream_m(const uint8_t *in) { return get_u64(in + 24); }
+uint64_t orc_stream_total(const uint8_t *in) { return get_u64(in + 32); }
+
+/* Array forms of the reduce arithmetic, for sweeps in the tests. */
+void orc_bf16_rne_array(const uint32_t *u, uint64_t n, uint16_t *out)
+{
+    for (uint64_t i = 0; i < n; i++) out[i] = orc_bf16_rne(u[i]);
+}
+
+void orc_add_bf16_array(const uint16_t *a, const uint16_t *b, uint64_t n, uint16_t *r)
+{
+    for (uint64_t i = 0; i < n; i++) r[i] = orc_add_bf16(a[i], b[i]);
+}

@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one. Each mutant is a one-token change (a shift, a sign, an index,
+a comparison, a dropped rounding term); it is compiled on the CPU into a
+temporary library and the oracle pin tests run against it in a subprocess.
+A mutant that passes every pin would mean the pins cannot tell that mistake
+from the correct oracle.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "uzip_oracle.c")
+
+MUTANTS = {
+    "exponent_shift": ("return (uint8_t)((x >> 7) & 0xffu);", "return (uint8_t)((x >> 8) & 0xffu);"),
+    "signmant_sign_bit": ("(((x >> 8) & 0x80u) | (x & 0x7fu))", "(((x >> 9) & 0x80u) | (x & 0x7fu))"),
+    "merge_sign_shift": ("(((unsigned)a & 0x80u) << 8)", "(((unsigned)a & 0x80u) << 7)"),
+    "tie_to_larger_exponent": ("hist[e] > hist[best]", "hist[e] >= hist[best]"),
+    "nibble_order": ("if (i % 2 == 0) out[L.codes + i / 2] |= (uint8_t)code;",
+                     "if (i % 2 == 1) out[L.codes + i / 2] |= (uint8_t)code;"),
+    "dummy_code_15": ("unsigned code = (k < 0) ? 0u : (unsigned)k;",
+                      "unsigned code = (k < 0) ? 15u : (unsigned)k;"),
+    "global_positions": ("put_u16(out + L.pos + 2 * j, (uint16_t)(i - lo));",
+                         "put_u16(out + L.pos + 2 * j, (uint16_t)(i));"),
+    "inclusive_offsets": ("put_u32(out + L.offs + 4 * c, (uint32_t)j);",
+                          "put_u32(out + L.offs + 4 * c, (uint32_t)(j + 1));"),
+    "rne_ties_away": ("if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;",
+                      "if (lo >= 0x8000u) hi += 1;"),
+    "rne_truncate": ("if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1;", ";"),
+    "add_becomes_sub": ("orc_bf16_to_f32(a) + orc_bf16_to_f32(b)", "orc_bf16_to_f32(a) - orc_bf16_to_f32(b)"),
+    "nan_payload_kept": ("return 0x7FC0;", "return (uint16_t)(u >> 16);"),
+    "section_alignment": ("return (v + 255u) & ~(uint64_t)255u;", "return (v + 127u) & ~(uint64_t)127u;"),
+    "patch_drops_signmant": ("y[i] = orc_merge(in[L.sm + i], in[L.val + j]);",
+                             "y[i] = orc_merge(0, in[L.val + j]);"),
+    "validate_equal_positions": ("if (j > j0 && p <= get_u16", "if (j > j0 && p < get_u16"),
+    "validate_skips_nibble": ("if (code != 0) return -3;", "if (code > 15) return -3;"),
+}
+
+PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py"]
+
+
+def _run(name, a, b, tmp):
+    src = open(SRC).read()
+    assert src.count(a) >= 1, name
+    path = os.path.join(tmp, f"{name}.c")
+    lib = os.path.join(tmp, f"lib{name}.so")
+    open(path, "w").write(src.replace(a, b, 1))
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-o", lib, path],
+                   check=True)
+    env = dict(os.environ, UZIP_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-m", "not gpu and not slow", *PIN_TESTS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_every_planted_mistake_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            futs = [ex.submit(_run, n, a, b, tmp) for n, (a, b) in MUTANTS.items()]
+            results = dict(f.result() for f in futs)
+    survivors = [n for n, rc in results.items() if rc == 0]
+    assert not survivors, f"mutants not caught by any pin: {survivors}"
+    # rc 1 = tests failed; anything else (2 = collection error) is not a catch
+    assert all(rc == 1 for rc in results.values()), results
