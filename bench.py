@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the split-exponent BF16 codec on one MI355X.
+
+Workload: the 2^28-value KV cache [K/V 2, layers 64, tokens 2048, kv_heads 8,
+head_dim 128], drawn by the seeded recipe in workloads.config_3 (per-layer
+log-uniform scale, per-channel log-normal scale, K bias). The codebook is
+calibrated on layer 0 of the same recipe drawn from another seed. Chunk 1024.
+
+A step is one round trip of the whole tensor: encode (dense pass, tile scan,
+escape placement), then decode (fused dense decode + sparse patch). The input
+and every buffer are resident in HBM before timing starts. Calibration runs
+once, offline, before the timed region: the SplitZip page (section 3.3) moves
+it out of the online path. Its time is reported separately, as is the fused
+decode-add-reencode reduce on two such tensors.
+
+Before timing, the GPU stream is compared byte for byte with the CPU oracle's,
+and the round trip is checked bit for bit.
+
+Output: one JSON line on stdout. value = uncompressed BF16 bytes (2N) per
+second of a round-trip step, in GB/s (1e9). Per-op rates, the compression
+ratio, the escape rate, the per-kernel HIP-event durations and the roofline of
+the dominant kernel are extra fields.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n, C, m):
+    """Bytes the method must move (uncompressed in/out, compressed sections)."""
+    nch = (n + C - 1) // C
+    comp = n + (n + 1) // 2 + 3 * m + 4 * (nch + 1) + 256
+    return {
+        "encode": 2 * n + comp,                 # read words, write stream
+        "decode": comp + 2 * n,                 # read stream, write words
+        "k_encode_tile": 2 * n + n + (n + 1) // 2,
+        "k_decode_tile": comp + 2 * n,
+    }
+
+
+def entropy_bits(hist):
+    p = hist[hist > 0].astype(np.float64) / hist.sum()
+    return float(-(p * np.log2(p)).sum())
+
+
+def cpu_baseline(x_np, calib_np, C, budget_s=12.0, sample=1 << 24):
+    """The CPU oracle (single thread, plain C) on a bounded sample."""
+    import oracle
+    xs = np.ascontiguousarray(x_np[:sample])
+    cb = oracle.calibrate(calib_np)
+    reps, t_enc, t_dec = 0, 0.0, 0.0
+    t_start = time.perf_counter()
+    while reps < 5 and (reps == 0 or time.perf_counter() - t_start < budget_s):
+        t0 = time.perf_counter()
+        s = oracle.encode(xs, C, cb.dec)
+        t1 = time.perf_counter()
+        y = oracle.decode(s, xs.size, C, cb.dec)
+        t2 = time.perf_counter()
+        assert np.array_equal(y, xs)
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        reps += 1
+    gb = 2 * xs.size * reps / 1e9
+    return {
+        "value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s",
+        "cores": 1, "kind": "oracle",
+        "sample": f"first {xs.size} values of the same workload, {reps} round trips "
+                  f"(encode {gb / t_enc:.4f} GB/s, decode {gb / t_dec:.4f} GB/s)",
+        "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4),
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-oracle-check", action="store_true")
+    ap.add_argument("--no-reduce", action="store_true")
+    ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the codec shards by chunk with no cross-GPU exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from lossless_bf16_tensor_amd import uzip
+
+    uzip.lib()                       # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    C = args.chunk
+
+    log("generating workload")
+    w = workloads.config(3, small=args.small)
+    x_np = w.x
+    n = x_np.size
+    log(f"workload {w.name}: n={n}")
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev)
+    cal = torch.from_numpy(w.calib.view(np.int16)).to(dev)
+    stream = torch.cuda.current_stream()
+
+    # --- calibration (offline step; timed on its own) ---
+    cb = uzip.calibrate(cal)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        cb = uzip.calibrate(cal)
+    t_cal = (time.perf_counter() - t0) / 5
+    hist = np.array(list(cb.hist), dtype=np.uint64)
+
+    out = torch.empty(uzip.max_bytes(n, C), dtype=torch.uint8, device=dev)
+    ws = torch.empty(uzip.workspace_bytes(n, C), dtype=torch.uint8, device=dev)
+    y = torch.empty(n, dtype=torch.int16, device=dev)
+
+    # --- correctness gate: oracle stream and bit-exact round trip ---
+    uzip.encode(x, cb, C, out=out, ws=ws)
+    total, m = uzip.stream_bytes(out)
+    uzip.decode(out, cb, n, C, out=y, in_bytes=total)
+    torch.cuda.synchronize()
+    round_trip = bool(torch.equal(y, x))
+    parity = None
+    if not args.no_oracle_check:
+        import oracle
+        log("oracle check")
+        ocb = oracle.calibrate(w.calib)
+        assert list(cb.dec) == ocb.dec.tolist(), "codebook differs from the oracle"
+        want = oracle.encode(x_np, C, ocb.dec)
+        parity = bool(want.size == total and np.array_equal(out[:total].cpu().numpy(), want))
+    if not round_trip or parity is False:
+        log(f"CORRECTNESS FAILURE round_trip={round_trip} parity={parity}")
+        sys.exit(1)
+
+    # --- timed round trips ---
+    def step(ev=None):
+        uzip.encode(x, cb, C, out=out, ws=ws, events=ev[:4] if ev else None)
+        uzip.decode(out, cb, n, C, out=y, in_bytes=total, events=ev[4:] if ev else None)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in evs:                  # torch creates the HIP event on first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    def avg(i, j):
+        return float(np.mean([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)]))
+
+    kern = {
+        "k_encode_tile": avg(0, 1), "k_scan_tiles": avg(1, 2), "k_place_escapes": avg(2, 3),
+        "k_decode_tile": avg(4, 5),
+    }
+    t_enc = avg(0, 3)
+    t_dec = avg(4, 5)
+    ab = algorithmic_bytes(n, C, m)
+    dom = max(("k_encode_tile", "k_decode_tile"), key=lambda k: kern[k])
+    achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
+    enc_gbps = 2 * n / (t_enc * 1e-3) / 1e9
+    dec_gbps = 2 * n / (t_dec * 1e-3) / 1e9
+    rho_payload = 2 * n / (n + (n + 1) // 2 + 3 * m)
+    rho_total = 2 * n / total
+    value = 2 * n / (ms_step * 1e-3) / 1e9
+
+    # --- fused reduce on two tensors of the same workload (K and V halves swapped) ---
+    reduce = None
+    if not args.no_reduce:
+        b = torch.roll(x, shifts=n // 2)
+        outb = torch.empty_like(out)
+        outr = torch.empty_like(out)
+        uzip.encode(b, cb, C, out=outb, ws=ws)
+        tb, _ = uzip.stream_bytes(outb)
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+        for row in rev:
+            for e in row:
+                e.record()
+        for k in range(3):
+            uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws)
+        for k in range(10):
+            uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws, events=rev[k])
+        torch.cuda.synchronize()
+        t_red = float(np.mean([rev[k][0].elapsed_time(rev[k][3]) for k in range(10)]))
+        t_red_k = float(np.mean([rev[k][0].elapsed_time(rev[k][1]) for k in range(10)]))
+        reduce = {"ms": round(t_red, 4), "k_reduce_tile_ms": round(t_red_k, 4),
+                  "GBps_uncompressed_in": round(2 * 2 * n / (t_red * 1e-3) / 1e9, 1),
+                  "inputs": "the workload and the same tensor with its K and V halves swapped"}
+
+    res = {
+        "metric": "encode/decode GB/s (uncompressed BF16) + ratio, 2^28-elt KV, 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: BF16 KV cache {list(w.shape)} = {n} values, "
+                               f"chunk {C}, codebook from layer 0 of another seed",
+                   "n": n, "chunk": C},
+        "encode_GBps": round(enc_gbps, 1), "decode_GBps": round(dec_gbps, 1),
+        "encode_ms": round(t_enc, 4), "decode_ms": round(t_dec, 4),
+        "ratio_payload": round(rho_payload, 4), "ratio_total": round(rho_total, 4),
+        "escape_rate": round(m / n, 6), "coverage": round(1 - m / n, 6), "M": m,
+        "stream_bytes": total, "calib_entropy_bits": round(entropy_bits(hist), 3),
+        "calibrate_ms": round(t_cal * 1e3, 3),
+        "B_hide_GBps": round(min(enc_gbps, dec_gbps) / rho_total, 1),
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "op_roofline_frac": {
+            "encode": round(ab["encode"] / (t_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "decode": round(ab["decode"] / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": ab[dom]},
+        "round_trip_bit_exact": round_trip, "oracle_stream_equal": parity,
+        "reduce": reduce,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(x_np, w.calib, C)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

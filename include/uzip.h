@@ -1,0 +1,203 @@
+/*
+ * uzip.h -- C-ABI of a lossless split-exponent codec for BF16 tensors on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The codec (source: "SplitZip: Ultra Fast Lossless KV Compression for
+ * Disaggregated LLM Serving", xllm-io paper review, section 3.2):
+ * every BF16 word x splits into an exact sign-mantissa byte
+ *     a = ((x >> 8) & 0x80) | (x & 0x7f)
+ * and an 8-bit exponent
+ *     e = (x >> 7) & 0xff.
+ * The 16 most frequent exponents of a calibration set (section 3.3) get 4-bit
+ * codes, packed two per byte. Any other exponent is an escape. It keeps a
+ * dummy code in the dense stream (section 3.4). Its in-chunk position (u16)
+ * and raw exponent (u8) go to per-chunk escape arrays. Payload: N + N/2 + 3M
+ * bytes for N values and M escapes. Decoding looks up all codes in a 16-entry
+ * table, rebuilds the words, then overwrites each escape's exponent.
+ *
+ * Stream format (all little-endian; A(v) = v rounded up to a multiple of 256):
+ *   header   256 bytes:  "UZB1" | u16 version=1 | u16 flags=0 | u32 chunk C |
+ *                        u32 0 | u64 n | u64 M | u64 total_bytes | u8 dec[16] |
+ *                        zeros to byte 256
+ *   sm       at 256                        n bytes       sign-mantissa bytes
+ *   codes    at sm + A(n)                  ceil(n/2)     element 2j -> low nibble
+ *                                                        of byte j, 2j+1 -> high
+ *   offsets  at codes + A(ceil(n/2))       4*(nch+1)     u32 escapes before each
+ *                                                        chunk, then M
+ *   pos      at offsets + A(4*(nch+1))     2*M           u16 in-chunk positions,
+ *                                                        ascending per chunk
+ *   val      at pos + A(2*M)               M             u8 raw exponents
+ *   total_bytes = offset(val) + M; every padding byte is zero.
+ *   nch = ceil(n / C). Escapes carry code 0.
+ *
+ * The code for exponent rank k (count descending, ties to the smaller
+ * exponent) is k.
+ *
+ * Conventions for every call:
+ *   - Device pointers (d_*) are device memory the caller owns. They must be
+ *     16-byte aligned. The library allocates no device memory and keeps no
+ *     state between calls.
+ *   - "async" calls only enqueue work on stream s and return. Their outputs
+ *     are valid once s reaches that point. "blocking" calls synchronise s
+ *     before returning.
+ *   - Arguments are checked on the host before anything is enqueued. A failed
+ *     check returns a negative UZIP_E* code and enqueues nothing.
+ *   - Calls on different streams may run concurrently when their buffers do
+ *     not overlap.
+ *   - 1 <= n < 2^32. chunk C is a power of two in [64, 65536].
+ */
+#ifndef UZIP_H
+#define UZIP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UZIP_VERSION 1u
+
+#define UZIP_OK          0
+#define UZIP_EINVAL     -1   /* null or misaligned pointer, bad n or chunk */
+#define UZIP_ENOSPC     -2   /* output capacity or workspace too small */
+#define UZIP_ECORRUPT   -3   /* stream fails a structural check */
+#define UZIP_ECODEBOOK  -4   /* stream's dec[16] differs from the codebook */
+#define UZIP_EHIP       -5   /* a HIP runtime call or kernel launch failed */
+
+/* Codebook: the three tables of the page's offline calibration (section 3.3)
+ * and the histogram they came from. Plain data, owned by the caller. It is
+ * copied into kernel arguments at each launch.
+ *   dec[k]    exponent of code k (k = 0..15)
+ *   enc[e]    code of exponent e, 0 when e has no code
+ *   member[e] 1 when e has a code, else 0
+ */
+typedef struct uzip_codebook {
+    uint32_t version;          /* UZIP_VERSION */
+    uint8_t  dec[16];
+    uint8_t  enc[256];
+    uint8_t  member[256];
+    uint64_t hist[256];
+    uint64_t n_cal;            /* sum of hist */
+} uzip_codebook_t;
+
+/* Optional per-call settings. A NULL pointer means all defaults.
+ *   events/n_events  If not NULL, the call records events[0] before its first
+ *                    kernel and events[i] after kernel i (i >= 1), up to
+ *                    n_events, all on the call's stream. The caller creates
+ *                    the events. Used to time single kernels.
+ *   flags            UZIP_F_SEPARATE_PATCH: decode with a dense kernel, then a
+ *                    separate sparse patch kernel, instead of the fused
+ *                    kernel. The output is the same.
+ */
+#define UZIP_F_SEPARATE_PATCH 0x1u
+typedef struct uzip_opts {
+    hipEvent_t *events;
+    uint32_t    n_events;
+    uint32_t    flags;
+} uzip_opts_t;
+
+/* ---------------------------------------------------------- host only -- */
+
+/* Largest stream for n values at chunk C: the format above with M = n.
+ * Returns 0 when n or C is invalid. */
+uint64_t uzip_max_bytes(uint64_t n, uint32_t chunk);
+
+/* Device workspace that uzip_encode / uzip_reduce_add need for (n, C): per-tile
+ * escape counts and prefixes, and a staging area for each tile's escapes
+ * (at most 3 bytes per value). Returns 0 when n or C is invalid. */
+uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk);
+
+/* Builds the codebook from a 256-bin exponent histogram (page section 3.3).
+ * Order: count descending, then exponent ascending, over all 256 values.
+ * The first 16 are codes 0..15. Zero-count exponents fill the codebook when
+ * fewer than 16 bins are non-zero. Returns UZIP_OK or UZIP_EINVAL (NULL). */
+int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
+
+/* Full structural check of a stream held in host memory: header fields,
+ * section sizes, zero padding, offsets monotone and ending at M, positions
+ * ascending and inside their chunk, every escape value outside the codebook
+ * with code 0 in the dense stream. Returns UZIP_OK, UZIP_ECORRUPT,
+ * UZIP_ECODEBOOK or UZIP_EINVAL. */
+int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook_t *cb);
+
+/* Parses a 256-byte header in host memory. Any output pointer may be NULL.
+ * Returns UZIP_OK or UZIP_ECORRUPT (bad magic or version). */
+int uzip_parse_header(const void *h_header, uint64_t *n, uint32_t *chunk,
+                      uint64_t *m, uint64_t *total_bytes, uint8_t dec[16]);
+
+/* Static text for an error code (never NULL). */
+const char *uzip_strerror(int code);
+
+/* ------------------------------------------------------------- device -- */
+
+/* async. Adds the exponent histogram of d_x[0..n) to d_hist[256]. The caller
+ * zeroes d_hist first, or keeps earlier counts to pool several sets (page
+ * section 3.3, the histogram step of calibration). */
+int uzip_histogram(const uint16_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s);
+
+/* blocking. Calibrates a codebook on d_x[0..n) (page section 3.3).
+ * It runs the histogram on the device into d_hist_ws (256 x u64 scratch the
+ * caller owns), copies the histogram back, and builds *cb on the host. */
+int uzip_calibrate(const uint16_t *d_x, uint64_t n, uint64_t *d_hist_ws,
+                   uzip_codebook_t *cb, hipStream_t s);
+
+/* async. Encodes d_x[0..n) into d_out with chunk C (page section 3.2: the
+ * dense transform, then the chunked escape arrays).
+ *   d_out    stream buffer of out_cap >= uzip_max_bytes(n, C) bytes. Bytes
+ *            past the stream's total_bytes are left as they were.
+ *   d_ws     workspace of ws_bytes >= uzip_workspace_bytes(n, C) bytes. Its
+ *            contents are scratch and are not preserved.
+ * The stream's size is in its header: see uzip_stream_bytes. */
+int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s);
+int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                   const uzip_opts_t *opts, hipStream_t s);
+
+/* blocking. Reads a device stream's header. Returns its size and M.
+ * Either output pointer may be NULL. */
+int uzip_stream_bytes(const void *d_stream, uint64_t *total_bytes, uint64_t *m, hipStream_t s);
+
+/* async. Decodes a stream of n values at chunk C into d_y[0..n) (page
+ * section 3.2: nibble unpack, 16-entry lookup, merge with the sign-mantissa
+ * byte, then the sparse escape patch). in_bytes is the size of the readable
+ * buffer at d_in (at least the stream's total_bytes). The kernels read
+ * nothing past it and never write past d_y[n-1], whatever the header holds.
+ * A stream that fails uzip_validate gives unspecified output values. n, C
+ * and the codebook must be the ones the stream was encoded with. */
+int uzip_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
+int uzip_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                   const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts,
+                   hipStream_t s);
+
+/* async. Fused decode-add-reencode: the one-GPU share of a compressed
+ * all-reduce hop ("UCCL-Zip: Lossless Compression Supercharged GPU
+ * Communication", section 3.4 / Figure 6: decompress a received slice, reduce
+ * it with the local slice, recompress).
+ *   r[i] = bf16_rne( (float)A[i] + (float)B[i] )
+ * The sum is one IEEE binary32 add (round to nearest even, subnormals kept).
+ * The result rounds half-to-even to BF16. A NaN sum becomes 0x7FC0. A and B
+ * are streams of n values at chunk C under codebook cb. The result is
+ * encoded with the same n, C and cb into d_out (out_cap >= uzip_max_bytes),
+ * with workspace as for uzip_encode. a_bytes and b_bytes bound the reads, as
+ * in_bytes does for uzip_decode. */
+int uzip_reduce_add(const void *d_a, uint64_t a_bytes, const void *d_b, uint64_t b_bytes,
+                    uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                    hipStream_t s);
+int uzip_reduce_add_ex(const void *d_a, uint64_t a_bytes, const void *d_b, uint64_t b_bytes,
+                       uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s);
+
+/* blocking. Copies a device stream of `bytes` bytes to the host and runs
+ * uzip_validate_host on it. */
+int uzip_validate(const void *d_stream, uint64_t bytes, const uzip_codebook_t *cb, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UZIP_H */

@@ -1,0 +1,1114 @@
+// uzip.hip -- HIP kernels (gfx950, wave64) and the C-ABI host library for the
+// split-exponent lossless BF16 codec. The C-ABI is declared in include/uzip.h.
+//
+// Method: "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+// Serving" (xllm-io paper review):
+//   section 3.2: split x into a = ((x>>8)&0x80)|(x&0x7f) and e = (x>>7)&0xff.
+//                Top-16 exponents become 4-bit codes, two per byte. Other
+//                exponents are escapes: u16 in-chunk position + u8 exponent.
+//                Encode = dense transform, then escape arrays. Decode = nibble
+//                unpack + 16-entry lookup + merge, then sparse patch.
+//   section 3.3: offline calibration (histogram, Top-16, three tables).
+//   section 3.4: every code is a real exponent; escapes carry a dummy code.
+// Reduce step: "UCCL-Zip: Lossless Compression Supercharged GPU
+// Communication", section 3.4 / Figure 6 (decompress, reduce, recompress).
+//
+// Kernels:
+//   k_hist          exponent histogram. Per-wave LDS sub-histograms, one
+//                   global 64-bit atomic per bin per workgroup.
+//   k_encode_tile   one pass over the input. 16-byte loads of 8 words per
+//                   lane, and the exponent->code table in LDS. Writes the
+//                   sign-mantissa and code sections. Counts escapes per wave
+//                   with 64-lane ballots, ranks them in element order, and
+//                   stages each tile's escapes (position, exponent) compactly
+//                   in the workspace.
+//   k_scan_tiles    single workgroup: exclusive scan of per-tile escape
+//                   counts -> tile prefixes and M. Writes the header, the last
+//                   chunk offset and the zero padding.
+//   k_place_escapes copies each tile's staged escapes to their final position
+//                   and value slots. Writes the per-chunk offsets.
+//   k_decode_tile   one pass: 16-byte sign-mantissa loads, 8-byte code loads,
+//                   16-entry lookup in registers (v_perm), merge. The tile's
+//                   escapes go into an LDS bitmap and are applied in registers
+//                   before the single store of the output.
+//   k_patch         standalone sparse patch (the two-kernel decode variant).
+//   k_reduce_tile   decodes both inputs of a tile as above, adds in binary32,
+//                   rounds to BF16 (half to even), then encodes like
+//                   k_encode_tile.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "uzip.h"
+
+namespace {
+
+// ------------------------------------------------------------------ layout --
+constexpr uint64_t kHeader = 256;
+
+__host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255u); }
+
+struct Layout {
+    uint64_t n, nch;
+    uint32_t C, logC;
+    uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader
+};
+
+__host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m) { return L.off_pos + align256(2 * m); }
+__host__ __device__ inline uint64_t total_of(const Layout &L, uint64_t m) { return off_val_of(L, m) + m; }
+
+Layout make_layout(uint64_t n, uint32_t C)
+{
+    Layout L;
+    L.n = n;
+    L.C = C;
+    L.logC = 0;
+    while ((1u << L.logC) < C) L.logC++;
+    L.nch = (n + C - 1) / C;
+    L.off_codes = kHeader + align256(n);
+    L.off_offs = L.off_codes + align256((n + 1) / 2);
+    L.off_pos = L.off_offs + align256(4 * (L.nch + 1));
+    return L;
+}
+
+// ------------------------------------------------------------ tile shapes --
+constexpr int kThreads = 256;                 // 4 waves of 64
+constexpr int kEncGroups = 4;                 // groups of 8 words per thread
+constexpr int kEncTile = kThreads * kEncGroups * 8;     // 8192 words
+constexpr int kDecGroups = 2;                 // groups of 16 words per thread
+constexpr int kDecTile = kThreads * kDecGroups * 16;    // 8192 words
+static_assert(kEncTile == kDecTile, "encode and decode tiles share the patch map size");
+constexpr int kTile = kEncTile;
+constexpr int kScanThreads = 1024;
+
+// Encode workspace (see uzip_workspace_bytes).
+struct EncWs {
+    uint32_t *counts;      // [ntiles] escapes per tile
+    uint32_t *tile_pre;    // [ntiles + 1] exclusive prefix, then M
+    uint32_t *chunk_pre;   // [nch] escapes in the tile before each chunk start
+    uint16_t *stage_pos;   // [ntiles * kTile] in-chunk positions, per tile
+    uint8_t  *stage_val;   // [ntiles * kTile] raw exponents, per tile
+};
+
+struct WsLayout {
+    uint64_t counts, tile_pre, chunk_pre, stage_pos, stage_val, total;
+};
+
+WsLayout ws_layout(uint64_t n, uint32_t C)
+{
+    uint64_t ntiles = (n + kTile - 1) / kTile;
+    uint64_t nch = (n + C - 1) / C;
+    WsLayout w;
+    w.counts = 0;
+    w.tile_pre = w.counts + align256(4 * ntiles);
+    w.chunk_pre = w.tile_pre + align256(4 * (ntiles + 1));
+    w.stage_pos = w.chunk_pre + align256(4 * nch);
+    w.stage_val = w.stage_pos + align256(2 * ntiles * kTile);
+    w.total = w.stage_val + align256(ntiles * kTile);
+    return w;
+}
+
+// Per-launch constants of an encoder (kernel argument, by value).
+struct EncParams {
+    uint8_t lut[256];      // code of e in bits 0..3, bit 7 set when e is an escape
+    uint64_t n, nch, ntiles;
+    uint32_t Cmask, logC;
+    uint64_t off_codes, off_offs, off_pos;
+};
+
+// Per-launch constants of a decoder.
+struct DecParams {
+    uint32_t dec[4];       // dec[16] packed little-endian, 4 codes per word
+    uint64_t n, nch;
+    uint32_t C, logC;
+    uint64_t off_codes, off_offs, off_pos;
+};
+
+struct HeaderParams {
+    uint8_t tmpl[256];     // header with M and total_bytes left zero
+    uint64_t n, nch, ntiles;
+    uint64_t off_codes, off_offs, off_pos;
+};
+
+// Native vector types for 8- and 16-byte memory operations.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming loads/stores: every byte is touched once per call.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_stream(T v, T *p) { __builtin_nontemporal_store(v, p); }
+
+// --------------------------------------------------------- bit helpers -----
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b)
+{
+    return (a & mask) | (b & ~mask);
+}
+
+// Sign-mantissa bytes of 4 words held in two dwords (word 2i in the low half).
+__device__ __forceinline__ uint32_t signmant4(uint32_t v0, uint32_t v1)
+{
+    // low byte of each half: bits 0..6 from the word, bit 7 = word bit 15
+    uint32_t t0 = bfi(0x007F007Fu, v0, v0 >> 8);
+    uint32_t t1 = bfi(0x007F007Fu, v1, v1 >> 8);
+    return perm(t1, t0, 0x06040200u);
+}
+
+// Exponent-table entries of 4 consecutive words: byte j = lut[e_j].
+__device__ __forceinline__ uint32_t lut4(const uint8_t *s_lut, uint32_t v0, uint32_t v1)
+{
+    uint32_t b0 = s_lut[(v0 >> 7) & 0xFFu];
+    uint32_t b1 = s_lut[(v0 >> 23) & 0xFFu];
+    uint32_t b2 = s_lut[(v1 >> 7) & 0xFFu];
+    uint32_t b3 = s_lut[(v1 >> 23) & 0xFFu];
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+// Pack the code nibbles of 8 table entries (bytes of L0, L1): word 2j in the
+// low nibble of byte j.
+__device__ __forceinline__ uint32_t pack_codes8(uint32_t L0, uint32_t L1)
+{
+    uint32_t t0 = L0 & 0x0F0F0F0Fu;
+    uint32_t t1 = L1 & 0x0F0F0F0Fu;
+    t0 |= t0 >> 4;
+    t1 |= t1 >> 4;
+    return perm(t1, t0, 0x06040200u);
+}
+
+// Exponents of 4 words from 4 code nibbles held one per byte (values 0..15),
+// through the 16-entry table dec (4 dwords).
+__device__ __forceinline__ uint32_t dec4(const uint32_t dec[4], uint32_t nib)
+{
+    uint32_t sel = nib & 0x07070707u;
+    uint32_t lo = perm(dec[1], dec[0], sel);
+    uint32_t hi = perm(dec[3], dec[2], sel);
+    // pick hi for bytes whose code has bit 3 set: selector byte k -> k or 4+k
+    uint32_t pick = ((nib >> 1) & 0x04040404u) | 0x03020100u;
+    return perm(hi, lo, pick);
+}
+
+// Rebuild 2 words from a dword of interleaved bytes [a0, e0, a1, e1].
+__device__ __forceinline__ uint32_t merge2(uint32_t w)
+{
+    // per half: bits 0..6 = a & 0x7f, bits 7..14 = e, bit 15 = a bit 7
+    uint32_t t = bfi(0x80008000u, w << 8, w);
+    return bfi(0x7F807F80u, w >> 1, t);
+}
+
+// Decode 8 words: sm (8 sign-mantissa bytes in 2 dwords), codes (8 nibbles).
+__device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t codes,
+                                        const uint32_t dec[4], uint32_t y[4])
+{
+    uint32_t lo = codes & 0x0F0F0F0Fu;          // nibbles of words 0,2,4,6
+    uint32_t hi = (codes >> 4) & 0x0F0F0F0Fu;   // nibbles of words 1,3,5,7
+    uint32_t n03 = perm(hi, lo, 0x05010400u);   // [c0, c1, c2, c3]
+    uint32_t n47 = perm(hi, lo, 0x07030602u);   // [c4, c5, c6, c7]
+    uint32_t e03 = dec4(dec, n03);
+    uint32_t e47 = dec4(dec, n47);
+    y[0] = merge2(perm(e03, sm0, 0x05010400u));
+    y[1] = merge2(perm(e03, sm0, 0x07030602u));
+    y[2] = merge2(perm(e47, sm1, 0x05010400u));
+    y[3] = merge2(perm(e47, sm1, 0x07030602u));
+}
+
+// Replace the exponent field of word j (0..1) of a dword.
+__device__ __forceinline__ uint32_t set_exp(uint32_t y, int half, uint32_t e)
+{
+    uint32_t sh = 7 + 16 * half;
+    return (y & ~(0xFFu << sh)) | (e << sh);
+}
+
+// binary32 bits -> BF16, round half to even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(uint32_t u)
+{
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+// Sum of the two BF16 words in each half of a and b.
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
+{
+    float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
+    float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
+    uint32_t r0 = bf16_rne(__float_as_uint(a0 + b0));
+    uint32_t r1 = bf16_rne(__float_as_uint(a1 + b1));
+    return r0 | (r1 << 16);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt()
+{
+    return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+
+// =========================================================== histogram ====
+__global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n,
+                                                   unsigned long long *__restrict__ hist)
+{
+    __shared__ uint32_t sh[kThreads / 64][256];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int i = tid; i < (kThreads / 64) * 256; i += kThreads) (&sh[0][0])[i] = 0;
+    __syncthreads();
+    const uint64_t ngroups = n / 8;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + tid; g < ngroups; g += stride) {
+        const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + 8 * g));
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            atomicAdd(&sh[wave][(w[q] >> 7) & 0xFFu], 1u);
+            atomicAdd(&sh[wave][(w[q] >> 23) & 0xFFu], 1u);
+        }
+    }
+    if (blockIdx.x == 0) {
+        for (uint64_t i = ngroups * 8 + tid; i < n; i += kThreads)
+            atomicAdd(&sh[wave][(x[i] >> 7) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < 256; b += kThreads) {
+        uint32_t s = 0;
+        for (int q = 0; q < kThreads / 64; q++) s += sh[q][b];
+        if (s) atomicAdd(&hist[b], (unsigned long long)s);
+    }
+}
+
+// ============================================================== encode ====
+// Shared encode back end: a thread holds 4 groups of 8 words (group k covers
+// tile words k*2048 + tid*8 .. +8) in xw[k][0..3] and valid counts.
+struct EncShared {
+    uint8_t lut[256];
+    uint32_t wtot[kEncGroups][kThreads / 64];
+};
+
+__device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], uint64_t t0, uint64_t tile,
+                                              uint8_t *__restrict__ out, const EncWs &ws,
+                                              const EncParams &p, EncShared &sh)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t Lw[kEncGroups][2];
+    uint32_t pre[kEncGroups];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        uint32_t L0 = 0, L1 = 0;
+        if (g0 < p.n) {
+            L0 = lut4(sh.lut, xw[k][0], xw[k][1]);
+            L1 = lut4(sh.lut, xw[k][2], xw[k][3]);
+            if (g0 + 8 > p.n) {       // tail group: words past n are not escapes
+                const uint32_t valid = (uint32_t)(p.n - g0);   // 1..7
+                const uint64_t keep = (1ull << (8 * valid)) - 1ull;
+                const uint64_t both = ((uint64_t)L1 << 32 | L0) & keep;
+                L0 = (uint32_t)both;
+                L1 = (uint32_t)(both >> 32);
+            }
+            u32x2 smv;
+            smv.x = signmant4(xw[k][0], xw[k][1]);
+            smv.y = signmant4(xw[k][2], xw[k][3]);
+            st_stream(smv, reinterpret_cast<u32x2 *>(out + kHeader + g0));
+            st_stream(pack_codes8(L0, L1), reinterpret_cast<uint32_t *>(out + p.off_codes + g0 / 2));
+        }
+        Lw[k][0] = L0;
+        Lw[k][1] = L1;
+        const uint32_t cnt = __builtin_popcount(L0 & 0x80808080u) + __builtin_popcount(L1 & 0x80808080u);
+        uint32_t wt = 0, pr = 0;
+        if (__ballot(cnt != 0) != 0ull) {
+            const uint64_t lt = lanemask_lt();
+            const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u);
+            const uint64_t b2 = __ballot(cnt & 4u), b3 = __ballot(cnt & 8u);
+            pr = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt) + 8 * __popcll(b3 & lt);
+            wt = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
+        }
+        pre[k] = pr;
+        if (lane == 0) sh.wtot[k][wave] = wt;
+    }
+    __syncthreads();
+    uint32_t run = 0, base[kEncGroups];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; w++) {
+            if (w == wave) base[k] = run;
+            run += sh.wtot[k][w];
+        }
+    }
+    if (tid == 0) ws.counts[tile] = run;
+    const uint32_t C = p.Cmask + 1;
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        uint32_t rank = base[k] + pre[k];
+        if (C < (uint32_t)kTile && g0 < p.n && (g0 & p.Cmask) == 0)
+            ws.chunk_pre[g0 >> p.logC] = rank;
+        uint64_t esc = ((uint64_t)(Lw[k][1] & 0x80808080u) << 32) | (Lw[k][0] & 0x80808080u);
+        while (esc) {
+            const int bit = __builtin_ctzll(esc);
+            const int j = bit >> 3;                       // word within the group
+            const uint32_t w = xw[k][j >> 1] >> (16 * (j & 1));
+            const uint64_t i = g0 + j;
+            ws.stage_pos[tile * kTile + rank] = (uint16_t)(i & p.Cmask);
+            ws.stage_val[tile * kTile + rank] = (uint8_t)((w >> 7) & 0xFFu);
+            rank++;
+            esc &= esc - 1;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_encode_tile(const uint16_t *__restrict__ x,
+                                                          uint8_t *__restrict__ out, EncWs ws, EncParams p)
+{
+    __shared__ EncShared sh;
+    const int tid = threadIdx.x;
+    if (tid < 64) reinterpret_cast<uint32_t *>(sh.lut)[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kTile;
+    uint32_t xw[kEncGroups][4];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        if (g0 + 8 <= p.n) {
+            const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + g0));
+            xw[k][0] = v.x; xw[k][1] = v.y; xw[k][2] = v.z; xw[k][3] = v.w;
+        } else {
+            uint16_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) h[j] = (g0 + j < p.n) ? x[g0 + j] : (uint16_t)0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) xw[k][q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
+        }
+    }
+    __syncthreads();
+    encode_groups(xw, t0, tile, out, ws, p, sh);
+}
+
+// Single workgroup. tile_pre[t] = escapes before tile t; tile_pre[ntiles] = M.
+// Also writes the header, offsets[nch] = M and every padding byte.
+__global__ __launch_bounds__(kScanThreads) void k_scan_tiles(EncWs ws, uint8_t *__restrict__ out, HeaderParams hp)
+{
+    __shared__ uint32_t s_wave[kScanThreads / 64];
+    __shared__ uint32_t s_total;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t per = (hp.ntiles + kScanThreads - 1) / kScanThreads;
+    const uint64_t lo = tid * per, hi = (lo + per < hp.ntiles) ? lo + per : hp.ntiles;
+    uint32_t sum = 0;
+    for (uint64_t t = lo; t < hi; t++) sum += ws.counts[t];
+    // inclusive scan across the wave
+    uint32_t inc = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t v = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += v;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < kScanThreads / 64; w++) {
+            uint32_t v = s_wave[w];
+            s_wave[w] = run;
+            run += v;
+        }
+        s_total = run;
+    }
+    __syncthreads();
+    uint32_t run = s_wave[wave] + inc - sum;
+    for (uint64_t t = lo; t < hi; t++) {
+        uint32_t c = ws.counts[t];
+        ws.tile_pre[t] = run;
+        run += c;
+    }
+    const uint64_t M = s_total;
+    if (tid == 0) ws.tile_pre[hp.ntiles] = (uint32_t)M;
+    // header: template + M + total_bytes
+    const uint64_t off_val = hp.off_pos + align256(2 * M);
+    const uint64_t total = off_val + M;
+    if (tid < 64) {
+        uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[tid];
+        if (tid == 6) w = (uint32_t)M;
+        if (tid == 7) w = (uint32_t)(M >> 32);
+        if (tid == 8) w = (uint32_t)total;
+        if (tid == 9) w = (uint32_t)(total >> 32);
+        reinterpret_cast<uint32_t *>(out)[tid] = w;
+    }
+    if (tid == 64) reinterpret_cast<uint32_t *>(out + hp.off_offs)[hp.nch] = (uint32_t)M;
+    // zero padding after each section (each gap is under 256 bytes)
+    if (tid < 256) {
+        const uint64_t sm_end = kHeader + hp.n;
+        if (sm_end + tid < hp.off_codes) out[sm_end + tid] = 0;
+        const uint64_t codes_end = hp.off_codes + (hp.n + 1) / 2;
+        if (codes_end + tid < hp.off_offs) out[codes_end + tid] = 0;
+        const uint64_t offs_end = hp.off_offs + 4 * (hp.nch + 1);
+        if (offs_end + tid < hp.off_pos) out[offs_end + tid] = 0;
+        const uint64_t pos_end = hp.off_pos + 2 * M;
+        if (pos_end + tid < off_val) out[pos_end + tid] = 0;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p)
+{
+    const uint64_t tile = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint32_t P = ws.tile_pre[tile];
+    const uint32_t m = ws.counts[tile];
+    const uint64_t M = ws.tile_pre[p.ntiles];
+    uint16_t *pos = reinterpret_cast<uint16_t *>(out + p.off_pos);
+    uint8_t *val = out + p.off_pos + align256(2 * M);
+    for (uint32_t j = tid; j < m; j += kThreads) {
+        pos[P + j] = ws.stage_pos[tile * kTile + j];
+        val[P + j] = ws.stage_val[tile * kTile + j];
+    }
+    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
+    const uint64_t t0 = tile * kTile;
+    const uint32_t C = p.Cmask + 1;
+    if (C < (uint32_t)kTile) {
+        const uint64_t c0 = t0 >> p.logC;
+        uint64_t cn = (uint64_t)kTile >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
+        for (uint64_t i = tid; i < cn; i += kThreads) offs[c0 + i] = P + ws.chunk_pre[c0 + i];
+    } else if ((t0 & p.Cmask) == 0 && tid == 0) {
+        offs[t0 >> p.logC] = P;
+    }
+}
+
+// ============================================================== decode ====
+// View of one input stream inside a kernel.
+struct StreamIn {
+    const uint8_t *base;
+    uint64_t bytes;       // readable bytes at base
+};
+
+struct PatchShared {
+    uint32_t mask[kTile / 32];
+    uint8_t val[kTile];
+    uint32_t offs[kTile / 64 + 1];
+    uint32_t range[2];
+};
+
+// Escape range [E0, E1) of the tile's words [t0, t0 + kTile) and its patch
+// map in LDS. Returns false when the tile has no escapes. Every thread of
+// the workgroup calls it; it ends with a barrier when it returns true.
+__device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams &p, PatchShared &sh)
+{
+    const int tid = threadIdx.x;
+    // M from the header; a value that does not fit the buffer disables the patch
+    const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
+    if (M > p.n || p.off_pos + align256(2 * M) + M > s.bytes) return false;
+    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs);
+    const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos);
+    const uint8_t *val = s.base + p.off_pos + align256(2 * M);
+    const uint64_t tile_end = (t0 + kTile < p.n) ? t0 + kTile : p.n;
+    uint64_t E0, E1;
+    const bool small_chunks = p.C <= (uint32_t)kTile;
+    uint64_t c0 = t0 >> p.logC, nc = 0;
+    if (small_chunks) {
+        nc = ((tile_end - 1) >> p.logC) - c0 + 1;
+        E0 = offs[c0];
+        E1 = offs[c0 + nc];
+        if (E1 > M) E1 = M;
+        if (E0 > E1) E0 = E1;
+    } else {
+        // one chunk spans several tiles: find the escapes whose position
+        // falls in this tile by a 256-way search over the ascending positions
+        uint64_t lo = offs[c0], hi = offs[c0 + 1];
+        if (hi > M) hi = M;
+        if (lo > hi) lo = hi;
+        const uint32_t rel0 = (uint32_t)(t0 - (c0 << p.logC));
+        uint64_t res[2];
+        for (int side = 0; side < 2; side++) {
+            const uint32_t target = rel0 + (side ? (uint32_t)kTile : 0u);
+            uint64_t a = lo, b = hi;            // answer in [a, b]
+            while (b - a > (uint64_t)kThreads) {
+                const uint64_t step = (b - a + kThreads - 1) / kThreads;
+                const uint64_t j = a + (uint64_t)tid * step;
+                const int below = (j < b) && (pos[j] < target);
+                const int cnt = __syncthreads_count(below);
+                const uint64_t na = (cnt > 0) ? a + (uint64_t)(cnt - 1) * step + 1 : a;
+                uint64_t nb = a + (uint64_t)cnt * step;
+                if (nb > b) nb = b;
+                a = na;
+                b = nb;
+            }
+            const uint64_t j = a + tid;
+            const int below = (j < b) && (pos[j] < target);
+            res[side] = a + (uint64_t)__syncthreads_count(below);
+        }
+        E0 = res[0];
+        E1 = res[1];
+        lo = res[0];
+        (void)lo;
+    }
+    if (E1 <= E0) return false;
+    for (int i = tid; i < kTile / 32; i += kThreads) sh.mask[i] = 0;
+    if (small_chunks)
+        for (uint64_t q = tid; q <= nc; q += kThreads) {
+            uint32_t o = offs[c0 + q];
+            sh.offs[q] = o > (uint32_t)E1 ? (uint32_t)E1 : o;
+        }
+    __syncthreads();
+    for (uint64_t j = E0 + tid; j < E1; j += kThreads) {
+        const uint32_t ps = pos[j];
+        uint64_t li;
+        if (small_chunks) {
+            // last chunk q with offs[q] <= j
+            uint32_t a = 0, b = (uint32_t)nc;   // offs[a] <= j < offs[b]
+            while (b - a > 1) {
+                const uint32_t mid = (a + b) >> 1;
+                if (sh.offs[mid] <= (uint32_t)j) a = mid; else b = mid;
+            }
+            li = ((uint64_t)a << p.logC) + ps;
+        } else {
+            li = (c0 << p.logC) + ps - t0;    // may wrap for a corrupt position
+        }
+        if (ps < p.C && li < (uint64_t)kTile && t0 + li < p.n) {
+            sh.val[li] = val[j];
+            atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
+        }
+    }
+    __syncthreads();
+    return true;
+}
+
+// Apply the patch map to the `NW` words of a thread's group starting at tile
+// word li0 (y holds NW/2 dwords).
+template <int NW>
+__device__ __forceinline__ void apply_patch(const PatchShared &sh, uint32_t li0, uint32_t *y)
+{
+    uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & ((NW == 32) ? 0xFFFFFFFFu : ((1u << NW) - 1u));
+    if (bits == 0) return;
+#pragma unroll
+    for (int j = 0; j < NW; j++)
+        if ((bits >> j) & 1u) y[j >> 1] = set_exp(y[j >> 1], j & 1, sh.val[li0 + j]);
+}
+
+template <bool kPatch>
+__global__ __launch_bounds__(kThreads) void k_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+{
+    __shared__ PatchShared sh;
+    const int tid = threadIdx.x;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kTile;
+    uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
+    uint32_t out[kDecGroups][8];
+#pragma unroll
+    for (int k = 0; k < kDecGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 16) + (uint64_t)tid * 16;
+        if (g0 < p.n) {
+            // sections are padded to 256 bytes, so a tail group's full loads stay inside them
+            const u32x4 sm = ld_stream(reinterpret_cast<const u32x4 *>(s.base + kHeader + g0));
+            const u32x2 cd = ld_stream(reinterpret_cast<const u32x2 *>(s.base + p.off_codes + g0 / 2));
+            decode8(sm.x, sm.y, cd.x, dec, &out[k][0]);
+            decode8(sm.z, sm.w, cd.y, dec, &out[k][4]);
+        }
+    }
+    if (kPatch) {
+        if (build_patch_map(s, t0, p, sh)) {
+#pragma unroll
+            for (int k = 0; k < kDecGroups; k++)
+                apply_patch<16>(sh, (uint32_t)(k * (kThreads * 16) + tid * 16), out[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kDecGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 16) + (uint64_t)tid * 16;
+        if (g0 + 16 <= p.n) {
+            u32x4 *dst = reinterpret_cast<u32x4 *>(y + g0);
+            u32x4 v0 = {out[k][0], out[k][1], out[k][2], out[k][3]};
+            u32x4 v1 = {out[k][4], out[k][5], out[k][6], out[k][7]};
+            st_stream(v0, dst);
+            st_stream(v1, dst + 1);
+        } else if (g0 < p.n) {
+            for (int j = 0; j < 16 && g0 + j < p.n; j++)
+                y[g0 + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
+// Two-kernel variant, step 2: for every escape, overwrite the exponent field
+// of the decoded word in place. One wave per chunk.
+__global__ __launch_bounds__(kThreads) void k_patch(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+{
+    const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
+    if (M > p.n || p.off_pos + align256(2 * M) + M > s.bytes) return;
+    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs);
+    const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos);
+    const uint8_t *val = s.base + p.off_pos + align256(2 * M);
+    const int lane = threadIdx.x & 63;
+    const uint64_t waves = (uint64_t)gridDim.x * (kThreads / 64);
+    for (uint64_t c = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); c < p.nch; c += waves) {
+        uint64_t j0 = offs[c], j1 = offs[c + 1];
+        if (j1 > M) j1 = M;
+        for (uint64_t j = j0 + lane; j < j1; j += 64) {
+            const uint32_t ps = pos[j];
+            const uint64_t i = (c << p.logC) + ps;
+            if (ps < p.C && i < p.n) {
+                const uint32_t w = y[i];
+                y[i] = (uint16_t)((w & 0x807Fu) | ((uint32_t)val[j] << 7));
+            }
+        }
+    }
+}
+
+// ============================================================== reduce ====
+__global__ __launch_bounds__(kThreads) void k_reduce_tile(StreamIn sa, StreamIn sb, uint8_t *__restrict__ out,
+                                                          EncWs ws, EncParams ep, DecParams dp)
+{
+    __shared__ EncShared esh;
+    __shared__ PatchShared psh;
+    const int tid = threadIdx.x;
+    if (tid < 64) reinterpret_cast<uint32_t *>(esh.lut)[tid] = reinterpret_cast<const uint32_t *>(ep.lut)[tid];
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kTile;
+    uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
+    uint32_t ya[kEncGroups][4], yb[kEncGroups][4];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        if (g0 < dp.n) {
+            const u32x2 sma = ld_stream(reinterpret_cast<const u32x2 *>(sa.base + kHeader + g0));
+            const uint32_t cda = ld_stream(reinterpret_cast<const uint32_t *>(sa.base + dp.off_codes + g0 / 2));
+            const u32x2 smb = ld_stream(reinterpret_cast<const u32x2 *>(sb.base + kHeader + g0));
+            const uint32_t cdb = ld_stream(reinterpret_cast<const uint32_t *>(sb.base + dp.off_codes + g0 / 2));
+            decode8(sma.x, sma.y, cda, dec, ya[k]);
+            decode8(smb.x, smb.y, cdb, dec, yb[k]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
+        }
+    }
+    if (build_patch_map(sa, t0, dp, psh)) {
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++)
+            apply_patch<8>(psh, (uint32_t)(k * (kThreads * 8) + tid * 8), ya[k]);
+    }
+    __syncthreads();       // the map is rebuilt for the second input
+    if (build_patch_map(sb, t0, dp, psh)) {
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++)
+            apply_patch<8>(psh, (uint32_t)(k * (kThreads * 8) + tid * 8), yb[k]);
+    }
+    uint32_t r[kEncGroups][4];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[k][q], yb[k][q]);
+    encode_groups(r, t0, tile, out, ws, ep, esh);
+}
+
+// ================================================================ host ====
+thread_local char g_hip_err[160];
+
+int hip_fail(hipError_t e, const char *what)
+{
+    snprintf(g_hip_err, sizeof g_hip_err, "HIP error in %s: %s", what, hipGetErrorString(e));
+    return UZIP_EHIP;
+}
+
+#define UZIP_LAUNCH_CHECK(what)                       \
+    do {                                              \
+        hipError_t e_ = hipGetLastError();            \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_nc(uint64_t n, uint32_t C)
+{
+    if (n == 0 || n >= (1ull << 32)) return false;
+    if (C < 64 || C > 65536 || (C & (C - 1)) != 0) return false;
+    return true;
+}
+
+// The codebook's three tables must agree with dec[].
+int check_codebook(const uzip_codebook_t *cb)
+{
+    if (!cb || cb->version != UZIP_VERSION) return UZIP_EINVAL;
+    uint8_t seen[256] = {0};
+    for (int k = 0; k < 16; k++) {
+        if (seen[cb->dec[k]]) return UZIP_EINVAL;
+        seen[cb->dec[k]] = 1;
+    }
+    for (int e = 0; e < 256; e++) {
+        if (cb->member[e] != seen[e]) return UZIP_EINVAL;
+        if (!seen[e] && cb->enc[e] != 0) return UZIP_EINVAL;
+    }
+    for (int k = 0; k < 16; k++)
+        if (cb->enc[cb->dec[k]] != k) return UZIP_EINVAL;
+    return UZIP_OK;
+}
+
+EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
+{
+    EncParams p;
+    for (int e = 0; e < 256; e++) p.lut[e] = 0x80;
+    for (int k = 0; k < 16; k++) p.lut[cb->dec[k]] = (uint8_t)k;
+    p.n = L.n;
+    p.nch = L.nch;
+    p.ntiles = (L.n + kTile - 1) / kTile;
+    p.Cmask = L.C - 1;
+    p.logC = L.logC;
+    p.off_codes = L.off_codes;
+    p.off_offs = L.off_offs;
+    p.off_pos = L.off_pos;
+    return p;
+}
+
+DecParams make_dec_params(const Layout &L, const uzip_codebook_t *cb)
+{
+    DecParams p;
+    memcpy(p.dec, cb->dec, 16);
+    p.n = L.n;
+    p.nch = L.nch;
+    p.C = L.C;
+    p.logC = L.logC;
+    p.off_codes = L.off_codes;
+    p.off_offs = L.off_offs;
+    p.off_pos = L.off_pos;
+    return p;
+}
+
+HeaderParams make_header_params(const Layout &L, const uzip_codebook_t *cb)
+{
+    HeaderParams h;
+    memset(h.tmpl, 0, sizeof h.tmpl);
+    h.tmpl[0] = 0x55; h.tmpl[1] = 0x5A; h.tmpl[2] = 0x42; h.tmpl[3] = 0x31;
+    const uint16_t ver = 1;
+    memcpy(h.tmpl + 4, &ver, 2);
+    memcpy(h.tmpl + 8, &L.C, 4);
+    memcpy(h.tmpl + 16, &L.n, 8);
+    memcpy(h.tmpl + 40, cb->dec, 16);
+    h.n = L.n;
+    h.nch = L.nch;
+    h.ntiles = (L.n + kTile - 1) / kTile;
+    h.off_codes = L.off_codes;
+    h.off_offs = L.off_offs;
+    h.off_pos = L.off_pos;
+    return h;
+}
+
+EncWs make_ws(void *d_ws, uint64_t n, uint32_t C)
+{
+    const WsLayout w = ws_layout(n, C);
+    uint8_t *b = static_cast<uint8_t *>(d_ws);
+    EncWs ws;
+    ws.counts = reinterpret_cast<uint32_t *>(b + w.counts);
+    ws.tile_pre = reinterpret_cast<uint32_t *>(b + w.tile_pre);
+    ws.chunk_pre = reinterpret_cast<uint32_t *>(b + w.chunk_pre);
+    ws.stage_pos = reinterpret_cast<uint16_t *>(b + w.stage_pos);
+    ws.stage_val = b + w.stage_val;
+    return ws;
+}
+
+struct Events {
+    const uzip_opts_t *o;
+    hipStream_t s;
+    int record(uint32_t i) const
+    {
+        if (!o || !o->events || i >= o->n_events) return UZIP_OK;
+        hipError_t e = hipEventRecord(o->events[i], s);
+        return e == hipSuccess ? UZIP_OK : hip_fail(e, "hipEventRecord");
+    }
+};
+
+// Scan + placement shared by encode and reduce (kernels 2 and 3 of the call).
+int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &ep, const EncWs &ws,
+                  uint8_t *out, const Events &ev, hipStream_t s)
+{
+    const HeaderParams hp = make_header_params(L, cb);
+    k_scan_tiles<<<1, kScanThreads, 0, s>>>(ws, out, hp);
+    UZIP_LAUNCH_CHECK("k_scan_tiles");
+    int rc = ev.record(2);
+    if (rc) return rc;
+    k_place_escapes<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(ws, out, ep);
+    UZIP_LAUNCH_CHECK("k_place_escapes");
+    return ev.record(3);
+}
+
+// Host-side structural check (same rules as the header comment of
+// uzip_validate_host).
+uint16_t rd16(const uint8_t *p) { uint16_t v; memcpy(&v, p, 2); return v; }
+uint32_t rd32(const uint8_t *p) { uint32_t v; memcpy(&v, p, 4); return v; }
+uint64_t rd64(const uint8_t *p) { uint64_t v; memcpy(&v, p, 8); return v; }
+
+}  // namespace
+
+// ============================================================== C-ABI =====
+extern "C" {
+
+uint64_t uzip_max_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk)) return 0;
+    return total_of(make_layout(n, chunk), n);
+}
+
+uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk)) return 0;
+    return ws_layout(n, chunk).total;
+}
+
+int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb)
+{
+    if (!hist || !cb) return UZIP_EINVAL;
+    // rank all 256 exponents: count descending, exponent ascending (stable
+    // insertion sort over an index array already in ascending order)
+    int order[256];
+    for (int e = 0; e < 256; e++) order[e] = e;
+    for (int i = 1; i < 256; i++) {
+        int v = order[i], j = i - 1;
+        while (j >= 0 && hist[order[j]] < hist[v]) {
+            order[j + 1] = order[j];
+            j--;
+        }
+        order[j + 1] = v;
+    }
+    memset(cb, 0, sizeof *cb);
+    cb->version = UZIP_VERSION;
+    uint64_t total = 0;
+    for (int e = 0; e < 256; e++) {
+        cb->hist[e] = hist[e];
+        total += hist[e];
+    }
+    cb->n_cal = total;
+    for (int k = 0; k < 16; k++) {
+        const int e = order[k];
+        cb->dec[k] = (uint8_t)e;
+        cb->enc[e] = (uint8_t)k;
+        cb->member[e] = 1;
+    }
+    return UZIP_OK;
+}
+
+int uzip_parse_header(const void *h_header, uint64_t *n, uint32_t *chunk, uint64_t *m,
+                      uint64_t *total_bytes, uint8_t dec[16])
+{
+    if (!h_header) return UZIP_EINVAL;
+    const uint8_t *h = static_cast<const uint8_t *>(h_header);
+    if (!(h[0] == 0x55 && h[1] == 0x5A && h[2] == 0x42 && h[3] == 0x31)) return UZIP_ECORRUPT;
+    if (rd16(h + 4) != 1) return UZIP_ECORRUPT;
+    if (n) *n = rd64(h + 16);
+    if (chunk) *chunk = rd32(h + 8);
+    if (m) *m = rd64(h + 24);
+    if (total_bytes) *total_bytes = rd64(h + 32);
+    if (dec) memcpy(dec, h + 40, 16);
+    return UZIP_OK;
+}
+
+int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook_t *cb)
+{
+    if (!h_stream || !cb) return UZIP_EINVAL;
+    const uint8_t *s = static_cast<const uint8_t *>(h_stream);
+    if (bytes < kHeader) return UZIP_ECORRUPT;
+    uint64_t n, m, total;
+    uint32_t C;
+    uint8_t dec[16];
+    if (uzip_parse_header(s, &n, &C, &m, &total, dec) != UZIP_OK) return UZIP_ECORRUPT;
+    if (rd16(s + 6) != 0 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    for (uint64_t i = 56; i < kHeader; i++)
+        if (s[i]) return UZIP_ECORRUPT;
+    if (!valid_nc(n, C) || m > n) return UZIP_ECORRUPT;
+    const Layout L = make_layout(n, C);
+    const uint64_t off_val = off_val_of(L, m);
+    if (total != off_val + m || bytes < total) return UZIP_ECORRUPT;
+    if (memcmp(dec, cb->dec, 16) != 0) return UZIP_ECODEBOOK;
+    bool in_book[256] = {false};
+    for (int k = 0; k < 16; k++) {
+        if (in_book[dec[k]]) return UZIP_ECORRUPT;
+        in_book[dec[k]] = true;
+    }
+    auto zero = [&](uint64_t a, uint64_t b) {
+        for (uint64_t i = a; i < b; i++)
+            if (s[i]) return false;
+        return true;
+    };
+    const uint64_t codes_bytes = (n + 1) / 2;
+    if (!zero(kHeader + n, L.off_codes)) return UZIP_ECORRUPT;
+    if ((n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
+    if (!zero(L.off_codes + codes_bytes, L.off_offs)) return UZIP_ECORRUPT;
+    if (!zero(L.off_offs + 4 * (L.nch + 1), L.off_pos)) return UZIP_ECORRUPT;
+    if (!zero(L.off_pos + 2 * m, off_val)) return UZIP_ECORRUPT;
+    const uint8_t *offs = s + L.off_offs;
+    if (rd32(offs) != 0 || rd32(offs + 4 * L.nch) != m) return UZIP_ECORRUPT;
+    for (uint64_t c = 0; c < L.nch; c++) {
+        const uint64_t j0 = rd32(offs + 4 * c), j1 = rd32(offs + 4 * (c + 1));
+        const uint64_t len = (c + 1) * C <= n ? C : n - c * C;
+        if (j1 < j0 || j1 > m || j1 - j0 > len) return UZIP_ECORRUPT;
+        uint32_t prev = 0;
+        for (uint64_t j = j0; j < j1; j++) {
+            const uint32_t p = rd16(s + L.off_pos + 2 * j);
+            if (p >= len || (j > j0 && p <= prev)) return UZIP_ECORRUPT;
+            prev = p;
+            if (in_book[s[off_val + j]]) return UZIP_ECORRUPT;
+            const uint64_t i = c * C + p;
+            const uint8_t b = s[L.off_codes + i / 2];
+            if (((i & 1) ? (b >> 4) : (b & 0xF)) != 0) return UZIP_ECORRUPT;
+        }
+    }
+    return UZIP_OK;
+}
+
+const char *uzip_strerror(int code)
+{
+    switch (code) {
+    case UZIP_OK: return "ok";
+    case UZIP_EINVAL: return "invalid argument (null or misaligned pointer, bad n, chunk or codebook)";
+    case UZIP_ENOSPC: return "output capacity or workspace too small";
+    case UZIP_ECORRUPT: return "stream is malformed";
+    case UZIP_ECODEBOOK: return "stream was encoded with a different codebook";
+    case UZIP_EHIP: return g_hip_err[0] ? g_hip_err : "HIP runtime error";
+    default: return "unknown error";
+    }
+}
+
+int uzip_histogram(const uint16_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s)
+{
+    if (!d_x || !d_hist || !aligned16(d_x) || ((uintptr_t)d_hist & 7u)) return UZIP_EINVAL;
+    if (n == 0 || n >= (1ull << 32)) return UZIP_EINVAL;
+    uint64_t groups = (n / 8 + kThreads - 1) / kThreads;
+    unsigned grid = (unsigned)(groups < 2048 ? (groups ? groups : 1) : 2048);
+    k_hist<<<grid, kThreads, 0, s>>>(d_x, n, reinterpret_cast<unsigned long long *>(d_hist));
+    UZIP_LAUNCH_CHECK("k_hist");
+    return UZIP_OK;
+}
+
+int uzip_calibrate(const uint16_t *d_x, uint64_t n, uint64_t *d_hist_ws, uzip_codebook_t *cb, hipStream_t s)
+{
+    if (!cb || !d_hist_ws) return UZIP_EINVAL;
+    hipError_t e = hipMemsetAsync(d_hist_ws, 0, 256 * sizeof(uint64_t), s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    int rc = uzip_histogram(d_x, n, d_hist_ws, s);
+    if (rc) return rc;
+    uint64_t h[256];
+    e = hipMemcpyAsync(h, d_hist_ws, sizeof h, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return uzip_codebook_from_hist(h, cb);
+}
+
+int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                   const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk);
+    const EncParams ep = make_enc_params(L, cb);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    k_encode_tile<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("k_encode_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_stream_bytes(const void *d_stream, uint64_t *total_bytes, uint64_t *m, hipStream_t s)
+{
+    if (!d_stream) return UZIP_EINVAL;
+    uint8_t h[kHeader];
+    hipError_t e = hipMemcpyAsync(h, d_stream, kHeader, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return uzip_parse_header(h, nullptr, nullptr, m, total_bytes, nullptr);
+}
+
+int uzip_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                   const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !d_y || !aligned16(d_in) || !aligned16(d_y)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    const Layout L = make_layout(n, chunk);
+    if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;   // smaller than any stream of n values
+    const DecParams dp = make_dec_params(L, cb);
+    const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
+    const unsigned grid = (unsigned)((n + kTile - 1) / kTile);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    if (opts && (opts->flags & UZIP_F_SEPARATE_PATCH)) {
+        k_decode_tile<false><<<grid, kThreads, 0, s>>>(si, d_y, dp);
+        UZIP_LAUNCH_CHECK("k_decode_tile<dense>");
+        if ((rc = ev.record(1))) return rc;
+        uint64_t wgs = (L.nch + (kThreads / 64) - 1) / (kThreads / 64);
+        k_patch<<<(unsigned)(wgs < 8192 ? wgs : 8192), kThreads, 0, s>>>(si, d_y, dp);
+        UZIP_LAUNCH_CHECK("k_patch");
+        return ev.record(2);
+    }
+    k_decode_tile<true><<<grid, kThreads, 0, s>>>(si, d_y, dp);
+    UZIP_LAUNCH_CHECK("k_decode_tile");
+    return ev.record(1);
+}
+
+int uzip_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s)
+{
+    return uzip_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
+}
+
+int uzip_reduce_add_ex(const void *d_a, uint64_t a_bytes, const void *d_b, uint64_t b_bytes,
+                       uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_a || !d_b || !d_out || !d_ws) return UZIP_EINVAL;
+    if (!aligned16(d_a) || !aligned16(d_b) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk);
+    if (a_bytes < total_of(L, 0) || b_bytes < total_of(L, 0)) return UZIP_EINVAL;
+    const EncParams ep = make_enc_params(L, cb);
+    const DecParams dp = make_dec_params(L, cb);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const StreamIn sa{static_cast<const uint8_t *>(d_a), a_bytes};
+    const StreamIn sb{static_cast<const uint8_t *>(d_b), b_bytes};
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    k_reduce_tile<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(sa, sb, static_cast<uint8_t *>(d_out), ws, ep, dp);
+    UZIP_LAUNCH_CHECK("k_reduce_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_reduce_add(const void *d_a, uint64_t a_bytes, const void *d_b, uint64_t b_bytes,
+                    uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_reduce_add_ex(d_a, a_bytes, d_b, b_bytes, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes,
+                              nullptr, s);
+}
+
+int uzip_validate(const void *d_stream, uint64_t bytes, const uzip_codebook_t *cb, hipStream_t s)
+{
+    if (!d_stream || !cb || bytes < kHeader) return d_stream && cb ? UZIP_ECORRUPT : UZIP_EINVAL;
+    uint8_t *h = static_cast<uint8_t *>(malloc(bytes));
+    if (!h) return UZIP_ENOSPC;
+    hipError_t e = hipMemcpyAsync(h, d_stream, bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        free(h);
+        return hip_fail(e, "hipMemcpyAsync");
+    }
+    int rc = uzip_validate_host(h, bytes, cb);
+    free(h);
+    return rc;
+}
+
+}  // extern "C"

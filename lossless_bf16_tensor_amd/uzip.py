@@ -1,0 +1,250 @@
+"""ctypes binding of libuzip.so (C-ABI: include/uzip.h).
+
+Argument marshalling only: every step of the codec runs in the library's HIP
+kernels. torch supplies device memory (tensors) and the stream
+(``torch.cuda.current_stream()``). The library must be built first
+(``python -m lossless_bf16_tensor_amd.build``); without it every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuzip.so")
+
+UZIP_VERSION = 1
+UZIP_F_SEPARATE_PATCH = 0x1
+ERRORS = {0: "UZIP_OK", -1: "UZIP_EINVAL", -2: "UZIP_ENOSPC", -3: "UZIP_ECORRUPT",
+          -4: "UZIP_ECODEBOOK", -5: "UZIP_EHIP"}
+
+# every symbol include/uzip.h declares
+EXPORTS = (
+    "uzip_max_bytes", "uzip_workspace_bytes", "uzip_codebook_from_hist", "uzip_validate_host",
+    "uzip_parse_header", "uzip_strerror", "uzip_histogram", "uzip_calibrate", "uzip_encode",
+    "uzip_encode_ex", "uzip_stream_bytes", "uzip_decode", "uzip_decode_ex", "uzip_reduce_add",
+    "uzip_reduce_add_ex", "uzip_validate",
+)
+
+
+class UzipError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Codebook(ctypes.Structure):
+    """uzip_codebook_t: dec[16], enc[256], member[256], hist[256], n_cal."""
+    _fields_ = [("version", ctypes.c_uint32), ("dec", ctypes.c_uint8 * 16),
+                ("enc", ctypes.c_uint8 * 256), ("member", ctypes.c_uint8 * 256),
+                ("hist", ctypes.c_uint64 * 256), ("n_cal", ctypes.c_uint64)]
+
+    @property
+    def dec_list(self):
+        return list(self.dec)
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_uint32),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libuzip.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m lossless_bf16_tensor_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u64, u32, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+    cbp = ctypes.POINTER(Codebook)
+    op = ctypes.POINTER(Opts)
+    sig = {
+        "uzip_max_bytes": (u64, [u64, u32]),
+        "uzip_workspace_bytes": (u64, [u64, u32]),
+        "uzip_codebook_from_hist": (i32, [vp, cbp]),
+        "uzip_validate_host": (i32, [vp, u64, cbp]),
+        "uzip_parse_header": (i32, [vp, vp, vp, vp, vp, vp]),
+        "uzip_strerror": (ctypes.c_char_p, [i32]),
+        "uzip_histogram": (i32, [vp, u64, vp, vp]),
+        "uzip_calibrate": (i32, [vp, u64, vp, cbp, vp]),
+        "uzip_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
+        "uzip_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_stream_bytes": (i32, [vp, vp, vp, vp]),
+        "uzip_decode": (i32, [vp, u64, u64, u32, cbp, vp, vp]),
+        "uzip_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
+        "uzip_reduce_add": (i32, [vp, u64, vp, u64, u64, u32, cbp, vp, u64, vp, u64, vp]),
+        "uzip_reduce_add_ex": (i32, [vp, u64, vp, u64, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_validate": (i32, [vp, u64, cbp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise UzipError(rc, f"{what}: {lib().uzip_strerror(rc).decode()}")
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _words(t: torch.Tensor) -> torch.Tensor:
+    """View a bfloat16/int16/uint16 tensor as flat 16-bit words."""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if t.dtype not in (torch.int16, torch.uint16):
+        raise ValueError(f"expected 16-bit words, got {t.dtype}")
+    return t.reshape(-1)
+
+
+def _opts(events=None, flags=0):
+    if not events and not flags:
+        return None
+    o = Opts()
+    if events:
+        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        o.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        o.n_events = len(events)
+        o._keep = arr
+    o.flags = flags
+    return o
+
+
+# ------------------------------------------------------------- host only ----
+def max_bytes(n: int, chunk: int) -> int:
+    return int(lib().uzip_max_bytes(n, chunk))
+
+
+def workspace_bytes(n: int, chunk: int) -> int:
+    return int(lib().uzip_workspace_bytes(n, chunk))
+
+
+def codebook_from_hist(hist) -> Codebook:
+    h = (ctypes.c_uint64 * 256)(*[int(v) for v in hist])
+    cb = Codebook()
+    _check(lib().uzip_codebook_from_hist(ctypes.cast(h, ctypes.c_void_p), ctypes.byref(cb)),
+           "codebook_from_hist")
+    return cb
+
+
+def validate_host(buf: bytes, cb: Codebook) -> int:
+    """Structural check of a host copy of a stream; returns the C status code."""
+    b = bytes(buf)
+    return int(lib().uzip_validate_host(ctypes.c_char_p(b), len(b), ctypes.byref(cb)))
+
+
+def parse_header(buf: bytes):
+    b = bytes(buf[:256])
+    n, m, tot = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    c = ctypes.c_uint32()
+    dec = (ctypes.c_uint8 * 16)()
+    _check(lib().uzip_parse_header(ctypes.c_char_p(b), ctypes.byref(n), ctypes.byref(c),
+                                   ctypes.byref(m), ctypes.byref(tot), ctypes.cast(dec, ctypes.c_void_p)),
+           "parse_header")
+    return {"n": n.value, "chunk": c.value, "m": m.value, "total_bytes": tot.value, "dec": list(dec)}
+
+
+# ---------------------------------------------------------------- device ----
+def histogram(x: torch.Tensor, hist: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Add the exponent histogram of x to hist (int64[256] on the device)."""
+    w = _words(x)
+    if hist is None:
+        hist = torch.zeros(256, dtype=torch.int64, device=w.device)
+    _check(lib().uzip_histogram(_ptr(w), w.numel(), _ptr(hist), _stream(stream)), "histogram")
+    return hist
+
+
+def calibrate(x: torch.Tensor, stream=None) -> Codebook:
+    w = _words(x)
+    ws = torch.empty(256, dtype=torch.int64, device=w.device)
+    cb = Codebook()
+    _check(lib().uzip_calibrate(_ptr(w), w.numel(), _ptr(ws), ctypes.byref(cb), _stream(stream)),
+           "calibrate")
+    return cb
+
+
+def encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor | None = None,
+           ws: torch.Tensor | None = None, events=None, stream=None) -> torch.Tensor:
+    """Encode; returns the uint8 output buffer (max_bytes long). The stream's
+    own size is in its header (stream_bytes)."""
+    w = _words(x)
+    n = w.numel()
+    cap = max_bytes(n, chunk)
+    if cap == 0:
+        raise UzipError(-1, f"bad n={n} or chunk={chunk}")
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=w.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+    o = _opts(events)
+    _check(lib().uzip_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(),
+                                _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
+           "encode")
+    return out
+
+
+def stream_bytes(buf: torch.Tensor, stream=None):
+    """(total_bytes, M) from a device stream's header (blocking)."""
+    tot, m = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().uzip_stream_bytes(_ptr(buf), ctypes.byref(tot), ctypes.byref(m), _stream(stream)),
+           "stream_bytes")
+    return tot.value, m.value
+
+
+def decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
+           in_bytes: int | None = None, separate_patch: bool = False, events=None,
+           stream=None) -> torch.Tensor:
+    """Decode n words; returns an int16 tensor of BF16 bit patterns."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+    w = _words(out)
+    o = _opts(events, UZIP_F_SEPARATE_PATCH if separate_patch else 0)
+    nb = buf.numel() if in_bytes is None else in_bytes
+    _check(lib().uzip_decode_ex(_ptr(buf), nb, n, chunk, ctypes.byref(cb), _ptr(w),
+                                ctypes.byref(o) if o else None, _stream(stream)), "decode")
+    return out
+
+
+def reduce_add(a: torch.Tensor, b: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024,
+               out: torch.Tensor | None = None, ws: torch.Tensor | None = None, events=None,
+               stream=None) -> torch.Tensor:
+    """Fused decode(a) + decode(b) -> binary32 add -> BF16 (RNE) -> encode."""
+    cap = max_bytes(n, chunk)
+    if out is None:
+        out = torch.empty(cap, dtype=torch.uint8, device=a.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=a.device)
+    o = _opts(events)
+    _check(lib().uzip_reduce_add_ex(_ptr(a), a.numel(), _ptr(b), b.numel(), n, chunk, ctypes.byref(cb),
+                                    _ptr(out), out.numel(), _ptr(ws), ws.numel(),
+                                    ctypes.byref(o) if o else None, _stream(stream)), "reduce_add")
+    return out
+
+
+def validate(buf: torch.Tensor, cb: Codebook, nbytes: int | None = None, stream=None) -> int:
+    """Full structural check of a device stream (blocking); returns the status code."""
+    if nbytes is None:
+        nbytes, _ = stream_bytes(buf, stream)
+    return int(lib().uzip_validate(_ptr(buf), nbytes, ctypes.byref(cb), _stream(stream)))

@@ -1,0 +1,143 @@
+"""CPU tests of the HIP library's host side (no kernel runs here).
+
+The library must load and export every symbol include/uzip.h declares; the
+host-only calls (sizes, codebook building, header parsing, structural
+validation) are checked against the CPU oracle and the stream format; and the
+device entry points must reject bad arguments before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from lossless_bf16_tensor_amd import uzip
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "uzip.h")).read()
+    return sorted(set(re.findall(r"\b(uzip_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = uzip.lib()
+    declared = header_symbols()
+    assert set(declared) == set(uzip.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_library_links_no_oracle():
+    # the product library must not contain the oracle's symbols
+    L = ctypes.CDLL(uzip.LIB_PATH)
+    for name in ("orc_encode", "orc_decode", "orc_top16"):
+        assert not hasattr(L, name)
+
+
+@pytest.mark.parametrize("n,C", [(1, 64), (1000, 64), (1 << 20, 1024), (3 * 65536 + 17, 4096),
+                                 ((1 << 32) - 1, 65536)])
+def test_max_bytes_matches_format(n, C):
+    assert uzip.max_bytes(n, C) == oracle.max_bytes(n, C)
+    assert uzip.workspace_bytes(n, C) >= 3 * n
+
+
+@pytest.mark.parametrize("n,C", [(0, 1024), (1 << 32, 1024), (100, 0), (100, 32), (100, 1000),
+                                 (100, 131072)])
+def test_max_bytes_rejects_bad_args(n, C):
+    assert uzip.max_bytes(n, C) == 0
+    assert uzip.workspace_bytes(n, C) == 0
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_codebook_from_hist_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    h = rng.integers(0, 30, 256).astype(np.uint64)
+    h[rng.integers(0, 256, 100)] = 0
+    cb = uzip.codebook_from_hist(h)
+    ocb = oracle.top16(h)
+    assert list(cb.dec) == ocb.dec.tolist()
+    assert list(cb.enc) == ocb.enc.tolist()
+    assert list(cb.member) == ocb.member.tolist()
+    assert cb.n_cal == int(h.sum()) and cb.version == 1
+
+
+def test_codebook_from_hist_special_cases():
+    h = np.zeros(256, np.uint64)
+    h[[7, 130, 250]] = [100, 5, 5]
+    assert list(uzip.codebook_from_hist(h).dec) == oracle.top16(h).dec.tolist()
+    assert list(uzip.codebook_from_hist(np.zeros(256, np.uint64)).dec) == list(range(16))
+
+
+def _stream():
+    w = workloads.config_1()
+    ocb = oracle.calibrate(w.calib)
+    cb = uzip.codebook_from_hist(ocb.hist)
+    return oracle.encode(w.x, 1024, ocb.dec), cb, ocb
+
+
+def test_parse_header():
+    s, cb, ocb = _stream()
+    h = uzip.parse_header(s.tobytes())
+    assert h["n"] == 1 << 20 and h["chunk"] == 1024 and h["total_bytes"] == s.size
+    assert h["m"] == oracle.stream_m(s) and h["dec"] == ocb.dec.tolist()
+
+
+def test_validate_host_accepts_oracle_streams():
+    s, cb, _ = _stream()
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    x = workloads.all_patterns(1)
+    for C in (64, 65536):
+        ocb = oracle.calibrate(x)
+        assert uzip.validate_host(oracle.encode(x, C, ocb.dec).tobytes(),
+                                  uzip.codebook_from_hist(ocb.hist)) == 0
+
+
+def test_validate_host_rejects_corruptions():
+    from test_oracle_codec import _corruptions
+    s, cb, ocb = _stream()
+    for name, t in _corruptions(s).items():
+        assert uzip.validate_host(t.tobytes(), cb) == -3, name
+    other = ocb.hist.copy()
+    a, b = int(ocb.dec[0]), int(ocb.dec[1])
+    other[a], other[b] = other[b], other[a] + 1
+    assert uzip.validate_host(s.tobytes(), uzip.codebook_from_hist(other)) == -4
+
+
+def test_strerror_texts():
+    L = uzip.lib()
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert L.uzip_strerror(code)
+
+
+def test_device_calls_reject_bad_args_without_gpu():
+    L = uzip.lib()
+    cb = uzip.codebook_from_hist(np.arange(256, dtype=np.uint64))
+    p = ctypes.c_void_p(4096)          # never dereferenced: arguments fail first
+    mis = ctypes.c_void_p(4097)
+    big = uzip.max_bytes(1000, 1024)
+    ws = uzip.workspace_bytes(1000, 1024)
+    cbr = ctypes.byref(cb)
+    assert L.uzip_encode(None, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_encode(mis, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_encode(p, 0, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_encode(p, 1000, 1000, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_encode(p, 1000, 1024, cbr, p, big - 1, p, ws, None) == -2
+    assert L.uzip_encode(p, 1000, 1024, cbr, p, big, p, ws - 1, None) == -2
+    bad = uzip.Codebook.from_buffer_copy(cb)
+    bad.enc[bad.dec[0]] = 5
+    assert L.uzip_encode(p, 1000, 1024, ctypes.byref(bad), p, big, p, ws, None) == -1
+    bad2 = uzip.Codebook.from_buffer_copy(cb)
+    bad2.version = 9
+    assert L.uzip_encode(p, 1000, 1024, ctypes.byref(bad2), p, big, p, ws, None) == -1
+    assert L.uzip_decode(p, 10, 1000, 1024, cbr, p, None) == -1       # in_bytes too small
+    assert L.uzip_decode(p, big, 1000, 1024, cbr, mis, None) == -1
+    assert L.uzip_reduce_add(p, big, p, big, 1000, 1024, cbr, p, big, p, ws - 1, None) == -2
+    assert L.uzip_reduce_add(p, 5, p, big, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_histogram(p, 0, p, None) == -1
+    assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
+    assert L.uzip_validate(None, 100, cbr, None) == -1
