@@ -389,15 +389,23 @@ __global__ __launch_bounds__(kThreads) void k_encode_tile(const uint16_t *__rest
 
 // Single workgroup. tile_pre[t] = escapes before tile t; tile_pre[ntiles] = M.
 // Also writes the header, offsets[nch] = M and every padding byte.
+// Each thread owns a contiguous run of `per` tiles (a multiple of 4, so the
+// run is read and written with 16-byte accesses).
 __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(EncWs ws, uint8_t *__restrict__ out, HeaderParams hp)
 {
     __shared__ uint32_t s_wave[kScanThreads / 64];
     __shared__ uint32_t s_total;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t per = (hp.ntiles + kScanThreads - 1) / kScanThreads;
-    const uint64_t lo = tid * per, hi = (lo + per < hp.ntiles) ? lo + per : hp.ntiles;
+    const uint64_t per = ((hp.ntiles + kScanThreads - 1) / kScanThreads + 3) & ~uint64_t(3);
+    const uint64_t lo = tid * per;
+    const uint64_t hi = (lo + per < hp.ntiles) ? lo + per : (lo < hp.ntiles ? hp.ntiles : lo);
     uint32_t sum = 0;
-    for (uint64_t t = lo; t < hi; t++) sum += ws.counts[t];
+#pragma unroll 8
+    for (uint64_t t = lo; t + 4 <= hi; t += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ws.counts + t);
+        sum += v.x + v.y + v.z + v.w;
+    }
+    for (uint64_t t = lo + ((hi - lo) & ~uint64_t(3)); t < hi; t++) sum += ws.counts[t];
     // inclusive scan across the wave
     uint32_t inc = sum;
 #pragma unroll
@@ -407,19 +415,33 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(EncWs ws, uint8_t *
     }
     if (lane == 63) s_wave[wave] = inc;
     __syncthreads();
-    if (tid == 0) {
-        uint32_t run = 0;
-        for (int w = 0; w < kScanThreads / 64; w++) {
-            uint32_t v = s_wave[w];
-            s_wave[w] = run;
-            run += v;
+    if (tid < 64) {
+        // exclusive scan of the 16 wave totals in one wave
+        uint32_t v = (tid < kScanThreads / 64) ? s_wave[tid] : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            uint32_t u = __shfl_up(x, d, 64);
+            if (lane >= d) x += u;
         }
-        s_total = run;
+        if (tid < kScanThreads / 64) s_wave[tid] = x - v;
+        if (tid == 63) s_total = x;
     }
     __syncthreads();
     uint32_t run = s_wave[wave] + inc - sum;
-    for (uint64_t t = lo; t < hi; t++) {
-        uint32_t c = ws.counts[t];
+#pragma unroll 8
+    for (uint64_t t = lo; t + 4 <= hi; t += 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ws.counts + t);
+        u32x4 o;
+        o.x = run;
+        o.y = o.x + v.x;
+        o.z = o.y + v.y;
+        o.w = o.z + v.z;
+        run = o.w + v.w;
+        *reinterpret_cast<u32x4 *>(ws.tile_pre + t) = o;
+    }
+    for (uint64_t t = lo + ((hi - lo) & ~uint64_t(3)); t < hi; t++) {
+        const uint32_t c = ws.counts[t];
         ws.tile_pre[t] = run;
         run += c;
     }
