@@ -22,11 +22,12 @@
 //                   with 64-lane ballots, ranks them in element order, and
 //                   stages each tile's escapes (position, exponent) compactly
 //                   in the workspace.
-//   k_scan_tiles    single workgroup: exclusive scan of per-tile escape
-//                   counts -> tile prefixes and M. Writes the header, the last
-//                   chunk offset and the zero padding.
-//   k_place_escapes copies each tile's staged escapes to their final position
-//                   and value slots. Writes the per-chunk offsets.
+//   k_group_sums    sums the per-tile escape counts of each group of tiles.
+//   k_place_escapes one workgroup per tile: its escape prefix (group sums
+//                   before its group + tile counts before it in its group),
+//                   then its staged escapes -> final position and value slots,
+//                   and the offsets of its chunks. Workgroup 0 also writes the
+//                   header, the last chunk offset and the zero padding.
 //   k_decode_tile   one pass: 16-byte sign-mantissa loads, 8-byte code loads,
 //                   16-entry lookup in registers (v_perm), merge. The tile's
 //                   escapes go into an LDS bitmap and are applied in registers
@@ -74,47 +75,76 @@ Layout make_layout(uint64_t n, uint32_t C)
 }
 
 // ------------------------------------------------------------ tile shapes --
-constexpr int kThreads = 256;                 // 4 waves of 64
-constexpr int kEncGroups = 4;                 // groups of 8 words per thread
-constexpr int kEncTile = kThreads * kEncGroups * 8;     // 8192 words
-constexpr int kDecGroups = 2;                 // groups of 16 words per thread
-constexpr int kDecTile = kThreads * kDecGroups * 16;    // 8192 words
-static_assert(kEncTile == kDecTile, "encode and decode tiles share the patch map size");
-constexpr int kTile = kEncTile;
-constexpr int kScanThreads = 1024;
+// Compile-time shapes (defaults measured on MI355X; override with -D to sweep).
+#ifndef UZIP_ENC_THREADS
+#define UZIP_ENC_THREADS 256
+#endif
+#ifndef UZIP_ENC_GROUPS
+#define UZIP_ENC_GROUPS 4          // groups of 8 words per thread
+#endif
+#ifndef UZIP_DEC_THREADS
+#define UZIP_DEC_THREADS 256
+#endif
+#ifndef UZIP_DEC_GROUPS
+#define UZIP_DEC_GROUPS 2          // groups of 16 words per thread
+#endif
+#ifndef UZIP_NT
+#define UZIP_NT 1                  // non-temporal streaming loads/stores
+#endif
+
+constexpr int kEncThreads = UZIP_ENC_THREADS;
+constexpr int kEncGroups = UZIP_ENC_GROUPS;
+constexpr int kEncTile = kEncThreads * kEncGroups * 8;
+constexpr int kDecThreads = UZIP_DEC_THREADS;
+constexpr int kDecGroups = UZIP_DEC_GROUPS;
+constexpr int kDecTile = kDecThreads * kDecGroups * 16;
+constexpr int kThreads = 256;               // histogram, placement and patch kernels
+static_assert((kEncTile & (kEncTile - 1)) == 0 && kEncTile <= 65536, "encode tile: power of two <= 65536");
+static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: power of two");
 
 // Encode workspace (see uzip_workspace_bytes).
 struct EncWs {
     uint32_t *counts;      // [ntiles] escapes per tile
-    uint32_t *tile_pre;    // [ntiles + 1] exclusive prefix, then M
+    uint32_t *gsum;        // [ngroups] escapes per group of 2^gshift tiles
     uint32_t *chunk_pre;   // [nch] escapes in the tile before each chunk start
-    uint16_t *stage_pos;   // [ntiles * kTile] in-chunk positions, per tile
-    uint8_t  *stage_val;   // [ntiles * kTile] raw exponents, per tile
+    uint16_t *stage_pos;   // [ntiles * kEncTile] in-chunk positions, per tile
+    uint8_t  *stage_val;   // [ntiles * kEncTile] raw exponents, per tile
 };
 
 struct WsLayout {
-    uint64_t counts, tile_pre, chunk_pre, stage_pos, stage_val, total;
+    uint64_t counts, gsum, chunk_pre, stage_pos, stage_val, total;
 };
+
+// Tiles are summed in groups of 2^gshift, with gshift about half of log2(ntiles)
+// (at least 6), so a tile's prefix reads at most ~2*sqrt(ntiles) counts.
+uint32_t group_shift(uint64_t ntiles)
+{
+    uint32_t lg = 0;
+    while ((1ull << lg) < ntiles) lg++;
+    const uint32_t g = (lg + 1) / 2;
+    return g < 6 ? 6 : g;
+}
 
 WsLayout ws_layout(uint64_t n, uint32_t C)
 {
-    uint64_t ntiles = (n + kTile - 1) / kTile;
+    uint64_t ntiles = (n + kEncTile - 1) / kEncTile;
+    uint64_t ngroups = (ntiles + (1ull << group_shift(ntiles)) - 1) >> group_shift(ntiles);
     uint64_t nch = (n + C - 1) / C;
     WsLayout w;
     w.counts = 0;
-    w.tile_pre = w.counts + align256(4 * ntiles);
-    w.chunk_pre = w.tile_pre + align256(4 * (ntiles + 1));
+    w.gsum = w.counts + align256(4 * ntiles);
+    w.chunk_pre = w.gsum + align256(4 * ngroups);
     w.stage_pos = w.chunk_pre + align256(4 * nch);
-    w.stage_val = w.stage_pos + align256(2 * ntiles * kTile);
-    w.total = w.stage_val + align256(ntiles * kTile);
+    w.stage_val = w.stage_pos + align256(2 * ntiles * kEncTile);
+    w.total = w.stage_val + align256(ntiles * kEncTile);
     return w;
 }
 
 // Per-launch constants of an encoder (kernel argument, by value).
 struct EncParams {
     uint8_t lut[256];      // code of e in bits 0..3, bit 7 set when e is an escape
-    uint64_t n, nch, ntiles;
-    uint32_t Cmask, logC;
+    uint64_t n, nch, ntiles, ngroups;
+    uint32_t Cmask, logC, gshift;
     uint64_t off_codes, off_offs, off_pos;
 };
 
@@ -128,8 +158,6 @@ struct DecParams {
 
 struct HeaderParams {
     uint8_t tmpl[256];     // header with M and total_bytes left zero
-    uint64_t n, nch, ntiles;
-    uint64_t off_codes, off_offs, off_pos;
 };
 
 // Native vector types for 8- and 16-byte memory operations.
@@ -138,9 +166,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming loads/stores: every byte is touched once per call.
 template <typename T>
-__device__ __forceinline__ T ld_stream(const T *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ T ld_stream(const T *p)
+{
+#if UZIP_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
 template <typename T>
-__device__ __forceinline__ void st_stream(T v, T *p) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_stream(T v, T *p)
+{
+#if UZIP_NT
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
 
 // --------------------------------------------------------- bit helpers -----
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -219,7 +261,7 @@ __device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t cod
     y[3] = merge2(perm(e47, sm1, 0x07030602u));
 }
 
-// Replace the exponent field of word j (0..1) of a dword.
+// Replace the exponent field of word `half` (0..1) of a dword.
 __device__ __forceinline__ uint32_t set_exp(uint32_t y, int half, uint32_t e)
 {
     uint32_t sh = 7 + 16 * half;
@@ -280,23 +322,33 @@ __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ 
 }
 
 // ============================================================== encode ====
-// Shared encode back end: a thread holds 4 groups of 8 words (group k covers
-// tile words k*2048 + tid*8 .. +8) in xw[k][0..3] and valid counts.
+// LDS of the encode back end.
 struct EncShared {
     uint8_t lut[256];
-    uint32_t wtot[kEncGroups][kThreads / 64];
+    uint32_t wtot[kEncGroups][kEncThreads / 64];
+};
+// A tile's escapes in element order (compacted), written out with 16-byte stores.
+struct alignas(16) EscBuf {
+    uint16_t pos[kEncTile];
+    uint8_t val[kEncTile];
 };
 
+// Encode back end shared by k_encode_tile and k_reduce_tile. Each thread holds
+// kEncGroups groups of 8 words (group k covers tile words
+// k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
+// xw[k][q]). Writes the dense sections, the tile's escape count, the in-tile
+// prefix at each chunk start, and the tile's escapes (compacted, in element
+// order) to its staging slot.
 __device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], uint64_t t0, uint64_t tile,
                                               uint8_t *__restrict__ out, const EncWs &ws,
-                                              const EncParams &p, EncShared &sh)
+                                              const EncParams &p, EncShared &sh, EscBuf &eb)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t Lw[kEncGroups][2];
     uint32_t pre[kEncGroups];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         uint32_t L0 = 0, L1 = 0;
         if (g0 < p.n) {
             L0 = lut4(sh.lut, xw[k][0], xw[k][1]);
@@ -316,6 +368,8 @@ __device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], 
         }
         Lw[k][0] = L0;
         Lw[k][1] = L1;
+        // escape count of this group -> exclusive prefix over the wave's lanes
+        // (4 ballots over the bits of the count, which is at most 8)
         const uint32_t cnt = __builtin_popcount(L0 & 0x80808080u) + __builtin_popcount(L1 & 0x80808080u);
         uint32_t wt = 0, pr = 0;
         if (__ballot(cnt != 0) != 0ull) {
@@ -329,49 +383,61 @@ __device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], 
         if (lane == 0) sh.wtot[k][wave] = wt;
     }
     __syncthreads();
+    // element order inside the tile is (group k, wave, lane, word)
     uint32_t run = 0, base[kEncGroups];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; w++) {
+        for (int w = 0; w < kEncThreads / 64; w++) {
             if (w == wave) base[k] = run;
             run += sh.wtot[k][w];
         }
     }
-    if (tid == 0) ws.counts[tile] = run;
+    const uint32_t m = run;
+    if (tid == 0) ws.counts[tile] = m;
     const uint32_t C = p.Cmask + 1;
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         uint32_t rank = base[k] + pre[k];
-        if (C < (uint32_t)kTile && g0 < p.n && (g0 & p.Cmask) == 0)
+        if (C < (uint32_t)kEncTile && g0 < p.n && (g0 & p.Cmask) == 0)
             ws.chunk_pre[g0 >> p.logC] = rank;
         uint64_t esc = ((uint64_t)(Lw[k][1] & 0x80808080u) << 32) | (Lw[k][0] & 0x80808080u);
         while (esc) {
-            const int bit = __builtin_ctzll(esc);
-            const int j = bit >> 3;                       // word within the group
+            const int j = __builtin_ctzll(esc) >> 3;       // word within the group
             const uint32_t w = xw[k][j >> 1] >> (16 * (j & 1));
-            const uint64_t i = g0 + j;
-            ws.stage_pos[tile * kTile + rank] = (uint16_t)(i & p.Cmask);
-            ws.stage_val[tile * kTile + rank] = (uint8_t)((w >> 7) & 0xFFu);
+            eb.pos[rank] = (uint16_t)((g0 + j) & p.Cmask);
+            eb.val[rank] = (uint8_t)((w >> 7) & 0xFFu);
             rank++;
             esc &= esc - 1;
         }
     }
+    if (m == 0) return;
+    __syncthreads();
+    // copy the compacted list to the tile's staging slot, 16 bytes per store
+    // (the last store of each array may carry stale bytes past m: the slot is
+    // scratch and only its first m entries are read)
+    u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_pos + tile * kEncTile);
+    const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
+    for (uint32_t q = tid; q < (m + 7) / 8; q += kEncThreads) sp[q] = lp[q];
+    u32x4 *sv = reinterpret_cast<u32x4 *>(ws.stage_val + tile * kEncTile);
+    const u32x4 *lv = reinterpret_cast<const u32x4 *>(eb.val);
+    for (uint32_t q = tid; q < (m + 15) / 16; q += kEncThreads) sv[q] = lv[q];
 }
 
-__global__ __launch_bounds__(kThreads) void k_encode_tile(const uint16_t *__restrict__ x,
-                                                          uint8_t *__restrict__ out, EncWs ws, EncParams p)
+__global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__restrict__ x,
+                                                             uint8_t *__restrict__ out, EncWs ws, EncParams p)
 {
     __shared__ EncShared sh;
+    __shared__ EscBuf eb;
     const int tid = threadIdx.x;
     if (tid < 64) reinterpret_cast<uint32_t *>(sh.lut)[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
     const uint64_t tile = blockIdx.x;
-    const uint64_t t0 = tile * kTile;
+    const uint64_t t0 = tile * kEncTile;
     uint32_t xw[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         if (g0 + 8 <= p.n) {
             const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + g0));
             xw[k][0] = v.x; xw[k][1] = v.y; xw[k][2] = v.z; xw[k][3] = v.w;
@@ -384,71 +450,114 @@ __global__ __launch_bounds__(kThreads) void k_encode_tile(const uint16_t *__rest
         }
     }
     __syncthreads();
-    encode_groups(xw, t0, tile, out, ws, p, sh);
+    encode_groups(xw, t0, tile, out, ws, p, sh, eb);
 }
 
-// Single workgroup. tile_pre[t] = escapes before tile t; tile_pre[ntiles] = M.
-// Also writes the header, offsets[nch] = M and every padding byte.
-// Each thread owns a contiguous run of `per` tiles (a multiple of 4, so the
-// run is read and written with 16-byte accesses).
-__global__ __launch_bounds__(kScanThreads) void k_scan_tiles(EncWs ws, uint8_t *__restrict__ out, HeaderParams hp)
+// gsum[g] = escapes in tiles [g << gshift, (g + 1) << gshift).
+__global__ __launch_bounds__(kThreads) void k_group_sums(EncWs ws, EncParams p)
 {
-    __shared__ uint32_t s_wave[kScanThreads / 64];
-    __shared__ uint32_t s_total;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint64_t per = ((hp.ntiles + kScanThreads - 1) / kScanThreads + 3) & ~uint64_t(3);
-    const uint64_t lo = tid * per;
-    const uint64_t hi = (lo + per < hp.ntiles) ? lo + per : (lo < hp.ntiles ? hp.ntiles : lo);
+    __shared__ uint32_t s_red[kThreads / 64];
+    const int tid = threadIdx.x;
+    const uint64_t lo = (uint64_t)blockIdx.x << p.gshift;
+    uint64_t hi = lo + (1ull << p.gshift);
+    if (hi > p.ntiles) hi = p.ntiles;
     uint32_t sum = 0;
-#pragma unroll 8
-    for (uint64_t t = lo; t + 4 <= hi; t += 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ws.counts + t);
-        sum += v.x + v.y + v.z + v.w;
-    }
-    for (uint64_t t = lo + ((hi - lo) & ~uint64_t(3)); t < hi; t++) sum += ws.counts[t];
-    // inclusive scan across the wave
-    uint32_t inc = sum;
+    for (uint64_t t = lo + tid; t < hi; t += kThreads) sum += ws.counts[t];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t v = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += v;
-    }
-    if (lane == 63) s_wave[wave] = inc;
+    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+    if ((tid & 63) == 0) s_red[tid >> 6] = sum;
     __syncthreads();
-    if (tid < 64) {
-        // exclusive scan of the 16 wave totals in one wave
-        uint32_t v = (tid < kScanThreads / 64) ? s_wave[tid] : 0u;
-        uint32_t x = v;
+    if (tid == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < kThreads / 64; w++) t += s_red[w];
+        ws.gsum[blockIdx.x] = t;
+    }
+}
+
+// Sums of three per-thread values over the workgroup (every thread gets them).
+__device__ __forceinline__ void block_sum3(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t (*s_red)[kThreads / 64])
+{
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            uint32_t u = __shfl_up(x, d, 64);
-            if (lane >= d) x += u;
+    for (int d = 32; d >= 1; d >>= 1) {
+        a += __shfl_xor(a, d, 64);
+        b += __shfl_xor(b, d, 64);
+        c += __shfl_xor(c, d, 64);
+    }
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) {
+        s_red[0][tid >> 6] = a;
+        s_red[1][tid >> 6] = b;
+        s_red[2][tid >> 6] = c;
+    }
+    __syncthreads();
+    a = b = c = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++) {
+        a += s_red[0][w];
+        b += s_red[1][w];
+        c += s_red[2][w];
+    }
+}
+
+// One workgroup per encode tile. Its escape prefix P = (group sums before
+// its group) + (tile counts before it inside its group); M = all group sums.
+// Copies the tile's staged escapes to pos[P..], val[P..] and writes the
+// offsets of the chunks that start in the tile. Workgroup 0 also writes the
+// header, offsets[nch] = M and every padding byte.
+__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
+                                                            HeaderParams hp)
+{
+    __shared__ uint32_t s_red[3][kThreads / 64];
+    const uint64_t tile = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint64_t g = tile >> p.gshift;
+    const uint64_t gfirst = g << p.gshift;
+    uint32_t before_g = 0, all = 0, in_g = 0;
+    for (uint64_t q = tid; q < p.ngroups; q += kThreads) {
+        const uint32_t v = ws.gsum[q];
+        all += v;
+        if (q < g) before_g += v;
+    }
+    for (uint64_t t = gfirst + tid; t < tile; t += kThreads) in_g += ws.counts[t];
+    block_sum3(before_g, all, in_g, s_red);
+    const uint32_t P = before_g + in_g;
+    const uint64_t M = all;
+    const uint32_t m = ws.counts[tile];
+    const uint64_t off_val = p.off_pos + align256(2 * M);
+    uint16_t *pos = reinterpret_cast<uint16_t *>(out + p.off_pos) + P;
+    uint8_t *val = out + off_val + P;
+    const uint16_t *sp = ws.stage_pos + tile * kEncTile;
+    const uint8_t *sv = ws.stage_val + tile * kEncTile;
+    for (uint32_t jb = 0; jb < m; jb += 4 * kThreads) {
+        uint32_t ps[4], vs[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t j = jb + u * kThreads + tid;
+            ps[u] = (j < m) ? sp[j] : 0u;
+            vs[u] = (j < m) ? sv[j] : 0u;
         }
-        if (tid < kScanThreads / 64) s_wave[tid] = x - v;
-        if (tid == 63) s_total = x;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t j = jb + u * kThreads + tid;
+            if (j < m) {
+                st_stream((uint16_t)ps[u], pos + j);
+                st_stream((uint8_t)vs[u], val + j);
+            }
+        }
     }
-    __syncthreads();
-    uint32_t run = s_wave[wave] + inc - sum;
-#pragma unroll 8
-    for (uint64_t t = lo; t + 4 <= hi; t += 4) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ws.counts + t);
-        u32x4 o;
-        o.x = run;
-        o.y = o.x + v.x;
-        o.z = o.y + v.y;
-        o.w = o.z + v.z;
-        run = o.w + v.w;
-        *reinterpret_cast<u32x4 *>(ws.tile_pre + t) = o;
+    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
+    const uint64_t t0 = tile * kEncTile;
+    const uint32_t C = p.Cmask + 1;
+    if (C < (uint32_t)kEncTile) {
+        const uint64_t c0 = t0 >> p.logC;
+        uint64_t cn = (uint64_t)kEncTile >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
+        for (uint64_t i = tid; i < cn; i += kThreads) offs[c0 + i] = P + ws.chunk_pre[c0 + i];
+    } else if ((t0 & p.Cmask) == 0 && tid == 0) {
+        offs[t0 >> p.logC] = P;
     }
-    for (uint64_t t = lo + ((hi - lo) & ~uint64_t(3)); t < hi; t++) {
-        const uint32_t c = ws.counts[t];
-        ws.tile_pre[t] = run;
-        run += c;
-    }
-    const uint64_t M = s_total;
-    if (tid == 0) ws.tile_pre[hp.ntiles] = (uint32_t)M;
+    if (tile != 0) return;
     // header: template + M + total_bytes
-    const uint64_t off_val = hp.off_pos + align256(2 * M);
     const uint64_t total = off_val + M;
     if (tid < 64) {
         uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[tid];
@@ -458,44 +567,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(EncWs ws, uint8_t *
         if (tid == 9) w = (uint32_t)(total >> 32);
         reinterpret_cast<uint32_t *>(out)[tid] = w;
     }
-    if (tid == 64) reinterpret_cast<uint32_t *>(out + hp.off_offs)[hp.nch] = (uint32_t)M;
+    if (tid == 64) offs[p.nch] = (uint32_t)M;
     // zero padding after each section (each gap is under 256 bytes)
-    if (tid < 256) {
-        const uint64_t sm_end = kHeader + hp.n;
-        if (sm_end + tid < hp.off_codes) out[sm_end + tid] = 0;
-        const uint64_t codes_end = hp.off_codes + (hp.n + 1) / 2;
-        if (codes_end + tid < hp.off_offs) out[codes_end + tid] = 0;
-        const uint64_t offs_end = hp.off_offs + 4 * (hp.nch + 1);
-        if (offs_end + tid < hp.off_pos) out[offs_end + tid] = 0;
-        const uint64_t pos_end = hp.off_pos + 2 * M;
-        if (pos_end + tid < off_val) out[pos_end + tid] = 0;
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p)
-{
-    const uint64_t tile = blockIdx.x;
-    const int tid = threadIdx.x;
-    const uint32_t P = ws.tile_pre[tile];
-    const uint32_t m = ws.counts[tile];
-    const uint64_t M = ws.tile_pre[p.ntiles];
-    uint16_t *pos = reinterpret_cast<uint16_t *>(out + p.off_pos);
-    uint8_t *val = out + p.off_pos + align256(2 * M);
-    for (uint32_t j = tid; j < m; j += kThreads) {
-        pos[P + j] = ws.stage_pos[tile * kTile + j];
-        val[P + j] = ws.stage_val[tile * kTile + j];
-    }
-    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
-    const uint64_t t0 = tile * kTile;
-    const uint32_t C = p.Cmask + 1;
-    if (C < (uint32_t)kTile) {
-        const uint64_t c0 = t0 >> p.logC;
-        uint64_t cn = (uint64_t)kTile >> p.logC;
-        if (c0 + cn > p.nch) cn = p.nch - c0;
-        for (uint64_t i = tid; i < cn; i += kThreads) offs[c0 + i] = P + ws.chunk_pre[c0 + i];
-    } else if ((t0 & p.Cmask) == 0 && tid == 0) {
-        offs[t0 >> p.logC] = P;
-    }
+    const uint64_t sm_end = kHeader + p.n;
+    if (sm_end + tid < p.off_codes) out[sm_end + tid] = 0;
+    const uint64_t codes_end = p.off_codes + (p.n + 1) / 2;
+    if (codes_end + tid < p.off_offs) out[codes_end + tid] = 0;
+    const uint64_t offs_end = p.off_offs + 4 * (p.nch + 1);
+    if (offs_end + tid < p.off_pos) out[offs_end + tid] = 0;
+    const uint64_t pos_end = p.off_pos + 2 * M;
+    if (pos_end + tid < off_val) out[pos_end + tid] = 0;
 }
 
 // ============================================================== decode ====
@@ -505,17 +586,20 @@ struct StreamIn {
     uint64_t bytes;       // readable bytes at base
 };
 
+// Patch map of a tile of TILE words: escape bitmap + each escape's exponent,
+// and the tile's chunk offsets.
+template <int TILE>
 struct PatchShared {
-    uint32_t mask[kTile / 32];
-    uint8_t val[kTile];
-    uint32_t offs[kTile / 64 + 1];
-    uint32_t range[2];
+    uint32_t mask[TILE / 32];
+    uint8_t val[TILE];
+    uint32_t offs[TILE / 64 + 1];
 };
 
-// Escape range [E0, E1) of the tile's words [t0, t0 + kTile) and its patch
-// map in LDS. Returns false when the tile has no escapes. Every thread of
-// the workgroup calls it; it ends with a barrier when it returns true.
-__device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams &p, PatchShared &sh)
+// Builds the patch map of the tile's words [t0, t0 + TILE) with NT threads.
+// Returns false when the tile has no escapes. Every thread of the workgroup
+// calls it; when it returns true it has ended with a barrier.
+template <int TILE, int NT>
+__device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams &p, PatchShared<TILE> &sh)
 {
     const int tid = threadIdx.x;
     // M from the header; a value that does not fit the buffer disables the patch
@@ -524,10 +608,11 @@ __device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams 
     const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs);
     const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos);
     const uint8_t *val = s.base + p.off_pos + align256(2 * M);
-    const uint64_t tile_end = (t0 + kTile < p.n) ? t0 + kTile : p.n;
+    const uint64_t tile_end = (t0 + TILE < p.n) ? t0 + TILE : p.n;
     uint64_t E0, E1;
-    const bool small_chunks = p.C <= (uint32_t)kTile;
-    uint64_t c0 = t0 >> p.logC, nc = 0;
+    const bool small_chunks = p.C <= (uint32_t)TILE;
+    const uint64_t c0 = t0 >> p.logC;
+    uint64_t nc = 0;
     if (small_chunks) {
         nc = ((tile_end - 1) >> p.logC) - c0 + 1;
         E0 = offs[c0];
@@ -536,17 +621,17 @@ __device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams 
         if (E0 > E1) E0 = E1;
     } else {
         // one chunk spans several tiles: find the escapes whose position
-        // falls in this tile by a 256-way search over the ascending positions
+        // falls in this tile by an NT-way search over the ascending positions
         uint64_t lo = offs[c0], hi = offs[c0 + 1];
         if (hi > M) hi = M;
         if (lo > hi) lo = hi;
         const uint32_t rel0 = (uint32_t)(t0 - (c0 << p.logC));
         uint64_t res[2];
         for (int side = 0; side < 2; side++) {
-            const uint32_t target = rel0 + (side ? (uint32_t)kTile : 0u);
+            const uint32_t target = rel0 + (side ? (uint32_t)TILE : 0u);
             uint64_t a = lo, b = hi;            // answer in [a, b]
-            while (b - a > (uint64_t)kThreads) {
-                const uint64_t step = (b - a + kThreads - 1) / kThreads;
+            while (b - a > (uint64_t)NT) {
+                const uint64_t step = (b - a + NT - 1) / NT;
                 const uint64_t j = a + (uint64_t)tid * step;
                 const int below = (j < b) && (pos[j] < target);
                 const int cnt = __syncthreads_count(below);
@@ -562,46 +647,56 @@ __device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams 
         }
         E0 = res[0];
         E1 = res[1];
-        lo = res[0];
-        (void)lo;
     }
     if (E1 <= E0) return false;
-    for (int i = tid; i < kTile / 32; i += kThreads) sh.mask[i] = 0;
+    for (int i = tid; i < TILE / 32; i += NT) sh.mask[i] = 0;
     if (small_chunks)
-        for (uint64_t q = tid; q <= nc; q += kThreads) {
-            uint32_t o = offs[c0 + q];
+        for (uint64_t q = tid; q <= nc; q += NT) {
+            const uint32_t o = offs[c0 + q];
             sh.offs[q] = o > (uint32_t)E1 ? (uint32_t)E1 : o;
         }
     __syncthreads();
-    for (uint64_t j = E0 + tid; j < E1; j += kThreads) {
-        const uint32_t ps = pos[j];
-        uint64_t li;
-        if (small_chunks) {
-            // last chunk q with offs[q] <= j
-            uint32_t a = 0, b = (uint32_t)nc;   // offs[a] <= j < offs[b]
-            while (b - a > 1) {
-                const uint32_t mid = (a + b) >> 1;
-                if (sh.offs[mid] <= (uint32_t)j) a = mid; else b = mid;
-            }
-            li = ((uint64_t)a << p.logC) + ps;
-        } else {
-            li = (c0 << p.logC) + ps - t0;    // may wrap for a corrupt position
+    for (uint64_t jb = E0; jb < E1; jb += 4 * NT) {
+        uint32_t ps[4], vv[4];
+        // issue the loads of 4 escapes per thread before using any of them
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint64_t j = jb + (uint64_t)u * NT + tid;
+            ps[u] = (j < E1) ? pos[j] : 0xFFFFFFFFu;
+            vv[u] = (j < E1) ? val[j] : 0u;
         }
-        if (ps < p.C && li < (uint64_t)kTile && t0 + li < p.n) {
-            sh.val[li] = val[j];
-            atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint64_t j = jb + (uint64_t)u * NT + tid;
+            if (j >= E1) continue;
+            uint64_t li;
+            if (small_chunks) {
+                // last chunk q with offs[q] <= j
+                uint32_t a = 0, b = (uint32_t)nc;   // offs[a] <= j < offs[b]
+                while (b - a > 1) {
+                    const uint32_t mid = (a + b) >> 1;
+                    if (sh.offs[mid] <= (uint32_t)j) a = mid; else b = mid;
+                }
+                li = ((uint64_t)a << p.logC) + ps[u];
+            } else {
+                li = (c0 << p.logC) + ps[u] - t0;    // wraps for a corrupt position
+            }
+            if (ps[u] < p.C && li < (uint64_t)TILE && t0 + li < p.n) {
+                sh.val[li] = (uint8_t)vv[u];
+                atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
+            }
         }
     }
     __syncthreads();
     return true;
 }
 
-// Apply the patch map to the `NW` words of a thread's group starting at tile
+// Apply the patch map to the NW words of a thread's group starting at tile
 // word li0 (y holds NW/2 dwords).
-template <int NW>
-__device__ __forceinline__ void apply_patch(const PatchShared &sh, uint32_t li0, uint32_t *y)
+template <int NW, int TILE>
+__device__ __forceinline__ void apply_patch(const PatchShared<TILE> &sh, uint32_t li0, uint32_t *y)
 {
-    uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & ((NW == 32) ? 0xFFFFFFFFu : ((1u << NW) - 1u));
+    const uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & ((1u << NW) - 1u);
     if (bits == 0) return;
 #pragma unroll
     for (int j = 0; j < NW; j++)
@@ -609,16 +704,16 @@ __device__ __forceinline__ void apply_patch(const PatchShared &sh, uint32_t li0,
 }
 
 template <bool kPatch>
-__global__ __launch_bounds__(kThreads) void k_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+__global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
 {
-    __shared__ PatchShared sh;
+    __shared__ PatchShared<kDecTile> sh;
     const int tid = threadIdx.x;
-    const uint64_t t0 = (uint64_t)blockIdx.x * kTile;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kDecTile;
     uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
     uint32_t out[kDecGroups][8];
 #pragma unroll
     for (int k = 0; k < kDecGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 16) + (uint64_t)tid * 16;
+        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 16) + (uint64_t)tid * 16;
         if (g0 < p.n) {
             // sections are padded to 256 bytes, so a tail group's full loads stay inside them
             const u32x4 sm = ld_stream(reinterpret_cast<const u32x4 *>(s.base + kHeader + g0));
@@ -628,15 +723,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_tile(StreamIn s, uint16_t *
         }
     }
     if (kPatch) {
-        if (build_patch_map(s, t0, p, sh)) {
+        if (build_patch_map<kDecTile, kDecThreads>(s, t0, p, sh)) {
 #pragma unroll
             for (int k = 0; k < kDecGroups; k++)
-                apply_patch<16>(sh, (uint32_t)(k * (kThreads * 16) + tid * 16), out[k]);
+                apply_patch<16>(sh, (uint32_t)(k * (kDecThreads * 16) + tid * 16), out[k]);
         }
     }
 #pragma unroll
     for (int k = 0; k < kDecGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 16) + (uint64_t)tid * 16;
+        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 16) + (uint64_t)tid * 16;
         if (g0 + 16 <= p.n) {
             u32x4 *dst = reinterpret_cast<u32x4 *>(y + g0);
             u32x4 v0 = {out[k][0], out[k][1], out[k][2], out[k][3]};
@@ -676,20 +771,27 @@ __global__ __launch_bounds__(kThreads) void k_patch(StreamIn s, uint16_t *__rest
 }
 
 // ============================================================== reduce ====
-__global__ __launch_bounds__(kThreads) void k_reduce_tile(StreamIn sa, StreamIn sb, uint8_t *__restrict__ out,
-                                                          EncWs ws, EncParams ep, DecParams dp)
+// LDS: the patch map (used while decoding) and the escape list (used while
+// encoding) are never live at the same time.
+union ReduceLds {
+    PatchShared<kEncTile> patch;
+    EscBuf esc;
+};
+
+__global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, StreamIn sb, uint8_t *__restrict__ out,
+                                                             EncWs ws, EncParams ep, DecParams dp)
 {
     __shared__ EncShared esh;
-    __shared__ PatchShared psh;
+    __shared__ ReduceLds lds;
     const int tid = threadIdx.x;
     if (tid < 64) reinterpret_cast<uint32_t *>(esh.lut)[tid] = reinterpret_cast<const uint32_t *>(ep.lut)[tid];
     const uint64_t tile = blockIdx.x;
-    const uint64_t t0 = tile * kTile;
+    const uint64_t t0 = tile * kEncTile;
     uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
     uint32_t ya[kEncGroups][4], yb[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kThreads * 8) + (uint64_t)tid * 8;
+        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         if (g0 < dp.n) {
             const u32x2 sma = ld_stream(reinterpret_cast<const u32x2 *>(sa.base + kHeader + g0));
             const uint32_t cda = ld_stream(reinterpret_cast<const uint32_t *>(sa.base + dp.off_codes + g0 / 2));
@@ -702,23 +804,25 @@ __global__ __launch_bounds__(kThreads) void k_reduce_tile(StreamIn sa, StreamIn 
             for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
         }
     }
-    if (build_patch_map(sa, t0, dp, psh)) {
+    if (build_patch_map<kEncTile, kEncThreads>(sa, t0, dp, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch<8>(psh, (uint32_t)(k * (kThreads * 8) + tid * 8), ya[k]);
+            apply_patch<8>(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ya[k]);
     }
     __syncthreads();       // the map is rebuilt for the second input
-    if (build_patch_map(sb, t0, dp, psh)) {
+    if (build_patch_map<kEncTile, kEncThreads>(sb, t0, dp, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch<8>(psh, (uint32_t)(k * (kThreads * 8) + tid * 8), yb[k]);
+            apply_patch<8>(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), yb[k]);
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++)
 #pragma unroll
         for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[k][q], yb[k][q]);
-    encode_groups(r, t0, tile, out, ws, ep, esh);
+    // encode_groups writes the escape list only after its first barrier, which
+    // every thread reaches after its last read of the patch map
+    encode_groups(r, t0, tile, out, ws, ep, esh, lds.esc);
 }
 
 // ================================================================ host ====
@@ -770,7 +874,9 @@ EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
     for (int k = 0; k < 16; k++) p.lut[cb->dec[k]] = (uint8_t)k;
     p.n = L.n;
     p.nch = L.nch;
-    p.ntiles = (L.n + kTile - 1) / kTile;
+    p.ntiles = (L.n + kEncTile - 1) / kEncTile;
+    p.gshift = group_shift(p.ntiles);
+    p.ngroups = (p.ntiles + (1ull << p.gshift) - 1) >> p.gshift;
     p.Cmask = L.C - 1;
     p.logC = L.logC;
     p.off_codes = L.off_codes;
@@ -803,12 +909,6 @@ HeaderParams make_header_params(const Layout &L, const uzip_codebook_t *cb)
     memcpy(h.tmpl + 8, &L.C, 4);
     memcpy(h.tmpl + 16, &L.n, 8);
     memcpy(h.tmpl + 40, cb->dec, 16);
-    h.n = L.n;
-    h.nch = L.nch;
-    h.ntiles = (L.n + kTile - 1) / kTile;
-    h.off_codes = L.off_codes;
-    h.off_offs = L.off_offs;
-    h.off_pos = L.off_pos;
     return h;
 }
 
@@ -818,7 +918,7 @@ EncWs make_ws(void *d_ws, uint64_t n, uint32_t C)
     uint8_t *b = static_cast<uint8_t *>(d_ws);
     EncWs ws;
     ws.counts = reinterpret_cast<uint32_t *>(b + w.counts);
-    ws.tile_pre = reinterpret_cast<uint32_t *>(b + w.tile_pre);
+    ws.gsum = reinterpret_cast<uint32_t *>(b + w.gsum);
     ws.chunk_pre = reinterpret_cast<uint32_t *>(b + w.chunk_pre);
     ws.stage_pos = reinterpret_cast<uint16_t *>(b + w.stage_pos);
     ws.stage_val = b + w.stage_val;
@@ -841,11 +941,11 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
                   uint8_t *out, const Events &ev, hipStream_t s)
 {
     const HeaderParams hp = make_header_params(L, cb);
-    k_scan_tiles<<<1, kScanThreads, 0, s>>>(ws, out, hp);
-    UZIP_LAUNCH_CHECK("k_scan_tiles");
+    k_group_sums<<<(unsigned)ep.ngroups, kThreads, 0, s>>>(ws, ep);
+    UZIP_LAUNCH_CHECK("k_group_sums");
     int rc = ev.record(2);
     if (rc) return rc;
-    k_place_escapes<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(ws, out, ep);
+    k_place_escapes<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
     return ev.record(3);
 }
@@ -1026,7 +1126,7 @@ int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_c
     const EncWs ws = make_ws(d_ws, n, chunk);
     const Events ev{opts, s};
     if ((rc = ev.record(0))) return rc;
-    k_encode_tile<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    k_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
     UZIP_LAUNCH_CHECK("k_encode_tile");
     if ((rc = ev.record(1))) return rc;
     return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
@@ -1060,11 +1160,11 @@ int uzip_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chu
     if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;   // smaller than any stream of n values
     const DecParams dp = make_dec_params(L, cb);
     const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
-    const unsigned grid = (unsigned)((n + kTile - 1) / kTile);
+    const unsigned grid = (unsigned)((n + kDecTile - 1) / kDecTile);
     const Events ev{opts, s};
     if ((rc = ev.record(0))) return rc;
     if (opts && (opts->flags & UZIP_F_SEPARATE_PATCH)) {
-        k_decode_tile<false><<<grid, kThreads, 0, s>>>(si, d_y, dp);
+        k_decode_tile<false><<<grid, kDecThreads, 0, s>>>(si, d_y, dp);
         UZIP_LAUNCH_CHECK("k_decode_tile<dense>");
         if ((rc = ev.record(1))) return rc;
         uint64_t wgs = (L.nch + (kThreads / 64) - 1) / (kThreads / 64);
@@ -1072,7 +1172,7 @@ int uzip_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chu
         UZIP_LAUNCH_CHECK("k_patch");
         return ev.record(2);
     }
-    k_decode_tile<true><<<grid, kThreads, 0, s>>>(si, d_y, dp);
+    k_decode_tile<true><<<grid, kDecThreads, 0, s>>>(si, d_y, dp);
     UZIP_LAUNCH_CHECK("k_decode_tile");
     return ev.record(1);
 }
@@ -1103,7 +1203,7 @@ int uzip_reduce_add_ex(const void *d_a, uint64_t a_bytes, const void *d_b, uint6
     const StreamIn sb{static_cast<const uint8_t *>(d_b), b_bytes};
     const Events ev{opts, s};
     if ((rc = ev.record(0))) return rc;
-    k_reduce_tile<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(sa, sb, static_cast<uint8_t *>(d_out), ws, ep, dp);
+    k_reduce_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(sa, sb, static_cast<uint8_t *>(d_out), ws, ep, dp);
     UZIP_LAUNCH_CHECK("k_reduce_tile");
     if ((rc = ev.record(1))) return rc;
     return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
