@@ -23,11 +23,12 @@
 //                   stages each tile's escapes (position, exponent) compactly
 //                   in the workspace.
 //   k_group_sums    sums the per-tile escape counts of each group of tiles.
-//   k_place_escapes one workgroup per tile: its escape prefix (group sums
-//                   before its group + tile counts before it in its group),
-//                   then its staged escapes -> final position and value slots,
-//                   and the offsets of its chunks. Workgroup 0 also writes the
-//                   header, the last chunk offset and the zero padding.
+//   k_place_escapes one wave per tile: its escape prefix (group sums before
+//                   its group + tile counts before it in its group), then its
+//                   staged escapes -> final position and value slots by
+//                   16-byte shifted block copies, and the offsets of its
+//                   chunks. Tile 0 also writes the header, the last chunk
+//                   offset and the zero padding.
 //   k_decode_tile   one pass: 16-byte sign-mantissa loads, 8-byte code loads,
 //                   16-entry lookup in registers (v_perm), merge. The tile's
 //                   escapes go into an LDS bitmap and are applied in registers
@@ -91,6 +92,10 @@ Layout make_layout(uint64_t n, uint32_t C)
 #ifndef UZIP_NT
 #define UZIP_NT 1                  // non-temporal streaming loads/stores
 #endif
+#ifndef UZIP_PLACE_TILES
+#define UZIP_PLACE_TILES 1         // encode tiles per escape-placement wave
+#endif
+
 
 constexpr int kEncThreads = UZIP_ENC_THREADS;
 constexpr int kEncGroups = UZIP_ENC_GROUPS;
@@ -99,6 +104,8 @@ constexpr int kDecThreads = UZIP_DEC_THREADS;
 constexpr int kDecGroups = UZIP_DEC_GROUPS;
 constexpr int kDecTile = kDecThreads * kDecGroups * 16;
 constexpr int kThreads = 256;               // histogram, placement and patch kernels
+constexpr int kPlaceTiles = UZIP_PLACE_TILES;
+
 static_assert((kEncTile & (kEncTile - 1)) == 0 && kEncTile <= 65536, "encode tile: power of two <= 65536");
 static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: power of two");
 
@@ -136,7 +143,7 @@ WsLayout ws_layout(uint64_t n, uint32_t C)
     w.chunk_pre = w.gsum + align256(4 * ngroups);
     w.stage_pos = w.chunk_pre + align256(4 * nch);
     w.stage_val = w.stage_pos + align256(2 * ntiles * kEncTile);
-    w.total = w.stage_val + align256(ntiles * kEncTile);
+    w.total = w.stage_val + align256(ntiles * kEncTile) + 256;   // slack for 16-byte over-reads
     return w;
 }
 
@@ -285,10 +292,6 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
     return r0 | (r1 << 16);
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt()
-{
-    return (1ull << (threadIdx.x & 63)) - 1ull;
-}
 
 // =========================================================== histogram ====
 __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n,
@@ -333,19 +336,27 @@ struct alignas(16) EscBuf {
     uint8_t val[kEncTile];
 };
 
-// Encode back end shared by k_encode_tile and k_reduce_tile. Each thread holds
-// kEncGroups groups of 8 words (group k covers tile words
+// Number of set bits of b in the lanes below this one (wave64).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t b)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
+// holds kEncGroups groups of 8 words (group k covers tile words
 // k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
-// xw[k][q]). Writes the dense sections, the tile's escape count, the in-tile
-// prefix at each chunk start, and the tile's escapes (compacted, in element
-// order) to its staging slot.
-__device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], uint64_t t0, uint64_t tile,
-                                              uint8_t *__restrict__ out, const EncWs &ws,
-                                              const EncParams &p, EncShared &sh, EscBuf &eb)
+// xw[k][q]). Writes the dense sections and lists the tile's escapes in
+// element order in LDS (eb). Returns the tile's escape count m (the same in
+// every thread). cstart[k] is the number of the tile's escapes before group k
+// when group k starts a chunk, else ~0u. Ends without a barrier after the LDS
+// writes of eb.
+__device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0,
+                                                      uint8_t *__restrict__ out, const EncParams &p,
+                                                      EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t Lw[kEncGroups][2];
-    uint32_t pre[kEncGroups];
+    uint32_t Lw[kEncGroups][2], sm[kEncGroups][2], cw[kEncGroups];
+    // table lookups and dense values for every group, then all the stores
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
@@ -360,23 +371,35 @@ __device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], 
                 L0 = (uint32_t)both;
                 L1 = (uint32_t)(both >> 32);
             }
-            u32x2 smv;
-            smv.x = signmant4(xw[k][0], xw[k][1]);
-            smv.y = signmant4(xw[k][2], xw[k][3]);
-            st_stream(smv, reinterpret_cast<u32x2 *>(out + kHeader + g0));
-            st_stream(pack_codes8(L0, L1), reinterpret_cast<uint32_t *>(out + p.off_codes + g0 / 2));
         }
         Lw[k][0] = L0;
         Lw[k][1] = L1;
-        // escape count of this group -> exclusive prefix over the wave's lanes
-        // (4 ballots over the bits of the count, which is at most 8)
-        const uint32_t cnt = __builtin_popcount(L0 & 0x80808080u) + __builtin_popcount(L1 & 0x80808080u);
+        sm[k][0] = signmant4(xw[k][0], xw[k][1]);
+        sm[k][1] = signmant4(xw[k][2], xw[k][3]);
+        cw[k] = pack_codes8(L0, L1);
+    }
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
+        if (g0 < p.n) {
+            u32x2 smv;
+            smv.x = sm[k][0];
+            smv.y = sm[k][1];
+            st_stream(smv, reinterpret_cast<u32x2 *>(out + kHeader + g0));
+            st_stream(cw[k], reinterpret_cast<uint32_t *>(out + p.off_codes + g0 / 2));
+        }
+    }
+    // escape count of each group -> exclusive prefix over the wave's lanes
+    // (ballots of the 4 bits of the count, which is at most 8)
+    uint32_t pre[kEncGroups];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint32_t cnt = __builtin_popcount(Lw[k][0] & 0x80808080u) + __builtin_popcount(Lw[k][1] & 0x80808080u);
         uint32_t wt = 0, pr = 0;
         if (__ballot(cnt != 0) != 0ull) {
-            const uint64_t lt = lanemask_lt();
             const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u);
             const uint64_t b2 = __ballot(cnt & 4u), b3 = __ballot(cnt & 8u);
-            pr = __popcll(b0 & lt) + 2 * __popcll(b1 & lt) + 4 * __popcll(b2 & lt) + 8 * __popcll(b3 & lt);
+            pr = lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
             wt = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
         }
         pre[k] = pr;
@@ -393,30 +416,50 @@ __device__ __forceinline__ void encode_groups(const uint32_t xw[kEncGroups][4], 
             run += sh.wtot[k][w];
         }
     }
-    const uint32_t m = run;
-    if (tid == 0) ws.counts[tile] = m;
-    const uint32_t C = p.Cmask + 1;
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         uint32_t rank = base[k] + pre[k];
-        if (C < (uint32_t)kEncTile && g0 < p.n && (g0 & p.Cmask) == 0)
-            ws.chunk_pre[g0 >> p.logC] = rank;
-        uint64_t esc = ((uint64_t)(Lw[k][1] & 0x80808080u) << 32) | (Lw[k][0] & 0x80808080u);
-        while (esc) {
-            const int j = __builtin_ctzll(esc) >> 3;       // word within the group
-            const uint32_t w = xw[k][j >> 1] >> (16 * (j & 1));
-            eb.pos[rank] = (uint16_t)((g0 + j) & p.Cmask);
-            eb.val[rank] = (uint8_t)((w >> 7) & 0xFFu);
-            rank++;
-            esc &= esc - 1;
+        cstart[k] = (g0 < p.n && (g0 & p.Cmask) == 0) ? rank : ~0u;
+        const uint32_t g0m = (uint32_t)(g0 & p.Cmask);     // a multiple of 8, below C
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t mask = Lw[k][h] & 0x80808080u;
+            if (mask == 0) continue;
+            // exponents of words 4h..4h+3, one per byte
+            const uint32_t ex = perm(xw[k][2 * h + 1] >> 7, xw[k][2 * h] >> 7, 0x06040200u);
+            while (mask) {
+                const uint32_t bit = __builtin_ctz(mask);          // 7, 15, 23 or 31
+                eb.pos[rank] = (uint16_t)(g0m + 4 * h + (bit >> 3));
+                eb.val[rank] = (uint8_t)(ex >> (bit - 7));
+                rank++;
+                mask &= mask - 1;
+            }
+        }
+    }
+    return run;
+}
+
+// Staging back half: the tile's count, its in-tile prefix at each chunk
+// start, and its escape list copied to the tile's staging slot with 16-byte
+// stores (the last store of each array may carry stale bytes past m: the
+// slot is scratch and only its first m entries are read). The stores are
+// temporal: the placement kernel reads the slot back right away, from the
+// Infinity Cache.
+__device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[kEncGroups], uint64_t t0,
+                                              uint64_t tile, const EncWs &ws, const EncParams &p, const EscBuf &eb)
+{
+    const int tid = threadIdx.x;
+    if (tid == 0) ws.counts[tile] = m;
+    if (p.Cmask + 1 < (uint32_t)kEncTile) {
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++) {
+            const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
+            if (cstart[k] != ~0u) ws.chunk_pre[g0 >> p.logC] = cstart[k];
         }
     }
     if (m == 0) return;
     __syncthreads();
-    // copy the compacted list to the tile's staging slot, 16 bytes per store
-    // (the last store of each array may carry stale bytes past m: the slot is
-    // scratch and only its first m entries are read)
     u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_pos + tile * kEncTile);
     const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
     for (uint32_t q = tid; q < (m + 7) / 8; q += kEncThreads) sp[q] = lp[q];
@@ -431,7 +474,6 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
     __shared__ EncShared sh;
     __shared__ EscBuf eb;
     const int tid = threadIdx.x;
-    if (tid < 64) reinterpret_cast<uint32_t *>(sh.lut)[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
     uint32_t xw[kEncGroups][4];
@@ -449,8 +491,12 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
             for (int q = 0; q < 4; q++) xw[k][q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
         }
     }
+    // the code table goes to LDS after the data loads are in flight
+    if (tid < 64) reinterpret_cast<uint32_t *>(sh.lut)[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
     __syncthreads();
-    encode_groups(xw, t0, tile, out, ws, p, sh, eb);
+    uint32_t cstart[kEncGroups];
+    const uint32_t m = encode_dense_rank(xw, t0, out, p, sh, eb, cstart);
+    stage_escapes(m, cstart, t0, tile, ws, p, eb);
 }
 
 // gsum[g] = escapes in tiles [g << gshift, (g + 1) << gshift).
@@ -474,109 +520,153 @@ __global__ __launch_bounds__(kThreads) void k_group_sums(EncWs ws, EncParams p)
     }
 }
 
-// Sums of three per-thread values over the workgroup (every thread gets them).
-__device__ __forceinline__ void block_sum3(uint32_t &a, uint32_t &b, uint32_t &c, uint32_t (*s_red)[kThreads / 64])
+// Bytes [r, r + 16) of the 32 bytes lo|hi (r in 0..15, the same in every
+// lane of the wave: the switch does not diverge).
+__device__ __forceinline__ u32x4 extract16(u32x4 lo, u32x4 hi, uint32_t r)
 {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        a += __shfl_xor(a, d, 64);
-        b += __shfl_xor(b, d, 64);
-        c += __shfl_xor(c, d, 64);
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t b = r & 3;
+    u32x4 o;
+    switch (r >> 2) {
+    case 0:
+        o.x = __builtin_amdgcn_alignbyte(d[1], d[0], b); o.y = __builtin_amdgcn_alignbyte(d[2], d[1], b);
+        o.z = __builtin_amdgcn_alignbyte(d[3], d[2], b); o.w = __builtin_amdgcn_alignbyte(d[4], d[3], b);
+        break;
+    case 1:
+        o.x = __builtin_amdgcn_alignbyte(d[2], d[1], b); o.y = __builtin_amdgcn_alignbyte(d[3], d[2], b);
+        o.z = __builtin_amdgcn_alignbyte(d[4], d[3], b); o.w = __builtin_amdgcn_alignbyte(d[5], d[4], b);
+        break;
+    case 2:
+        o.x = __builtin_amdgcn_alignbyte(d[3], d[2], b); o.y = __builtin_amdgcn_alignbyte(d[4], d[3], b);
+        o.z = __builtin_amdgcn_alignbyte(d[5], d[4], b); o.w = __builtin_amdgcn_alignbyte(d[6], d[5], b);
+        break;
+    default:
+        o.x = __builtin_amdgcn_alignbyte(d[4], d[3], b); o.y = __builtin_amdgcn_alignbyte(d[5], d[4], b);
+        o.z = __builtin_amdgcn_alignbyte(d[6], d[5], b); o.w = __builtin_amdgcn_alignbyte(d[7], d[6], b);
+        break;
     }
-    const int tid = threadIdx.x;
-    if ((tid & 63) == 0) {
-        s_red[0][tid >> 6] = a;
-        s_red[1][tid >> 6] = b;
-        s_red[2][tid >> 6] = c;
+    return o;
+}
+
+// One wave copies len bytes from src (16-byte aligned, readable 16 bytes past
+// len) to dst (any alignment). Whole 16-byte blocks of dst are written with
+// one store each (two aligned source loads and a byte funnel); the partial
+// blocks at both ends byte by byte. pf0/pf1 are source blocks lane and
+// lane + 1, loaded by the caller ahead of time.
+__device__ __forceinline__ void wave_copy_shifted(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
+                                                  uint64_t len, int lane, u32x4 pf0, u32x4 pf1)
+{
+    if (len == 0) return;
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t first = (d0 + 15) & ~uintptr_t(15);        // first whole block
+    const uintptr_t last = (d0 + len) & ~uintptr_t(15);        // end of whole blocks
+    if (first >= last) {                                        // no whole block
+        for (uint64_t i = lane; i < len; i += 64) dst[i] = src[i];
+        return;
     }
-    __syncthreads();
-    a = b = c = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; w++) {
-        a += s_red[0][w];
-        b += s_red[1][w];
-        c += s_red[2][w];
+    const uint64_t head = first - d0, tail0 = last - d0;
+    if ((uint64_t)lane < head) dst[lane] = src[lane];
+    for (uint64_t i = tail0 + lane; i < len; i += 64) dst[i] = src[i];
+    // whole block k of dst starts at source byte head + 16k: byte `head` of
+    // the aligned source block k
+    const uint32_t r = (uint32_t)head;
+    const uint64_t nblk = (last - first) / 16;
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(first);
+    for (uint64_t k = lane; k < nblk; k += 64) {
+        const u32x4 lo = (k < 64) ? pf0 : s4[k];
+        const u32x4 hi = (k < 64) ? pf1 : s4[k + 1];
+        st_stream(r == 0 ? lo : extract16(lo, hi, r), d4 + k);
     }
 }
 
-// One workgroup per encode tile. Its escape prefix P = (group sums before
-// its group) + (tile counts before it inside its group); M = all group sums.
-// Copies the tile's staged escapes to pos[P..], val[P..] and writes the
-// offsets of the chunks that start in the tile. Workgroup 0 also writes the
+// One wave per kPlaceTiles consecutive encode tiles. The escape prefix P of
+// its first tile = (group sums before that tile's group) + (tile counts before
+// it inside its group), read from L2-resident arrays; M = all group sums. All
+// of the wave's loads are issued before any is used: the sums, the tiles'
+// counts and the first source blocks of every staging slot (only the
+// destination alignment depends on P). Then, tile by tile, the staged
+// positions and exponents go to pos[P..] and val[P..], and the offsets of the
+// chunks that start in the tile are written. Tile 0's wave also writes the
 // header, offsets[nch] = M and every padding byte.
+static_assert(kEncTile >= 16 * 65, "placement prefetches 65 blocks of a staging slot");
 __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
                                                             HeaderParams hp)
 {
-    __shared__ uint32_t s_red[3][kThreads / 64];
-    const uint64_t tile = blockIdx.x;
-    const int tid = threadIdx.x;
-    const uint64_t g = tile >> p.gshift;
-    const uint64_t gfirst = g << p.gshift;
-    uint32_t before_g = 0, all = 0, in_g = 0;
-    for (uint64_t q = tid; q < p.ngroups; q += kThreads) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t tfirst = ((uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kPlaceTiles;
+    if (tfirst >= p.ntiles) return;
+    u32x4 pp0[kPlaceTiles], pp1[kPlaceTiles], pv0[kPlaceTiles], pv1[kPlaceTiles];
+    uint32_t m[kPlaceTiles];
+#pragma unroll
+    for (int i = 0; i < kPlaceTiles; i++) {
+        const uint64_t t = tfirst + i < p.ntiles ? tfirst + i : tfirst;
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(ws.stage_pos + t * kEncTile);
+        const u32x4 *sv = reinterpret_cast<const u32x4 *>(ws.stage_val + t * kEncTile);
+        pp0[i] = sp[lane];
+        pp1[i] = sp[lane + 1];
+        pv0[i] = sv[lane];
+        pv1[i] = sv[lane + 1];
+        m[i] = (tfirst + i < p.ntiles) ? ws.counts[t] : 0u;
+    }
+    const uint64_t g = tfirst >> p.gshift;
+    uint32_t before = 0, all = 0;
+    for (uint64_t q = lane; q < p.ngroups; q += 64) {
         const uint32_t v = ws.gsum[q];
         all += v;
-        if (q < g) before_g += v;
+        if (q < g) before += v;
     }
-    for (uint64_t t = gfirst + tid; t < tile; t += kThreads) in_g += ws.counts[t];
-    block_sum3(before_g, all, in_g, s_red);
-    const uint32_t P = before_g + in_g;
+    for (uint64_t t = (g << p.gshift) + lane; t < tfirst; t += 64) before += ws.counts[t];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        before += __shfl_xor(before, d, 64);
+        all += __shfl_xor(all, d, 64);
+    }
     const uint64_t M = all;
-    const uint32_t m = ws.counts[tile];
     const uint64_t off_val = p.off_pos + align256(2 * M);
-    uint16_t *pos = reinterpret_cast<uint16_t *>(out + p.off_pos) + P;
-    uint8_t *val = out + off_val + P;
-    const uint16_t *sp = ws.stage_pos + tile * kEncTile;
-    const uint8_t *sv = ws.stage_val + tile * kEncTile;
-    for (uint32_t jb = 0; jb < m; jb += 4 * kThreads) {
-        uint32_t ps[4], vs[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const uint32_t j = jb + u * kThreads + tid;
-            ps[u] = (j < m) ? sp[j] : 0u;
-            vs[u] = (j < m) ? sv[j] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const uint32_t j = jb + u * kThreads + tid;
-            if (j < m) {
-                st_stream((uint16_t)ps[u], pos + j);
-                st_stream((uint8_t)vs[u], val + j);
-            }
-        }
-    }
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
-    const uint64_t t0 = tile * kEncTile;
     const uint32_t C = p.Cmask + 1;
-    if (C < (uint32_t)kEncTile) {
-        const uint64_t c0 = t0 >> p.logC;
-        uint64_t cn = (uint64_t)kEncTile >> p.logC;
-        if (c0 + cn > p.nch) cn = p.nch - c0;
-        for (uint64_t i = tid; i < cn; i += kThreads) offs[c0 + i] = P + ws.chunk_pre[c0 + i];
-    } else if ((t0 & p.Cmask) == 0 && tid == 0) {
-        offs[t0 >> p.logC] = P;
+    uint32_t P = before;
+#pragma unroll
+    for (int i = 0; i < kPlaceTiles; i++) {
+        const uint64_t tile = tfirst + i;
+        if (tile >= p.ntiles) break;
+        wave_copy_shifted(out + p.off_pos + 2 * (uint64_t)P,
+                          reinterpret_cast<const uint8_t *>(ws.stage_pos + tile * kEncTile), 2 * (uint64_t)m[i],
+                          lane, pp0[i], pp1[i]);
+        wave_copy_shifted(out + off_val + P, ws.stage_val + tile * kEncTile, m[i], lane, pv0[i], pv1[i]);
+        const uint64_t t0 = tile * kEncTile;
+        if (C < (uint32_t)kEncTile) {
+            const uint64_t c0 = t0 >> p.logC;
+            uint64_t cn = (uint64_t)kEncTile >> p.logC;
+            if (c0 + cn > p.nch) cn = p.nch - c0;
+            for (uint64_t j = lane; j < cn; j += 64) offs[c0 + j] = P + ws.chunk_pre[c0 + j];
+        } else if ((t0 & p.Cmask) == 0 && lane == 0) {
+            offs[t0 >> p.logC] = P;
+        }
+        P += m[i];
     }
-    if (tile != 0) return;
+    if (tfirst != 0) return;
     // header: template + M + total_bytes
     const uint64_t total = off_val + M;
-    if (tid < 64) {
-        uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[tid];
-        if (tid == 6) w = (uint32_t)M;
-        if (tid == 7) w = (uint32_t)(M >> 32);
-        if (tid == 8) w = (uint32_t)total;
-        if (tid == 9) w = (uint32_t)(total >> 32);
-        reinterpret_cast<uint32_t *>(out)[tid] = w;
-    }
-    if (tid == 64) offs[p.nch] = (uint32_t)M;
+    uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[lane];
+    if (lane == 6) w = (uint32_t)M;
+    if (lane == 7) w = (uint32_t)(M >> 32);
+    if (lane == 8) w = (uint32_t)total;
+    if (lane == 9) w = (uint32_t)(total >> 32);
+    reinterpret_cast<uint32_t *>(out)[lane] = w;
+    if (lane == 0) offs[p.nch] = (uint32_t)M;
     // zero padding after each section (each gap is under 256 bytes)
-    const uint64_t sm_end = kHeader + p.n;
-    if (sm_end + tid < p.off_codes) out[sm_end + tid] = 0;
-    const uint64_t codes_end = p.off_codes + (p.n + 1) / 2;
-    if (codes_end + tid < p.off_offs) out[codes_end + tid] = 0;
-    const uint64_t offs_end = p.off_offs + 4 * (p.nch + 1);
-    if (offs_end + tid < p.off_pos) out[offs_end + tid] = 0;
-    const uint64_t pos_end = p.off_pos + 2 * M;
-    if (pos_end + tid < off_val) out[pos_end + tid] = 0;
+    for (int i = lane; i < 256; i += 64) {
+        const uint64_t sm_end = kHeader + p.n;
+        if (sm_end + i < p.off_codes) out[sm_end + i] = 0;
+        const uint64_t codes_end = p.off_codes + (p.n + 1) / 2;
+        if (codes_end + i < p.off_offs) out[codes_end + i] = 0;
+        const uint64_t offs_end = p.off_offs + 4 * (p.nch + 1);
+        if (offs_end + i < p.off_pos) out[offs_end + i] = 0;
+        const uint64_t pos_end = p.off_pos + 2 * M;
+        if (pos_end + i < off_val) out[pos_end + i] = 0;
+    }
 }
 
 // ============================================================== decode ====
@@ -784,7 +874,6 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     __shared__ EncShared esh;
     __shared__ ReduceLds lds;
     const int tid = threadIdx.x;
-    if (tid < 64) reinterpret_cast<uint32_t *>(esh.lut)[tid] = reinterpret_cast<const uint32_t *>(ep.lut)[tid];
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
     uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
@@ -804,6 +893,9 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
             for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
         }
     }
+    // the code table goes to LDS after the data loads are in flight (the
+    // barrier between the two patch maps publishes it)
+    if (tid < 64) reinterpret_cast<uint32_t *>(esh.lut)[tid] = reinterpret_cast<const uint32_t *>(ep.lut)[tid];
     if (build_patch_map<kEncTile, kEncThreads>(sa, t0, dp, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
@@ -820,9 +912,11 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     for (int k = 0; k < kEncGroups; k++)
 #pragma unroll
         for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[k][q], yb[k][q]);
-    // encode_groups writes the escape list only after its first barrier, which
-    // every thread reaches after its last read of the patch map
-    encode_groups(r, t0, tile, out, ws, ep, esh, lds.esc);
+    // encode_dense_rank writes the escape list only after its first barrier,
+    // which every thread reaches after its last read of the patch map
+    uint32_t cstart[kEncGroups];
+    const uint32_t m = encode_dense_rank(r, t0, out, ep, esh, lds.esc, cstart);
+    stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
 // ================================================================ host ====
@@ -945,7 +1039,8 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
     UZIP_LAUNCH_CHECK("k_group_sums");
     int rc = ev.record(2);
     if (rc) return rc;
-    k_place_escapes<<<(unsigned)ep.ntiles, kThreads, 0, s>>>(ws, out, ep, hp);
+    const uint64_t place_waves = (ep.ntiles + kPlaceTiles - 1) / kPlaceTiles;
+    k_place_escapes<<<(unsigned)((place_waves + kThreads / 64 - 1) / (kThreads / 64)), kThreads, 0, s>>>(ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
     return ev.record(3);
 }
