@@ -84,13 +84,22 @@ Layout make_layout(uint64_t n, uint32_t C)
 #define UZIP_ENC_GROUPS 4          // groups of 8 words per thread
 #endif
 #ifndef UZIP_DEC_THREADS
-#define UZIP_DEC_THREADS 256
+#define UZIP_DEC_THREADS 128
 #endif
 #ifndef UZIP_DEC_GROUPS
 #define UZIP_DEC_GROUPS 2          // groups of 16 words per thread
 #endif
 #ifndef UZIP_NT
 #define UZIP_NT 1                  // non-temporal streaming loads/stores
+#endif
+#ifndef UZIP_DEC_G8
+#define UZIP_DEC_G8 1
+#endif
+#ifndef UZIP_TPRE
+#define UZIP_TPRE 1
+#endif
+#ifndef UZIP_PLACE_SHUFFLE
+#define UZIP_PLACE_SHUFFLE 1
 #endif
 #ifndef UZIP_PLACE_TILES
 #define UZIP_PLACE_TILES 1         // encode tiles per escape-placement wave
@@ -113,13 +122,14 @@ static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: 
 struct EncWs {
     uint32_t *counts;      // [ntiles] escapes per tile
     uint32_t *gsum;        // [ngroups] escapes per group of 2^gshift tiles
+    uint32_t *tpre;        // [ntiles] escapes of the tiles before it inside its group
     uint32_t *chunk_pre;   // [nch] escapes in the tile before each chunk start
     uint16_t *stage_pos;   // [ntiles * kEncTile] in-chunk positions, per tile
     uint8_t  *stage_val;   // [ntiles * kEncTile] raw exponents, per tile
 };
 
 struct WsLayout {
-    uint64_t counts, gsum, chunk_pre, stage_pos, stage_val, total;
+    uint64_t counts, gsum, tpre, chunk_pre, stage_pos, stage_val, total;
 };
 
 // Tiles are summed in groups of 2^gshift, with gshift about half of log2(ntiles)
@@ -140,7 +150,8 @@ WsLayout ws_layout(uint64_t n, uint32_t C)
     WsLayout w;
     w.counts = 0;
     w.gsum = w.counts + align256(4 * ntiles);
-    w.chunk_pre = w.gsum + align256(4 * ngroups);
+    w.tpre = w.gsum + align256(4 * ngroups);
+    w.chunk_pre = w.tpre + align256(4 * ntiles);
     w.stage_pos = w.chunk_pre + align256(4 * nch);
     w.stage_val = w.stage_pos + align256(2 * ntiles * kEncTile);
     w.total = w.stage_val + align256(ntiles * kEncTile) + 256;   // slack for 16-byte over-reads
@@ -327,20 +338,40 @@ __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ 
 // ============================================================== encode ====
 // LDS of the encode back end.
 struct EncShared {
-    uint8_t lut[256];
+    uint8_t lut[kEncThreads / 64][256];     // one copy per wave: no barrier to publish it
     uint32_t wtot[kEncGroups][kEncThreads / 64];
 };
-// A tile's escapes in element order (compacted), written out with 16-byte stores.
+// A tile's escapes in element order (compacted), written out with 16-byte
+// stores; room for every word of the tile.
 struct alignas(16) EscBuf {
     uint16_t pos[kEncTile];
     uint8_t val[kEncTile];
 };
 
-// Number of set bits of b in the lanes below this one (wave64).
-__device__ __forceinline__ uint32_t lanes_below(uint64_t b)
+// Copies the code table to this wave's LDS copy (64 lanes x 4 bytes).
+__device__ __forceinline__ void load_wave_lut(EncShared &sh, const uint8_t *lut)
 {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    reinterpret_cast<uint32_t *>(sh.lut[wave])[lane] = reinterpret_cast<const uint32_t *>(lut)[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Inclusive prefix sum of v over the 64 lanes of a wave: row shifts by 1, 2,
+// 4 and 8 within each row of 16 lanes, then lane 15 of each row added to the
+// next row and lane 31 to the upper two rows (DPP row broadcasts).
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
+}
+
 
 // Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
 // holds kEncGroups groups of 8 words (group k covers tile words
@@ -362,8 +393,8 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
         uint32_t L0 = 0, L1 = 0;
         if (g0 < p.n) {
-            L0 = lut4(sh.lut, xw[k][0], xw[k][1]);
-            L1 = lut4(sh.lut, xw[k][2], xw[k][3]);
+            L0 = lut4(sh.lut[wave], xw[k][0], xw[k][1]);
+            L1 = lut4(sh.lut[wave], xw[k][2], xw[k][3]);
             if (g0 + 8 > p.n) {       // tail group: words past n are not escapes
                 const uint32_t valid = (uint32_t)(p.n - g0);   // 1..7
                 const uint64_t keep = (1ull << (8 * valid)) - 1ull;
@@ -390,17 +421,15 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         }
     }
     // escape count of each group -> exclusive prefix over the wave's lanes
-    // (ballots of the 4 bits of the count, which is at most 8)
     uint32_t pre[kEncGroups];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint32_t cnt = __builtin_popcount(Lw[k][0] & 0x80808080u) + __builtin_popcount(Lw[k][1] & 0x80808080u);
         uint32_t wt = 0, pr = 0;
         if (__ballot(cnt != 0) != 0ull) {
-            const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u);
-            const uint64_t b2 = __ballot(cnt & 4u), b3 = __ballot(cnt & 8u);
-            pr = lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
-            wt = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
+            const uint32_t inc = wave_inclusive_sum(cnt);
+            pr = inc - cnt;
+            wt = __builtin_amdgcn_readlane(inc, 63);
         }
         pre[k] = pr;
         if (lane == 0) sh.wtot[k][wave] = wt;
@@ -492,32 +521,47 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
         }
     }
     // the code table goes to LDS after the data loads are in flight
-    if (tid < 64) reinterpret_cast<uint32_t *>(sh.lut)[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
-    __syncthreads();
+    load_wave_lut(sh, p.lut);
     uint32_t cstart[kEncGroups];
     const uint32_t m = encode_dense_rank(xw, t0, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
 }
 
-// gsum[g] = escapes in tiles [g << gshift, (g + 1) << gshift).
+// One workgroup per group of 2^gshift tiles: gsum[g] = escapes in the group,
+// tpre[t] = escapes of the group's tiles before t (each thread scans a run
+// of consecutive tiles, then the runs are scanned across the workgroup).
 __global__ __launch_bounds__(kThreads) void k_group_sums(EncWs ws, EncParams p)
 {
-    __shared__ uint32_t s_red[kThreads / 64];
-    const int tid = threadIdx.x;
-    const uint64_t lo = (uint64_t)blockIdx.x << p.gshift;
-    uint64_t hi = lo + (1ull << p.gshift);
-    if (hi > p.ntiles) hi = p.ntiles;
+    __shared__ uint32_t s_wave[kThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t glo = (uint64_t)blockIdx.x << p.gshift;
+    uint64_t ghi = glo + (1ull << p.gshift);
+    if (ghi > p.ntiles) ghi = p.ntiles;
+    const uint64_t per = ((1ull << p.gshift) + kThreads - 1) / kThreads;
+    const uint64_t lo = glo + tid * per;
+    const uint64_t hi = (lo + per < ghi) ? lo + per : (lo < ghi ? ghi : lo);
     uint32_t sum = 0;
-    for (uint64_t t = lo + tid; t < hi; t += kThreads) sum += ws.counts[t];
+    for (uint64_t t = lo; t < hi; t++) sum += ws.counts[t];
+    uint32_t inc = sum;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
-    if ((tid & 63) == 0) s_red[tid >> 6] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t t = 0;
-        for (int w = 0; w < kThreads / 64; w++) t += s_red[w];
-        ws.gsum[blockIdx.x] = t;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t u = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += u;
     }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; w++) {
+        if (w < wave) run += s_wave[w];
+        total += s_wave[w];
+    }
+    for (uint64_t t = lo; t < hi; t++) {
+        const uint32_t c = ws.counts[t];
+        ws.tpre[t] = run;
+        run += c;
+    }
+    if (tid == 0) ws.gsum[blockIdx.x] = total;
 }
 
 // Bytes [r, r + 16) of the 32 bytes lo|hi (r in 0..15, the same in every
@@ -565,8 +609,25 @@ __device__ __forceinline__ void wave_copy_shifted(uint8_t *__restrict__ dst, con
         return;
     }
     const uint64_t head = first - d0, tail0 = last - d0;
+#if UZIP_PLACE_SHUFFLE
+    {
+        // head bytes by lanes 0..15, tail bytes by lanes 16..31, taken from
+        // the prefetched block of the lane that holds them (cross-lane
+        // shuffles); bytes past the prefetched 64 blocks are loaded
+        const uint64_t j = (lane < 16) ? (uint64_t)lane : tail0 + (uint64_t)(lane - 16);
+        const bool want = (lane < 16) ? j < head : (lane < 32 && j < len);
+        const uint64_t jj = want ? j : 0;
+        const int sl = (int)((jj >> 4) & 63);
+        const uint32_t comp = (uint32_t)(jj >> 2) & 3u;
+        const uint32_t x = __shfl(pf0.x, sl, 64), y = __shfl(pf0.y, sl, 64);
+        const uint32_t z = __shfl(pf0.z, sl, 64), w = __shfl(pf0.w, sl, 64);
+        const uint32_t d = comp == 0 ? x : comp == 1 ? y : comp == 2 ? z : w;
+        if (want) dst[j] = (jj >> 4) < 64 ? (uint8_t)(d >> (8 * (jj & 3))) : src[j];
+    }
+#else
     if ((uint64_t)lane < head) dst[lane] = src[lane];
     for (uint64_t i = tail0 + lane; i < len; i += 64) dst[i] = src[i];
+#endif
     // whole block k of dst starts at source byte head + 16k: byte `head` of
     // the aligned source block k
     const uint32_t r = (uint32_t)head;
@@ -616,7 +677,11 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
         all += v;
         if (q < g) before += v;
     }
+#if UZIP_TPRE
+    if (lane == 0) before += ws.tpre[tfirst];
+#else
     for (uint64_t t = (g << p.gshift) + lane; t < tfirst; t += 64) before += ws.counts[t];
+#endif
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         before += __shfl_xor(before, d, 64);
@@ -800,6 +865,40 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_
     const int tid = threadIdx.x;
     const uint64_t t0 = (uint64_t)blockIdx.x * kDecTile;
     uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
+#if UZIP_DEC_G8
+    // groups of 8 words: group k covers tile words k*kDecThreads*8 + tid*8,
+    // so every load and store instruction covers a contiguous span of the wave
+    constexpr int kG = kDecGroups * 2;
+    uint32_t out[kG][4];
+#pragma unroll
+    for (int k = 0; k < kG; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 8) + (uint64_t)tid * 8;
+        if (g0 < p.n) {
+            // sections are padded to 256 bytes, so a tail group's full loads stay inside them
+            const u32x2 sm = ld_stream(reinterpret_cast<const u32x2 *>(s.base + kHeader + g0));
+            const uint32_t cd = ld_stream(reinterpret_cast<const uint32_t *>(s.base + p.off_codes + g0 / 2));
+            decode8(sm.x, sm.y, cd, dec, out[k]);
+        }
+    }
+    if (kPatch) {
+        if (build_patch_map<kDecTile, kDecThreads>(s, t0, p, sh)) {
+#pragma unroll
+            for (int k = 0; k < kG; k++)
+                apply_patch<8>(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), out[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kG; k++) {
+        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 8) + (uint64_t)tid * 8;
+        if (g0 + 8 <= p.n) {
+            u32x4 v = {out[k][0], out[k][1], out[k][2], out[k][3]};
+            st_stream(v, reinterpret_cast<u32x4 *>(y + g0));
+        } else if (g0 < p.n) {
+            for (int j = 0; j < 8 && g0 + j < p.n; j++)
+                y[g0 + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+#else
     uint32_t out[kDecGroups][8];
 #pragma unroll
     for (int k = 0; k < kDecGroups; k++) {
@@ -833,6 +932,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_
                 y[g0 + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
         }
     }
+#endif
 }
 
 // Two-kernel variant, step 2: for every escape, overwrite the exponent field
@@ -893,9 +993,8 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
             for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
         }
     }
-    // the code table goes to LDS after the data loads are in flight (the
-    // barrier between the two patch maps publishes it)
-    if (tid < 64) reinterpret_cast<uint32_t *>(esh.lut)[tid] = reinterpret_cast<const uint32_t *>(ep.lut)[tid];
+    // the code table goes to LDS after the data loads are in flight
+    load_wave_lut(esh, ep.lut);
     if (build_patch_map<kEncTile, kEncThreads>(sa, t0, dp, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
@@ -1013,6 +1112,7 @@ EncWs make_ws(void *d_ws, uint64_t n, uint32_t C)
     EncWs ws;
     ws.counts = reinterpret_cast<uint32_t *>(b + w.counts);
     ws.gsum = reinterpret_cast<uint32_t *>(b + w.gsum);
+    ws.tpre = reinterpret_cast<uint32_t *>(b + w.tpre);
     ws.chunk_pre = reinterpret_cast<uint32_t *>(b + w.chunk_pre);
     ws.stage_pos = reinterpret_cast<uint16_t *>(b + w.stage_pos);
     ws.stage_val = b + w.stage_val;
