@@ -115,6 +115,106 @@ def _cpu_model():
     return "unknown"
 
 
+def table(uzip, torch, reps=10):
+    """One JSON line per (config, chunk): encode/decode (and, for the
+    gradient-reduce config, fused reduce) throughput, ratio, escape rate, and
+    the CPU oracle on a bounded sample. Every row is gated on a bit-exact
+    round trip."""
+    import oracle
+    import workloads
+    dev = torch.device("cuda:0")
+    for k in (1, 2, 3, 4, 5):
+        log(f"config {k}: generating")
+        w = workloads.config(k)
+        xs = w.x if isinstance(w.x, tuple) else (w.x,)
+        cals = w.calib if isinstance(w.calib, tuple) else (w.calib,)
+        hist = None
+        for c in cals:
+            hist = uzip.histogram(torch.from_numpy(c.view(np.int16)).to(dev), hist)
+        cb = uzip.codebook_from_hist(hist.cpu().numpy().astype(np.uint64))
+        x_np = xs[0]
+        n = x_np.size
+        x = torch.from_numpy(x_np.view(np.int16)).to(dev)
+        for C in w.chunks:
+            out = torch.empty(uzip.max_bytes(n, C), dtype=torch.uint8, device=dev)
+            ws = torch.empty(uzip.workspace_bytes(n, C), dtype=torch.uint8, device=dev)
+            y = torch.empty(n, dtype=torch.int16, device=dev)
+            uzip.encode(x, cb, C, out=out, ws=ws)
+            total, m = uzip.stream_bytes(out)
+            uzip.decode(out, cb, n, C, out=y, in_bytes=total)
+            torch.cuda.synchronize()
+            if not torch.equal(y, x):
+                log(f"CORRECTNESS FAILURE config {k} C={C}")
+                sys.exit(1)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+            for row in ev:
+                for e in row:
+                    e.record()
+            for _ in range(3):
+                uzip.encode(x, cb, C, out=out, ws=ws)
+                uzip.decode(out, cb, n, C, out=y, in_bytes=total)
+            for r in range(reps):
+                ev[r][0].record()
+                uzip.encode(x, cb, C, out=out, ws=ws)
+                ev[r][1].record()
+                ev[r][2].record()
+                uzip.decode(out, cb, n, C, out=y, in_bytes=total)
+                ev[r][3].record()
+            torch.cuda.synchronize()
+            te = [ev[r][0].elapsed_time(ev[r][1]) for r in range(reps)]
+            td = [ev[r][2].elapsed_time(ev[r][3]) for r in range(reps)]
+            ab = algorithmic_bytes(n, C, m)
+            row = {"config": k, "workload": w.name, "n": n, "chunk": C, "M": m, "escape_rate": round(m / n, 6),
+                   "ratio_payload": round(2 * n / (n + (n + 1) // 2 + 3 * m), 4),
+                   "ratio_total": round(2 * n / total, 4),
+                   "encode_ms_mean": round(float(np.mean(te)), 4), "encode_ms_median": round(float(np.median(te)), 4),
+                   "decode_ms_mean": round(float(np.mean(td)), 4), "decode_ms_median": round(float(np.median(td)), 4),
+                   "encode_GBps": round(2 * n / (np.mean(te) * 1e-3) / 1e9, 1),
+                   "decode_GBps": round(2 * n / (np.mean(td) * 1e-3) / 1e9, 1),
+                   "encode_roofline": round(ab["encode"] / (np.mean(te) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "decode_roofline": round(ab["decode"] / (np.mean(td) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            if len(xs) == 2:
+                b = torch.from_numpy(xs[1].view(np.int16)).to(dev)
+                outb = torch.empty_like(out)
+                outr = torch.empty_like(out)
+                uzip.encode(b, cb, C, out=outb, ws=ws)
+                tb, _ = uzip.stream_bytes(outb)
+                for _ in range(2):
+                    uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws)
+                rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+                for rr in rev:
+                    for e in rr:
+                        e.record()
+                for r in range(reps):
+                    rev[r][0].record()
+                    uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws)
+                    rev[r][1].record()
+                torch.cuda.synchronize()
+                tr = [rev[r][0].elapsed_time(rev[r][1]) for r in range(reps)]
+                trr, mr = uzip.stream_bytes(outr)
+                red_bytes = (total + tb) + trr
+                row.update({"reduce_ms_mean": round(float(np.mean(tr)), 4),
+                            "reduce_GBps_uncompressed_in": round(2 * 2 * n / (np.mean(tr) * 1e-3) / 1e9, 1),
+                            "reduce_stream_roofline": round(red_bytes / (np.mean(tr) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "reduce_escape_rate": round(mr / n, 6)})
+                del b, outb, outr
+            # the CPU oracle on a bounded sample (one thread)
+            sample = min(n, 1 << 22)
+            xs_np = np.ascontiguousarray(x_np[:sample])
+            ocb = oracle.top16(hist.cpu().numpy().astype(np.uint64))
+            t0 = time.perf_counter()
+            st = oracle.encode(xs_np, C, ocb.dec)
+            t1 = time.perf_counter()
+            oracle.decode(st, sample, C, ocb.dec)
+            t2 = time.perf_counter()
+            row.update({"oracle_sample": sample, "oracle_encode_GBps": round(2 * sample / (t1 - t0) / 1e9, 4),
+                        "oracle_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4), "oracle_cores": 1})
+            print("TABLE " + json.dumps(row), flush=True)
+            del out, ws, y
+        del x
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +227,8 @@ def main():
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
+    ap.add_argument("--table", action="store_true",
+                    help="measure every configuration (one TABLE line each) instead of the headline")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,6 +244,9 @@ def main():
     uzip.lib()                       # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     C = args.chunk
+    if args.table:
+        table(uzip, torch)
+        return
 
     if args.pmc_calibration:
         # a plain copy kernel of known size: 2^29 16-bit words, 1 GiB read + 1 GiB write
