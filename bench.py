@@ -115,7 +115,17 @@ def _cpu_model():
     return "unknown"
 
 
-def table(uzip, torch, reps=10):
+def make_flush(torch, dev, mib):
+    """A callable that reads `mib` MiB on the current stream (0: a no-op).
+    Reads allocate in the Infinity Cache, so they evict earlier contents,
+    and they leave only clean lines behind."""
+    if mib <= 0:
+        return lambda: None
+    buf = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    return lambda: buf.sum()
+
+
+def table(uzip, torch, reps=10, flush_mib=1024):
     """One JSON line per (config, chunk): encode/decode (and, for the
     gradient-reduce config, fused reduce) throughput, ratio, escape rate, and
     the CPU oracle on a bounded sample. Every row is gated on a bit-exact
@@ -123,6 +133,8 @@ def table(uzip, torch, reps=10):
     import oracle
     import workloads
     dev = torch.device("cuda:0")
+    flush = make_flush(torch, dev, flush_mib)   # evicts the Infinity Cache before each timed call
+
     for k in (1, 2, 3, 4, 5):
         log(f"config {k}: generating")
         w = workloads.config(k)
@@ -154,9 +166,11 @@ def table(uzip, torch, reps=10):
                 uzip.encode(x, cb, C, out=out, ws=ws)
                 uzip.decode(out, cb, n, C, out=y, in_bytes=total)
             for r in range(reps):
+                flush()
                 ev[r][0].record()
                 uzip.encode(x, cb, C, out=out, ws=ws)
                 ev[r][1].record()
+                flush()
                 ev[r][2].record()
                 uzip.decode(out, cb, n, C, out=y, in_bytes=total)
                 ev[r][3].record()
@@ -186,6 +200,7 @@ def table(uzip, torch, reps=10):
                     for e in rr:
                         e.record()
                 for r in range(reps):
+                    flush()
                     rev[r][0].record()
                     uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws)
                     rev[r][1].record()
@@ -227,6 +242,9 @@ def main():
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB read from a scratch buffer before every timed codec call to evict "
+                         "the Infinity Cache (0: back-to-back calls)")
     ap.add_argument("--table", action="store_true",
                     help="measure every configuration (one TABLE line each) instead of the headline")
     args = ap.parse_args()
@@ -245,7 +263,7 @@ def main():
     dev = torch.device("cuda:0")
     C = args.chunk
     if args.table:
-        table(uzip, torch)
+        table(uzip, torch, flush_mib=args.flush_mib)
         return
 
     if args.pmc_calibration:
@@ -297,8 +315,18 @@ def main():
         sys.exit(1)
 
     # --- timed round trips (no events inside the timed region) ---
+    # With --flush-mib F > 0, every codec call is preceded by a read of F MiB
+    # from a scratch buffer (a sum), which evicts the 256 MB Infinity Cache,
+    # so neither call finds the other's output in the cache. A read, not a
+    # write: a write-based flush would leave the cache full of dirty lines
+    # whose write-back lands in the next call's time. The flushes' own time
+    # is measured in a separate loop and subtracted.
+    flush = make_flush(torch, dev, args.flush_mib)
+
     def step(ev=None):
+        flush()
         uzip.encode(x, cb, C, out=out, ws=ws, events=ev[:4] if ev else None)
+        flush()
         uzip.decode(out, cb, n, C, out=y, in_bytes=total, events=ev[4:] if ev else None)
 
     log(f"warmup {args.warmup}")
@@ -311,7 +339,17 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
+    wall_flush = 0.0
+    if args.flush_mib > 0:
+        for _ in range(2):
+            flush()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(2 * args.steps):
+            flush()
+        torch.cuda.synchronize()
+        wall_flush = time.perf_counter() - t0
+    ms_step = (wall - wall_flush) / args.steps * 1e3
 
     # --- per-kernel durations: HIP events recorded between the kernels of
     # each call, on the stream they run on (a second pass of K steps) ---
@@ -357,6 +395,7 @@ def main():
         for k in range(3):
             uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws)
         for k in range(10):
+            flush()
             uzip.reduce_add(out[:total], outb[:tb], cb, n, C, out=outr, ws=ws, events=rev[k])
         torch.cuda.synchronize()
         t_red = float(np.mean([rev[k][0].elapsed_time(rev[k][3]) for k in range(10)]))
@@ -389,6 +428,7 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom]},
+        "cache_flush_mib_before_each_call": args.flush_mib,
         "round_trip_bit_exact": round_trip, "oracle_stream_equal": parity,
         "reduce": reduce,
     }

@@ -89,22 +89,15 @@ Layout make_layout(uint64_t n, uint32_t C)
 #ifndef UZIP_DEC_GROUPS
 #define UZIP_DEC_GROUPS 2          // groups of 16 words per thread
 #endif
+#ifndef UZIP_PLACE_PRE
+#define UZIP_PLACE_PRE 0           // staging blocks each placement wave loads before its count is known
+#endif
 #ifndef UZIP_NT
 #define UZIP_NT 1                  // non-temporal streaming loads/stores
 #endif
 #ifndef UZIP_DEC_G8
 #define UZIP_DEC_G8 1
 #endif
-#ifndef UZIP_TPRE
-#define UZIP_TPRE 1
-#endif
-#ifndef UZIP_PLACE_SHUFFLE
-#define UZIP_PLACE_SHUFFLE 1
-#endif
-#ifndef UZIP_PLACE_TILES
-#define UZIP_PLACE_TILES 1         // encode tiles per escape-placement wave
-#endif
-
 
 constexpr int kEncThreads = UZIP_ENC_THREADS;
 constexpr int kEncGroups = UZIP_ENC_GROUPS;
@@ -113,7 +106,7 @@ constexpr int kDecThreads = UZIP_DEC_THREADS;
 constexpr int kDecGroups = UZIP_DEC_GROUPS;
 constexpr int kDecTile = kDecThreads * kDecGroups * 16;
 constexpr int kThreads = 256;               // histogram, placement and patch kernels
-constexpr int kPlaceTiles = UZIP_PLACE_TILES;
+constexpr int kPlacePre = UZIP_PLACE_PRE;
 
 static_assert((kEncTile & (kEncTile - 1)) == 0 && kEncTile <= 65536, "encode tile: power of two <= 65536");
 static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: power of two");
@@ -592,126 +585,209 @@ __device__ __forceinline__ u32x4 extract16(u32x4 lo, u32x4 hi, uint32_t r)
     return o;
 }
 
-// One wave copies len bytes from src (16-byte aligned, readable 16 bytes past
-// len) to dst (any alignment). Whole 16-byte blocks of dst are written with
-// one store each (two aligned source loads and a byte funnel); the partial
-// blocks at both ends byte by byte. pf0/pf1 are source blocks lane and
-// lane + 1, loaded by the caller ahead of time.
-__device__ __forceinline__ void wave_copy_shifted(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
-                                                  uint64_t len, int lane, u32x4 pf0, u32x4 pf1)
+// Geometry of a copy of len bytes to dst (any alignment) from a 16-byte
+// aligned source: whole destination blocks d4[0..nblk), whose block k holds
+// source bytes [r + 16k, r + 16k + 16); and at most 31 edge bytes, the
+// first `head` bytes and the bytes from tail0 to len. Without a whole block
+// (len <= 30), head = min(len, 16) and tail0 = 16.
+struct ShiftPlan {
+    uint8_t *dst;
+    u32x4 *d4;
+    uint64_t len, head, tail0, nblk;
+    uint32_t r;
+};
+
+__device__ __forceinline__ ShiftPlan shift_plan(uint8_t *dst, uint64_t len)
 {
-    if (len == 0) return;
+    ShiftPlan q;
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst);
-    const uintptr_t first = (d0 + 15) & ~uintptr_t(15);        // first whole block
-    const uintptr_t last = (d0 + len) & ~uintptr_t(15);        // end of whole blocks
-    if (first >= last) {                                        // no whole block
-        for (uint64_t i = lane; i < len; i += 64) dst[i] = src[i];
-        return;
+    const uintptr_t first = (d0 + 15) & ~uintptr_t(15);
+    const uintptr_t last = (d0 + len) & ~uintptr_t(15);
+    q.dst = dst;
+    q.len = len;
+    if (first < last) {
+        q.head = first - d0;
+        q.tail0 = last - d0;
+        q.nblk = (last - first) / 16;
+    } else {
+        q.head = len < 16 ? len : 16;
+        q.tail0 = 16;
+        q.nblk = 0;
     }
-    const uint64_t head = first - d0, tail0 = last - d0;
-#if UZIP_PLACE_SHUFFLE
-    {
-        // head bytes by lanes 0..15, tail bytes by lanes 16..31, taken from
-        // the prefetched block of the lane that holds them (cross-lane
-        // shuffles); bytes past the prefetched 64 blocks are loaded
-        const uint64_t j = (lane < 16) ? (uint64_t)lane : tail0 + (uint64_t)(lane - 16);
-        const bool want = (lane < 16) ? j < head : (lane < 32 && j < len);
-        const uint64_t jj = want ? j : 0;
-        const int sl = (int)((jj >> 4) & 63);
-        const uint32_t comp = (uint32_t)(jj >> 2) & 3u;
-        const uint32_t x = __shfl(pf0.x, sl, 64), y = __shfl(pf0.y, sl, 64);
-        const uint32_t z = __shfl(pf0.z, sl, 64), w = __shfl(pf0.w, sl, 64);
-        const uint32_t d = comp == 0 ? x : comp == 1 ? y : comp == 2 ? z : w;
-        if (want) dst[j] = (jj >> 4) < 64 ? (uint8_t)(d >> (8 * (jj & 3))) : src[j];
-    }
-#else
-    if ((uint64_t)lane < head) dst[lane] = src[lane];
-    for (uint64_t i = tail0 + lane; i < len; i += 64) dst[i] = src[i];
-#endif
-    // whole block k of dst starts at source byte head + 16k: byte `head` of
-    // the aligned source block k
-    const uint32_t r = (uint32_t)head;
-    const uint64_t nblk = (last - first) / 16;
-    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
-    u32x4 *d4 = reinterpret_cast<u32x4 *>(first);
-    for (uint64_t k = lane; k < nblk; k += 64) {
-        const u32x4 lo = (k < 64) ? pf0 : s4[k];
-        const u32x4 hi = (k < 64) ? pf1 : s4[k + 1];
-        st_stream(r == 0 ? lo : extract16(lo, hi, r), d4 + k);
-    }
+    q.d4 = reinterpret_cast<u32x4 *>(dst + (first - d0));   // derived from dst: stays a global pointer
+    q.r = (uint32_t)(q.head & 15);
+    return q;
 }
 
-// One wave per kPlaceTiles consecutive encode tiles. The escape prefix P of
-// its first tile = (group sums before that tile's group) + (tile counts before
-// it inside its group), read from L2-resident arrays; M = all group sums. All
-// of the wave's loads are issued before any is used: the sums, the tiles'
-// counts and the first source blocks of every staging slot (only the
-// destination alignment depends on P). Then, tile by tile, the staged
-// positions and exponents go to pos[P..] and val[P..], and the offsets of the
-// chunks that start in the tile are written. Tile 0's wave also writes the
-// header, offsets[nch] = M and every padding byte.
-static_assert(kEncTile >= 16 * 65, "placement prefetches 65 blocks of a staging slot");
+// Edge byte e (0..31) of a copy: its offset, or ~0 when there is none
+// (e < 16: head bytes; e >= 16: tail bytes).
+__device__ __forceinline__ uint64_t edge_offset(uint64_t head, uint64_t tail0, uint64_t len, int e)
+{
+    const uint64_t j = (e < 16) ? (uint64_t)e : tail0 + (uint64_t)(e - 16);
+    const bool ok = (e < 16) ? j < head : j < len;
+    return ok ? j : ~0ull;
+}
+
+// Byte j of the source from the prefetched blocks pf (block `lane` in each
+// lane), for j < 64 * 16; every lane must call it (cross-lane shuffles).
+__device__ __forceinline__ uint32_t byte_from_blocks(u32x4 pf, uint64_t j)
+{
+    const int sl = (int)((j >> 4) & 63);
+    const uint32_t comp = (uint32_t)(j >> 2) & 3u;
+    const uint32_t x = __shfl(pf.x, sl, 64), y = __shfl(pf.y, sl, 64);
+    const uint32_t z = __shfl(pf.z, sl, 64), w = __shfl(pf.w, sl, 64);
+    const uint32_t d = comp == 0 ? x : comp == 1 ? y : comp == 2 ? z : w;
+    return (d >> (8 * (j & 3))) & 0xFFu;
+}
+
+// Whole destination block k of a plan from source blocks lo = k, hi = k + 1.
+__device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 lo, u32x4 hi)
+{
+    st_stream(q.r == 0 ? lo : extract16(lo, hi, q.r), q.d4 + k);
+}
+
+// One wave per encode tile. Its escape prefix P = (group sums before the
+// tile's group) + (the tile's prefix inside its group). Every load that
+// needs neither the tile's escape count nor P goes out first, in one round:
+// the count, the sums, the tile's chunk prefixes and the first kPlacePre + 1
+// blocks of both staging arrays (speculative: most tiles need only a few).
+// Then positions and exponents go to pos[P..] and val[P..]: each whole
+// 16-byte destination block by one store (two aligned source blocks and a
+// byte funnel), the partial blocks at the ends by byte stores (lanes 0..31
+// for pos, 32..63 for val), their bytes taken from the prefetched blocks by
+// cross-lane shuffles or else loaded. Pos and val blocks past the prefetch
+// are copied together, 64 per round, with the loads of each round issued
+// before the stores of the round before it (a wait for a load also waits
+// for every store issued before it). Tile 0's wave also writes the header,
+// offsets[nch] = M and every padding byte.
+static_assert(kPlacePre >= 0 && kPlacePre <= 64, "placement prefetch: 0..64 blocks");
+static_assert(kEncTile >= 16 * 65, "placement reads at most 65 blocks past a round start");
+static_assert(kEncTile / 64 <= 128, "placement loads at most two chunk prefixes per lane");
 __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
                                                             HeaderParams hp)
 {
+    // wave-uniform values are moved to scalar registers (readfirstlane)
     const int lane = threadIdx.x & 63;
-    const uint64_t tfirst = ((uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kPlaceTiles;
-    if (tfirst >= p.ntiles) return;
-    u32x4 pp0[kPlaceTiles], pp1[kPlaceTiles], pv0[kPlaceTiles], pv1[kPlaceTiles];
-    uint32_t m[kPlaceTiles];
-#pragma unroll
-    for (int i = 0; i < kPlaceTiles; i++) {
-        const uint64_t t = tfirst + i < p.ntiles ? tfirst + i : tfirst;
-        const u32x4 *sp = reinterpret_cast<const u32x4 *>(ws.stage_pos + t * kEncTile);
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(ws.stage_val + t * kEncTile);
-        pp0[i] = sp[lane];
-        pp1[i] = sp[lane + 1];
-        pv0[i] = sv[lane];
-        pv1[i] = sv[lane + 1];
-        m[i] = (tfirst + i < p.ntiles) ? ws.counts[t] : 0u;
+    const uint64_t tile = (uint64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (tile >= p.ntiles) return;
+    const uint64_t t0 = tile * kEncTile;
+    const uint32_t C = p.Cmask + 1;
+    // ---- round 1: loads independent of the count and of P
+    const uint8_t *src_p = reinterpret_cast<const uint8_t *>(ws.stage_pos + tile * kEncTile);
+    const uint8_t *src_v = ws.stage_val + tile * kEncTile;
+    const u32x4 *sp4 = reinterpret_cast<const u32x4 *>(src_p);
+    const u32x4 *sv4 = reinterpret_cast<const u32x4 *>(src_v);
+    u32x4 pp0 = {}, pp1 = {}, pv0 = {}, pv1 = {};
+    if (lane < kPlacePre) {
+        pp0 = sp4[lane];
+        pp1 = sp4[lane + 1];
+        pv0 = sv4[lane];
+        pv1 = sv4[lane + 1];
     }
-    const uint64_t g = tfirst >> p.gshift;
+    const uint32_t m_l = ws.counts[tile];
+    const uint32_t tp_l = ws.tpre[tile];
+    const uint64_t g = tile >> p.gshift;
+    uint32_t gs[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t q = (uint64_t)lane + 64 * i;
+        gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
+    }
+    uint64_t c0 = 0, cn = 0;
+    uint32_t cp[2] = {0u, 0u};
+    if (C < (uint32_t)kEncTile) {
+        c0 = t0 >> p.logC;
+        cn = (uint64_t)kEncTile >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            if ((uint64_t)lane + 64 * i < cn) cp[i] = ws.chunk_pre[c0 + lane + 64 * i];
+    }
+    // ---- the prefix
     uint32_t before = 0, all = 0;
-    for (uint64_t q = lane; q < p.ngroups; q += 64) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t q = (uint64_t)lane + 64 * i;
+        all += gs[i];
+        if (q < g) before += gs[i];
+    }
+    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) {
         const uint32_t v = ws.gsum[q];
         all += v;
         if (q < g) before += v;
     }
-#if UZIP_TPRE
-    if (lane == 0) before += ws.tpre[tfirst];
-#else
-    for (uint64_t t = (g << p.gshift) + lane; t < tfirst; t += 64) before += ws.counts[t];
-#endif
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         before += __shfl_xor(before, d, 64);
         all += __shfl_xor(all, d, 64);
     }
-    const uint64_t M = all;
+    const uint32_t m = __builtin_amdgcn_readfirstlane(m_l);
+    const uint32_t P = __builtin_amdgcn_readfirstlane(before + tp_l);
+    const uint64_t M = __builtin_amdgcn_readfirstlane(all);
     const uint64_t off_val = p.off_pos + align256(2 * M);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
-    const uint32_t C = p.Cmask + 1;
-    uint32_t P = before;
-#pragma unroll
-    for (int i = 0; i < kPlaceTiles; i++) {
-        const uint64_t tile = tfirst + i;
-        if (tile >= p.ntiles) break;
-        wave_copy_shifted(out + p.off_pos + 2 * (uint64_t)P,
-                          reinterpret_cast<const uint8_t *>(ws.stage_pos + tile * kEncTile), 2 * (uint64_t)m[i],
-                          lane, pp0[i], pp1[i]);
-        wave_copy_shifted(out + off_val + P, ws.stage_val + tile * kEncTile, m[i], lane, pv0[i], pv1[i]);
-        const uint64_t t0 = tile * kEncTile;
-        if (C < (uint32_t)kEncTile) {
-            const uint64_t c0 = t0 >> p.logC;
-            uint64_t cn = (uint64_t)kEncTile >> p.logC;
-            if (c0 + cn > p.nch) cn = p.nch - c0;
-            for (uint64_t j = lane; j < cn; j += 64) offs[c0 + j] = P + ws.chunk_pre[c0 + j];
-        } else if ((t0 & p.Cmask) == 0 && lane == 0) {
-            offs[t0 >> p.logC] = P;
+    // ---- the copies
+    const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, 2 * (uint64_t)m);
+    const ShiftPlan qv = shift_plan(out + off_val + P, m);
+    const uint64_t nb = qp.nblk > qv.nblk ? qp.nblk : qv.nblk;
+    // loads of the first round past the prefetch
+    u32x4 alo = {}, ahi = {}, blo = {}, bhi = {};
+    {
+        const uint64_t k = (uint64_t)kPlacePre + lane;
+        if (k < qp.nblk) {
+            alo = sp4[k];
+            ahi = sp4[k + 1];
         }
-        P += m[i];
+        if (k < qv.nblk) {
+            blo = sv4[k];
+            bhi = sv4[k + 1];
+        }
     }
-    if (tfirst != 0) return;
+    // edge bytes: this lane's byte, from the prefetched blocks if it is
+    // there, else loaded now and stored after the block rounds
+    const bool is_p = lane < 32;
+    const uint64_t ej = edge_offset(is_p ? qp.head : qv.head, is_p ? qp.tail0 : qv.tail0,
+                                    is_p ? qp.len : qv.len, lane & 31);
+    const uint64_t jj = ej == ~0ull ? 0 : ej;
+    uint32_t eb = 0;
+    if (kPlacePre > 0) {
+        const uint32_t bp = byte_from_blocks(pp0, jj), bv = byte_from_blocks(pv0, jj);
+        eb = is_p ? bp : bv;
+    }
+    if (ej != ~0ull && (ej >> 4) >= (uint64_t)kPlacePre) eb = is_p ? src_p[ej] : src_v[ej];
+    if ((uint64_t)lane < qp.nblk && lane < kPlacePre) put_block(qp, lane, pp0, pp1);
+    if ((uint64_t)lane < qv.nblk && lane < kPlacePre) put_block(qv, lane, pv0, pv1);
+    for (uint64_t k0 = kPlacePre; k0 < nb; k0 += 64) {
+        const uint64_t k = k0 + lane, kn = k + 64;
+        u32x4 nalo = alo, nahi = ahi, nblo = blo, nbhi = bhi;
+        if (kn < qp.nblk) {
+            nalo = sp4[kn];
+            nahi = sp4[kn + 1];
+        }
+        if (kn < qv.nblk) {
+            nblo = sv4[kn];
+            nbhi = sv4[kn + 1];
+        }
+        if (k < qp.nblk) put_block(qp, k, alo, ahi);
+        if (k < qv.nblk) put_block(qv, k, blo, bhi);
+        alo = nalo;
+        ahi = nahi;
+        blo = nblo;
+        bhi = nbhi;
+    }
+    if (ej != ~0ull) {
+        uint8_t *edst = is_p ? qp.dst : qv.dst;
+        edst[ej] = (uint8_t)eb;
+    }
+    // offsets of the chunks that start in the tile
+    if (C < (uint32_t)kEncTile) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + cp[i];
+    } else if ((t0 & p.Cmask) == 0 && lane == 0) {
+        offs[t0 >> p.logC] = P;
+    }
+    if (tile != 0) return;
     // header: template + M + total_bytes
     const uint64_t total = off_val + M;
     uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[lane];
@@ -1139,8 +1215,7 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
     UZIP_LAUNCH_CHECK("k_group_sums");
     int rc = ev.record(2);
     if (rc) return rc;
-    const uint64_t place_waves = (ep.ntiles + kPlaceTiles - 1) / kPlaceTiles;
-    k_place_escapes<<<(unsigned)((place_waves + kThreads / 64 - 1) / (kThreads / 64)), kThreads, 0, s>>>(ws, out, ep, hp);
+    k_place_escapes<<<(unsigned)((ep.ntiles + kThreads / 64 - 1) / (kThreads / 64)), kThreads, 0, s>>>(ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
     return ev.record(3);
 }
