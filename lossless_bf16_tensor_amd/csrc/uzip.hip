@@ -92,11 +92,14 @@ Layout make_layout(uint64_t n, uint32_t C)
 #ifndef UZIP_PLACE_PRE
 #define UZIP_PLACE_PRE 0           // staging blocks each placement wave loads before its count is known
 #endif
+#ifndef UZIP_DEC_FETCH
+#define UZIP_DEC_FETCH 2           // escapes per thread a decode tile loads with its first patch round
+#endif
+#ifndef UZIP_RED_FETCH
+#define UZIP_RED_FETCH 2           // the same, per input, in the reduce
+#endif
 #ifndef UZIP_NT
 #define UZIP_NT 1                  // non-temporal streaming loads/stores
-#endif
-#ifndef UZIP_DEC_G8
-#define UZIP_DEC_G8 1
 #endif
 
 constexpr int kEncThreads = UZIP_ENC_THREADS;
@@ -107,6 +110,8 @@ constexpr int kDecGroups = UZIP_DEC_GROUPS;
 constexpr int kDecTile = kDecThreads * kDecGroups * 16;
 constexpr int kThreads = 256;               // histogram, placement and patch kernels
 constexpr int kPlacePre = UZIP_PLACE_PRE;
+constexpr int kDecFetch = UZIP_DEC_FETCH;
+constexpr int kRedFetch = UZIP_RED_FETCH;
 
 static_assert((kEncTile & (kEncTile - 1)) == 0 && kEncTile <= 65536, "encode tile: power of two <= 65536");
 static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: power of two");
@@ -272,28 +277,23 @@ __device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t cod
     y[3] = merge2(perm(e47, sm1, 0x07030602u));
 }
 
-// Replace the exponent field of word `half` (0..1) of a dword.
-__device__ __forceinline__ uint32_t set_exp(uint32_t y, int half, uint32_t e)
+// binary32 sum -> BF16 in the high half, round half to even (a carry out
+// of the mantissa rounds up into the exponent, up to infinity); NaN ->
+// 0x7FC0. The low half is left over.
+__device__ __forceinline__ uint32_t bf16_rne_hi(float s)
 {
-    uint32_t sh = 7 + 16 * half;
-    return (y & ~(0xFFu << sh)) | (e << sh);
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (s != s) ? 0x7FC00000u : r;
 }
 
-// binary32 bits -> BF16, round half to even; NaN -> 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_rne(uint32_t u)
-{
-    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
-}
-
-// Sum of the two BF16 words in each half of a and b.
+// Sum of the two BF16 words in each half of a and b: binary32 add, then
+// round to BF16.
 __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
 {
-    float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
-    float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
-    uint32_t r0 = bf16_rne(__float_as_uint(a0 + b0));
-    uint32_t r1 = bf16_rne(__float_as_uint(a1 + b1));
-    return r0 | (r1 << 16);
+    const float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
+    const float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
+    return perm(bf16_rne_hi(a1 + b1), bf16_rne_hi(a0 + b0), 0x07060302u);
 }
 
 
@@ -366,30 +366,40 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v)
 }
 
 
+// Words of tile t0 (at most kEncTile), a scalar.
+__device__ __forceinline__ uint32_t enc_tile_words(uint64_t t0, const EncParams &p)
+{
+    return (uint32_t)((p.n - t0 < (uint64_t)kEncTile) ? p.n - t0 : (uint64_t)kEncTile);
+}
+
 // Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
 // holds kEncGroups groups of 8 words (group k covers tile words
 // k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
-// xw[k][q]). Writes the dense sections and lists the tile's escapes in
-// element order in LDS (eb). Returns the tile's escape count m (the same in
-// every thread). cstart[k] is the number of the tile's escapes before group k
-// when group k starts a chunk, else ~0u. Ends without a barrier after the LDS
-// writes of eb.
-__device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0,
+// xw[k][q]); the tile has rem words. Writes the dense sections and lists the
+// tile's escapes in element order in LDS (eb). Returns the tile's escape
+// count m (the same in every thread). cstart[k] is the number of the tile's
+// escapes before group k when group k starts a chunk, else ~0u. Ends without
+// a barrier after the LDS writes of eb.
+__device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
                                                       EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the tile's bases (scalar); lanes index them with 32-bit offsets
+    uint8_t *smt = out + kHeader + t0;
+    uint8_t *cdt = out + p.off_codes + t0 / 2;
+    const uint32_t t0m = (uint32_t)(t0 & p.Cmask);      // offset of the tile in its chunk
     uint32_t Lw[kEncGroups][2], sm[kEncGroups][2], cw[kEncGroups];
     // table lookups and dense values for every group, then all the stores
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         uint32_t L0 = 0, L1 = 0;
-        if (g0 < p.n) {
+        if (lo < rem) {
             L0 = lut4(sh.lut[wave], xw[k][0], xw[k][1]);
             L1 = lut4(sh.lut[wave], xw[k][2], xw[k][3]);
-            if (g0 + 8 > p.n) {       // tail group: words past n are not escapes
-                const uint32_t valid = (uint32_t)(p.n - g0);   // 1..7
+            if (lo + 8 > rem) {       // tail group: words past n are not escapes
+                const uint32_t valid = rem - lo;   // 1..7
                 const uint64_t keep = (1ull << (8 * valid)) - 1ull;
                 const uint64_t both = ((uint64_t)L1 << 32 | L0) & keep;
                 L0 = (uint32_t)both;
@@ -404,13 +414,13 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     }
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
-        if (g0 < p.n) {
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        if (lo < rem) {
             u32x2 smv;
             smv.x = sm[k][0];
             smv.y = sm[k][1];
-            st_stream(smv, reinterpret_cast<u32x2 *>(out + kHeader + g0));
-            st_stream(cw[k], reinterpret_cast<uint32_t *>(out + p.off_codes + g0 / 2));
+            st_stream(smv, reinterpret_cast<u32x2 *>(smt + lo));
+            st_stream(cw[k], reinterpret_cast<uint32_t *>(cdt + lo / 2));
         }
     }
     // escape count of each group -> exclusive prefix over the wave's lanes
@@ -440,10 +450,10 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     }
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         uint32_t rank = base[k] + pre[k];
-        cstart[k] = (g0 < p.n && (g0 & p.Cmask) == 0) ? rank : ~0u;
-        const uint32_t g0m = (uint32_t)(g0 & p.Cmask);     // a multiple of 8, below C
+        const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
+        cstart[k] = (lo < rem && g0m == 0) ? rank : ~0u;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             uint32_t mask = Lw[k][h] & 0x80808080u;
@@ -474,10 +484,11 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
     const int tid = threadIdx.x;
     if (tid == 0) ws.counts[tile] = m;
     if (p.Cmask + 1 < (uint32_t)kEncTile) {
+        uint32_t *cpt = ws.chunk_pre + (t0 >> p.logC);     // chunks no larger than the tile start at t0
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++) {
-            const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
-            if (cstart[k] != ~0u) ws.chunk_pre[g0 >> p.logC] = cstart[k];
+            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            if (cstart[k] != ~0u) cpt[lo >> p.logC] = cstart[k];
         }
     }
     if (m == 0) return;
@@ -498,17 +509,19 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
     const int tid = threadIdx.x;
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
+    const uint32_t rem = enc_tile_words(t0, p);
+    const uint16_t *xt = x + t0;
     uint32_t xw[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
-        if (g0 + 8 <= p.n) {
-            const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + g0));
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        if (lo + 8 <= rem) {
+            const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(xt + lo));
             xw[k][0] = v.x; xw[k][1] = v.y; xw[k][2] = v.z; xw[k][3] = v.w;
         } else {
             uint16_t h[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) h[j] = (g0 + j < p.n) ? x[g0 + j] : (uint16_t)0;
+            for (int j = 0; j < 8; j++) h[j] = (lo + j < rem) ? xt[lo + j] : (uint16_t)0;
 #pragma unroll
             for (int q = 0; q < 4; q++) xw[k][q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
         }
@@ -516,7 +529,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
     // the code table goes to LDS after the data loads are in flight
     load_wave_lut(sh, p.lut);
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank(xw, t0, out, p, sh, eb, cstart);
+    const uint32_t m = encode_dense_rank(xw, t0, rem, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
 }
 
@@ -826,95 +839,174 @@ struct PatchShared {
     uint32_t offs[TILE / 64 + 1];
 };
 
-// Builds the patch map of the tile's words [t0, t0 + TILE) with NT threads.
-// Returns false when the tile has no escapes. Every thread of the workgroup
-// calls it; when it returns true it has ended with a barrier.
+// A tile's patch map, for the tile's words [t0, t0 + TILE) and NT threads,
+// is built in three steps, so that its dependent loads take two rounds and
+// overlap the tile's dense loads:
+//   patch_begin, before the dense loads: the stream's M and the tile's chunk
+//     offsets (one per thread);
+//   patch_fetch, after the dense loads are issued: the tile's escape range
+//     and its first FB * NT escapes, held in registers;
+//   patch_build: the LDS map (more escapes are loaded there, 4 * NT per
+//     round, only for tiles with over FB * NT of them); ends with a barrier.
+// Every thread of the workgroup calls all three. Values read from the stream
+// are clamped so that a corrupt stream cannot drive an access out of bounds.
+struct PatchHead {
+    uint64_t M;
+    uint32_t lo, hi;      // offsets at the tile's first chunk and past its last one
+    uint32_t mine;        // offs[c0 + tid], for tid <= nc (chunks no larger than the tile)
+};
+
+template <int FB>
+struct PatchFetch {
+    uint32_t E0, cnt;     // the tile's escapes are [E0, E0 + cnt)
+    uint32_t ps[FB], vv[FB];
+    bool live;            // the same in every thread
+};
+
+template <int TILE>
+__device__ __forceinline__ uint64_t tile_chunks(uint64_t t0, const DecParams &p)
+{
+    const uint64_t tile_end = (t0 + TILE < p.n) ? t0 + TILE : p.n;
+    return ((tile_end - 1) >> p.logC) - (t0 >> p.logC) + 1;
+}
+
 template <int TILE, int NT>
-__device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams &p, PatchShared<TILE> &sh)
+__device__ __forceinline__ PatchHead patch_begin(const StreamIn &s, uint64_t t0, const DecParams &p)
+{
+    static_assert(TILE / 64 + 1 <= NT, "one chunk offset per thread");
+    const int tid = threadIdx.x;
+    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs) + (t0 >> p.logC);
+    PatchHead h;
+    h.M = *reinterpret_cast<const uint64_t *>(s.base + 24);
+    if (p.C <= (uint32_t)TILE) {
+        const uint32_t nc = (uint32_t)tile_chunks<TILE>(t0, p);
+        h.lo = offs[0];
+        h.hi = offs[nc];
+        h.mine = (uint32_t)tid <= nc ? offs[tid] : 0u;
+    } else {
+        h.lo = offs[0];
+        h.hi = offs[1];
+        h.mine = 0u;
+    }
+    return h;
+}
+
+template <int TILE, int NT, int FB>
+__device__ __forceinline__ PatchFetch<FB> patch_fetch(const StreamIn &s, uint64_t t0, const DecParams &p,
+                                                      const PatchHead &h)
 {
     const int tid = threadIdx.x;
-    // M from the header; a value that does not fit the buffer disables the patch
-    const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
-    if (M > p.n || p.off_pos + align256(2 * M) + M > s.bytes) return false;
-    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs);
+    PatchFetch<FB> f;
+    f.E0 = f.cnt = 0;
+    // an M that does not fit the buffer disables the patch
+    const uint64_t M = h.M;
+    if (M > p.n || p.off_pos + align256(2 * M) + M > s.bytes) {
+        f.live = false;
+        return f;
+    }
     const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos);
     const uint8_t *val = s.base + p.off_pos + align256(2 * M);
-    const uint64_t tile_end = (t0 + TILE < p.n) ? t0 + TILE : p.n;
-    uint64_t E0, E1;
-    const bool small_chunks = p.C <= (uint32_t)TILE;
-    const uint64_t c0 = t0 >> p.logC;
-    uint64_t nc = 0;
-    if (small_chunks) {
-        nc = ((tile_end - 1) >> p.logC) - c0 + 1;
-        E0 = offs[c0];
-        E1 = offs[c0 + nc];
-        if (E1 > M) E1 = M;
-        if (E0 > E1) E0 = E1;
+    uint32_t lo = h.lo, hi = h.hi;                 // M < 2^32 here
+    if (hi > (uint32_t)M) hi = (uint32_t)M;
+    if (lo > hi) lo = hi;
+    if (p.C <= (uint32_t)TILE) {
+        f.E0 = lo;
+        f.cnt = hi - lo;
     } else {
         // one chunk spans several tiles: find the escapes whose position
         // falls in this tile by an NT-way search over the ascending positions
-        uint64_t lo = offs[c0], hi = offs[c0 + 1];
-        if (hi > M) hi = M;
-        if (lo > hi) lo = hi;
-        const uint32_t rel0 = (uint32_t)(t0 - (c0 << p.logC));
-        uint64_t res[2];
+        const uint32_t rel0 = (uint32_t)(t0 & (uint64_t)(p.C - 1));
+        uint32_t res[2];
         for (int side = 0; side < 2; side++) {
             const uint32_t target = rel0 + (side ? (uint32_t)TILE : 0u);
-            uint64_t a = lo, b = hi;            // answer in [a, b]
-            while (b - a > (uint64_t)NT) {
-                const uint64_t step = (b - a + NT - 1) / NT;
+            uint32_t a = lo, b = hi;                // answer in [a, b]
+            while (b - a > (uint32_t)NT) {
+                const uint32_t step = (b - a + NT - 1) / NT;
                 const uint64_t j = a + (uint64_t)tid * step;
                 const int below = (j < b) && (pos[j] < target);
                 const int cnt = __syncthreads_count(below);
-                const uint64_t na = (cnt > 0) ? a + (uint64_t)(cnt - 1) * step + 1 : a;
+                const uint32_t na = (cnt > 0) ? a + (uint32_t)(cnt - 1) * step + 1 : a;
                 uint64_t nb = a + (uint64_t)cnt * step;
                 if (nb > b) nb = b;
                 a = na;
-                b = nb;
+                b = (uint32_t)nb;
             }
-            const uint64_t j = a + tid;
+            const uint32_t j = a + tid;
             const int below = (j < b) && (pos[j] < target);
-            res[side] = a + (uint64_t)__syncthreads_count(below);
+            res[side] = a + (uint32_t)__syncthreads_count(below);
         }
-        E0 = res[0];
-        E1 = res[1];
+        f.E0 = res[0];
+        f.cnt = res[1] - res[0];
     }
-    if (E1 <= E0) return false;
+    f.live = f.cnt > 0;
+#pragma unroll
+    for (int u = 0; u < FB; u++) {
+        const uint32_t d = (uint32_t)(u * NT + tid);
+        f.ps[u] = (d < f.cnt) ? pos[f.E0 + d] : 0xFFFFFFFFu;
+        f.vv[u] = (d < f.cnt) ? val[f.E0 + d] : 0u;
+    }
+    return f;
+}
+
+// Marks escape j (position ps, exponent v) in the map of a tile of rem words
+// at t0.
+template <int TILE>
+__device__ __forceinline__ void patch_mark(PatchShared<TILE> &sh, uint64_t t0, uint32_t rem, const DecParams &p,
+                                           uint32_t nc, uint32_t j, uint32_t ps, uint32_t v)
+{
+    uint32_t li;
+    if (p.C <= (uint32_t)TILE) {
+        // last chunk q with offs[q] <= j
+        uint32_t a = 0, b = nc;             // offs[a] <= j < offs[b]
+        while (b - a > 1) {
+            const uint32_t mid = (a + b) >> 1;
+            if (sh.offs[mid] <= j) a = mid; else b = mid;
+        }
+        li = (a << p.logC) + ps;
+    } else {
+        li = ps - (uint32_t)(t0 & (uint64_t)(p.C - 1));   // wraps for a position before the tile
+    }
+    if (ps < p.C && li < rem) {
+        sh.val[li] = (uint8_t)v;
+        atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
+    }
+}
+
+// Returns false (without a barrier) when the tile has no escapes.
+template <int TILE, int NT, int FB>
+__device__ bool patch_build(const StreamIn &s, uint64_t t0, const DecParams &p, const PatchHead &h,
+                            const PatchFetch<FB> &f, PatchShared<TILE> &sh)
+{
+    const int tid = threadIdx.x;
+    if (!f.live) return false;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)TILE) ? p.n - t0 : (uint64_t)TILE);
+    const uint32_t nc = (p.C <= (uint32_t)TILE) ? (uint32_t)tile_chunks<TILE>(t0, p) : 0u;
+    const uint32_t E1 = f.E0 + f.cnt;
     for (int i = tid; i < TILE / 32; i += NT) sh.mask[i] = 0;
-    if (small_chunks)
-        for (uint64_t q = tid; q <= nc; q += NT) {
-            const uint32_t o = offs[c0 + q];
-            sh.offs[q] = o > (uint32_t)E1 ? (uint32_t)E1 : o;
-        }
+    if ((uint32_t)tid <= nc && p.C <= (uint32_t)TILE) sh.offs[tid] = h.mine > E1 ? E1 : h.mine;
     __syncthreads();
-    for (uint64_t jb = E0; jb < E1; jb += 4 * NT) {
-        uint32_t ps[4], vv[4];
-        // issue the loads of 4 escapes per thread before using any of them
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const uint64_t j = jb + (uint64_t)u * NT + tid;
-            ps[u] = (j < E1) ? pos[j] : 0xFFFFFFFFu;
-            vv[u] = (j < E1) ? val[j] : 0u;
-        }
+    for (int u = 0; u < FB; u++) {
+        const uint32_t d = (uint32_t)(u * NT + tid);
+        if (d < f.cnt) patch_mark<TILE>(sh, t0, rem, p, nc, f.E0 + d, f.ps[u], f.vv[u]);
+    }
+    if (f.cnt > (uint32_t)(FB * NT)) {
+        const uint64_t M = h.M;
+        const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos) + f.E0;
+        const uint8_t *val = s.base + p.off_pos + align256(2 * M) + f.E0;
+        for (uint64_t db = FB * NT; db < f.cnt; db += 4 * NT) {
+            uint32_t ps[4], vv[4];
+            // issue the loads of 4 escapes per thread before using any of them
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const uint64_t j = jb + (uint64_t)u * NT + tid;
-            if (j >= E1) continue;
-            uint64_t li;
-            if (small_chunks) {
-                // last chunk q with offs[q] <= j
-                uint32_t a = 0, b = (uint32_t)nc;   // offs[a] <= j < offs[b]
-                while (b - a > 1) {
-                    const uint32_t mid = (a + b) >> 1;
-                    if (sh.offs[mid] <= (uint32_t)j) a = mid; else b = mid;
-                }
-                li = ((uint64_t)a << p.logC) + ps[u];
-            } else {
-                li = (c0 << p.logC) + ps[u] - t0;    // wraps for a corrupt position
+            for (int u = 0; u < 4; u++) {
+                const uint64_t d = db + (uint64_t)(u * NT + tid);
+                ps[u] = (d < f.cnt) ? pos[d] : 0xFFFFFFFFu;
+                vv[u] = (d < f.cnt) ? val[d] : 0u;
             }
-            if (ps[u] < p.C && li < (uint64_t)TILE && t0 + li < p.n) {
-                sh.val[li] = (uint8_t)vv[u];
-                atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint64_t d = db + (uint64_t)(u * NT + tid);
+                if (d < f.cnt) patch_mark<TILE>(sh, t0, rem, p, nc, f.E0 + (uint32_t)d, ps[u], vv[u]);
             }
         }
     }
@@ -922,16 +1014,25 @@ __device__ bool build_patch_map(const StreamIn &s, uint64_t t0, const DecParams 
     return true;
 }
 
-// Apply the patch map to the NW words of a thread's group starting at tile
-// word li0 (y holds NW/2 dwords).
-template <int NW, int TILE>
-__device__ __forceinline__ void apply_patch(const PatchShared<TILE> &sh, uint32_t li0, uint32_t *y)
+// Apply the patch map to the 8 words of a thread's group starting at tile
+// word li0 (a multiple of 8; y holds 4 dwords, word 2q in the low half of
+// y[q]). The group's 8 exponent bytes come in one LDS read; each dword takes
+// its two new exponent fields through one byte permute and one bitfield
+// insert under a mask built from the group's 2 patch bits.
+template <int TILE>
+__device__ __forceinline__ void apply_patch8(const PatchShared<TILE> &sh, uint32_t li0, uint32_t y[4])
 {
-    const uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & ((1u << NW) - 1u);
+    const uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & 0xFFu;
     if (bits == 0) return;
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(&sh.val[li0]);
 #pragma unroll
-    for (int j = 0; j < NW; j++)
-        if ((bits >> j) & 1u) y[j >> 1] = set_exp(y[j >> 1], j & 1, sh.val[li0 + j]);
+    for (int q = 0; q < 4; q++) {
+        const uint32_t t = (bits >> (2 * q)) & 3u;                 // patch bits of words 2q, 2q+1
+        const uint32_t m = (((t * 0x8001u) & 0x10001u) * 0x7F80u);  // their exponent fields
+        const uint32_t src = (q < 2) ? v.x : v.y;
+        const uint32_t e2 = perm(0u, src, (q & 1) ? 0x0C030C02u : 0x0C010C00u) << 7;
+        y[q] = bfi(m, e2, y[q]);
+    }
 }
 
 template <bool kPatch>
@@ -940,75 +1041,55 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_
     __shared__ PatchShared<kDecTile> sh;
     const int tid = threadIdx.x;
     const uint64_t t0 = (uint64_t)blockIdx.x * kDecTile;
+    // words of this tile (scalar), and the tile's bases: lanes index them
+    // with 32-bit offsets
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kDecTile) ? p.n - t0 : (uint64_t)kDecTile);
+    const uint8_t *smt = s.base + kHeader + t0;
+    const uint8_t *cdt = s.base + p.off_codes + t0 / 2;
+    uint16_t *yt = y + t0;
     uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
-#if UZIP_DEC_G8
     // groups of 8 words: group k covers tile words k*kDecThreads*8 + tid*8,
     // so every load and store instruction covers a contiguous span of the wave
     constexpr int kG = kDecGroups * 2;
+    PatchHead ph;
+    if (kPatch) ph = patch_begin<kDecTile, kDecThreads>(s, t0, p);
+    u32x2 sm[kG];
+    uint32_t cd[kG];
+#pragma unroll
+    for (int k = 0; k < kG; k++) {
+        const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+        if (lo < rem) {
+            // sections are padded to 256 bytes, so a tail group's full loads stay inside them
+            sm[k] = ld_stream(reinterpret_cast<const u32x2 *>(smt + lo));
+            cd[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdt + lo / 2));
+        }
+    }
+    PatchFetch<kDecFetch> pf;
+    if (kPatch) pf = patch_fetch<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph);
     uint32_t out[kG][4];
 #pragma unroll
     for (int k = 0; k < kG; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 8) + (uint64_t)tid * 8;
-        if (g0 < p.n) {
-            // sections are padded to 256 bytes, so a tail group's full loads stay inside them
-            const u32x2 sm = ld_stream(reinterpret_cast<const u32x2 *>(s.base + kHeader + g0));
-            const uint32_t cd = ld_stream(reinterpret_cast<const uint32_t *>(s.base + p.off_codes + g0 / 2));
-            decode8(sm.x, sm.y, cd, dec, out[k]);
-        }
+        const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+        if (lo < rem) decode8(sm[k].x, sm[k].y, cd[k], dec, out[k]);
     }
     if (kPatch) {
-        if (build_patch_map<kDecTile, kDecThreads>(s, t0, p, sh)) {
+        if (patch_build<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) {
 #pragma unroll
             for (int k = 0; k < kG; k++)
-                apply_patch<8>(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), out[k]);
+                apply_patch8(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), out[k]);
         }
     }
 #pragma unroll
     for (int k = 0; k < kG; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 8) + (uint64_t)tid * 8;
-        if (g0 + 8 <= p.n) {
+        const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+        if (lo + 8 <= rem) {
             u32x4 v = {out[k][0], out[k][1], out[k][2], out[k][3]};
-            st_stream(v, reinterpret_cast<u32x4 *>(y + g0));
-        } else if (g0 < p.n) {
-            for (int j = 0; j < 8 && g0 + j < p.n; j++)
-                y[g0 + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
+            st_stream(v, reinterpret_cast<u32x4 *>(yt + lo));
+        } else if (lo < rem) {
+            for (uint32_t j = 0; j < 8 && lo + j < rem; j++)
+                yt[lo + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
         }
     }
-#else
-    uint32_t out[kDecGroups][8];
-#pragma unroll
-    for (int k = 0; k < kDecGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 16) + (uint64_t)tid * 16;
-        if (g0 < p.n) {
-            // sections are padded to 256 bytes, so a tail group's full loads stay inside them
-            const u32x4 sm = ld_stream(reinterpret_cast<const u32x4 *>(s.base + kHeader + g0));
-            const u32x2 cd = ld_stream(reinterpret_cast<const u32x2 *>(s.base + p.off_codes + g0 / 2));
-            decode8(sm.x, sm.y, cd.x, dec, &out[k][0]);
-            decode8(sm.z, sm.w, cd.y, dec, &out[k][4]);
-        }
-    }
-    if (kPatch) {
-        if (build_patch_map<kDecTile, kDecThreads>(s, t0, p, sh)) {
-#pragma unroll
-            for (int k = 0; k < kDecGroups; k++)
-                apply_patch<16>(sh, (uint32_t)(k * (kDecThreads * 16) + tid * 16), out[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < kDecGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kDecThreads * 16) + (uint64_t)tid * 16;
-        if (g0 + 16 <= p.n) {
-            u32x4 *dst = reinterpret_cast<u32x4 *>(y + g0);
-            u32x4 v0 = {out[k][0], out[k][1], out[k][2], out[k][3]};
-            u32x4 v1 = {out[k][4], out[k][5], out[k][6], out[k][7]};
-            st_stream(v0, dst);
-            st_stream(v1, dst + 1);
-        } else if (g0 < p.n) {
-            for (int j = 0; j < 16 && g0 + j < p.n; j++)
-                y[g0 + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
-        }
-    }
-#endif
 }
 
 // Two-kernel variant, step 2: for every escape, overwrite the exponent field
@@ -1053,17 +1134,32 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
     uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
+    const uint32_t rem = enc_tile_words(t0, ep);
+    const PatchHead ha = patch_begin<kEncTile, kEncThreads>(sa, t0, dp);
+    const PatchHead hb = patch_begin<kEncTile, kEncThreads>(sb, t0, dp);
+    const uint8_t *smta = sa.base + kHeader + t0, *cdta = sa.base + dp.off_codes + t0 / 2;
+    const uint8_t *smtb = sb.base + kHeader + t0, *cdtb = sb.base + dp.off_codes + t0 / 2;
+    u32x2 sma[kEncGroups], smb[kEncGroups];
+    uint32_t cda[kEncGroups], cdb[kEncGroups];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        if (lo < rem) {
+            sma[k] = ld_stream(reinterpret_cast<const u32x2 *>(smta + lo));
+            cda[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdta + lo / 2));
+            smb[k] = ld_stream(reinterpret_cast<const u32x2 *>(smtb + lo));
+            cdb[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdtb + lo / 2));
+        }
+    }
+    const PatchFetch<kRedFetch> fa = patch_fetch<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha);
+    const PatchFetch<kRedFetch> fb = patch_fetch<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb);
     uint32_t ya[kEncGroups][4], yb[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint64_t g0 = t0 + (uint64_t)k * (kEncThreads * 8) + (uint64_t)tid * 8;
-        if (g0 < dp.n) {
-            const u32x2 sma = ld_stream(reinterpret_cast<const u32x2 *>(sa.base + kHeader + g0));
-            const uint32_t cda = ld_stream(reinterpret_cast<const uint32_t *>(sa.base + dp.off_codes + g0 / 2));
-            const u32x2 smb = ld_stream(reinterpret_cast<const u32x2 *>(sb.base + kHeader + g0));
-            const uint32_t cdb = ld_stream(reinterpret_cast<const uint32_t *>(sb.base + dp.off_codes + g0 / 2));
-            decode8(sma.x, sma.y, cda, dec, ya[k]);
-            decode8(smb.x, smb.y, cdb, dec, yb[k]);
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        if (lo < rem) {
+            decode8(sma[k].x, sma[k].y, cda[k], dec, ya[k]);
+            decode8(smb[k].x, smb[k].y, cdb[k], dec, yb[k]);
         } else {
 #pragma unroll
             for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
@@ -1071,16 +1167,16 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     }
     // the code table goes to LDS after the data loads are in flight
     load_wave_lut(esh, ep.lut);
-    if (build_patch_map<kEncTile, kEncThreads>(sa, t0, dp, lds.patch)) {
+    if (patch_build<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha, fa, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch<8>(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ya[k]);
+            apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ya[k]);
     }
     __syncthreads();       // the map is rebuilt for the second input
-    if (build_patch_map<kEncTile, kEncThreads>(sb, t0, dp, lds.patch)) {
+    if (patch_build<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb, fb, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch<8>(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), yb[k]);
+            apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), yb[k]);
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
@@ -1090,7 +1186,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank(r, t0, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
