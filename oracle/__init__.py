@@ -9,8 +9,9 @@ this module only marshals NumPy arrays through ctypes. See that file's header
 for the passages each function follows and the readings taken where the pages
 leave a point open.
 
-Parity status: split/merge, histogram, Top-16, encode, decode and the reduce's
-rounding are pinned by the tests under ``tests/test_oracle_*.py``. The one
+Parity status: split/merge, histogram, Top-16, encode, decode, the reduce's
+rounding and the k-input reduce's summation order are pinned by the tests
+under ``tests/test_oracle_*.py``. The one
 choice the pages do not fix at all -- a NaN sum in the reduce becomes 0x7FC0 --
 is "parity unpinned" (it is our own convention).
 """
@@ -71,6 +72,9 @@ def _load():
         "orc_stream_total": (c64, [u8p]),
         "orc_bf16_rne_array": (None, [ctypes.POINTER(ctypes.c_uint32), c64, u16p]),
         "orc_add_bf16_array": (None, [u16p, u16p, c64, u16p]),
+        "orc_sum_bf16": (ctypes.c_uint16, [u16p, c32, c64]),
+        "orc_reduce_k": (c64, [ctypes.POINTER(u8p), u64p, c32, c64, c32, u8p, u8p, c64, u16p]),
+        "orc_sum_bf16_array": (None, [u16p, c32, c64, u16p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -191,6 +195,34 @@ def reduce_add(sa, sb, n: int, chunk: int, dec) -> np.ndarray:
     if total == 0:
         raise ValueError("oracle reduce_add failed")
     return out[:total].copy()
+
+
+def reduce_k(streams, n: int, chunk: int, dec) -> np.ndarray:
+    """k-input reduce of compressed streams (same n, chunk and codebook)."""
+    arrs = [np.ascontiguousarray(x, dtype=np.uint8) for x in streams]
+    k = len(arrs)
+    dec = np.ascontiguousarray(dec, dtype=np.uint8)
+    cap = max_bytes(n, chunk)
+    out = np.empty(cap, dtype=np.uint8)
+    tmp = np.empty((k + 1) * n, dtype=np.uint16)
+    ptrs = (ctypes.POINTER(ctypes.c_uint8) * max(k, 1))(*[_p(x, ctypes.c_uint8) for x in arrs])
+    sizes = (ctypes.c_uint64 * max(k, 1))(*[x.size for x in arrs])
+    total = _load().orc_reduce_k(ptrs, sizes, k, n, chunk, _p(dec, ctypes.c_uint8),
+                                 _p(out, ctypes.c_uint8), cap, _p(tmp, ctypes.c_uint16))
+    if total == 0:
+        raise ValueError("oracle reduce_k failed")
+    return out[:total].copy()
+
+
+def sum_words(rows) -> np.ndarray:
+    """k-input reduce arithmetic on raw words (no codec): rows is (k, n)."""
+    v = np.ascontiguousarray(rows, dtype=np.uint16)
+    if v.ndim != 2:
+        raise ValueError("rows must be (k, n)")
+    k, n = v.shape
+    r = np.empty(n, dtype=np.uint16)
+    _load().orc_sum_bf16_array(_p(v, ctypes.c_uint16), k, n, _p(r, ctypes.c_uint16))
+    return r
 
 
 def add_words(a, b) -> np.ndarray:

@@ -17,7 +17,12 @@
  *         code and are overwritten from the position list).
  *   [UZ]  "UCCL-Zip: Lossless Compression Supercharged GPU Communication",
  *         section 3.4 / Figure 6: a receiver decompresses a slice, reduces it
- *         with its own slice, and recompresses the result.
+ *         with its own slice, and recompresses the result; section 5.2 /
+ *         Figure 9: two-shot all-reduce, whose reduce-scatter phase
+ *         decompresses every received chunk before reducing it.
+ *   [ZC]  "ZipCCL: Efficient Lossless Data Compression of Communication
+ *         Collectives", adaptive communication strategies: a zipped
+ *         all-to-all followed by a local reduction.
  *
  * Readings where the pages leave a point open (each is the plainest reading;
  * the same list stands in the design notes):
@@ -35,7 +40,12 @@
  *   - reduce: one IEEE binary32 add of the two decoded values (round to
  *     nearest even, subnormals kept), then round-half-to-even to BF16; a NaN
  *     sum becomes 0x7FC0 (this last choice is ours: parity unpinned by the
- *     pages).
+ *     pages);
+ *   - k-input reduce: the k values are added in binary32 in input order, one
+ *     rounding per add, and the sum is rounded once to BF16 (the pages name
+ *     the operation, a local reduction of received chunks, but not its
+ *     arithmetic; this is the plainest reading that agrees with the
+ *     two-input case).
  *
  * Everything here is scalar C on 16-bit words; floats appear only in the
  * reduce's binary32 add. Build: gcc -O2 -std=c99 -ffp-contract=off (no
@@ -277,6 +287,40 @@ uint64_t orc_reduce_add(const uint8_t *a, uint64_t a_bytes, const uint8_t *b, ui
     return orc_encode(r, n, C, dec, out, cap);
 }
 
+/* One element of the k-input reduce: the k values added in binary32 in
+ * input order (the first value is the starting sum; k - 1 IEEE adds, each
+ * rounded to nearest even), then rounded once to BF16. v[i * stride] is the
+ * element of input i. */
+uint16_t orc_sum_bf16(const uint16_t *v, uint32_t k, uint64_t stride)
+{
+    volatile float s = orc_bf16_to_f32(v[0]);
+    for (uint32_t i = 1; i < k; i++) s = s + orc_bf16_to_f32(v[(uint64_t)i * stride]);
+    float sv = s;
+    uint32_t u;
+    memcpy(&u, &sv, 4);
+    return orc_bf16_rne(u);
+}
+
+/* The k-input reduce: the local step of one GPU after a compressed exchange
+ * ([ZC], adaptive communication strategies: a zipped all-to-all followed by
+ * a local reduction; [UZ] section 5.2, Figure 9: in the reduce-scatter phase
+ * of a two-shot all-reduce each received chunk is decompressed before it is
+ * reduced). Decode the k inputs, sum each element as orc_sum_bf16 does, and
+ * encode the sums with the same codebook and chunk size. k = 2 is
+ * orc_reduce_add; k = 1 re-encodes the input with every NaN made 0x7FC0.
+ * tmp must hold (k + 1) n words. Returns the output stream size or 0. */
+uint64_t orc_reduce_k(const uint8_t *const *in, const uint64_t *in_bytes, uint32_t k,
+                      uint64_t n, uint32_t C, const uint8_t *dec,
+                      uint8_t *out, uint64_t cap, uint16_t *tmp)
+{
+    if (k == 0) return 0;
+    for (uint32_t i = 0; i < k; i++)
+        if (orc_decode(in[i], in_bytes[i], n, C, dec, tmp + (uint64_t)i * n) != 0) return 0;
+    uint16_t *r = tmp + (uint64_t)k * n;
+    for (uint64_t e = 0; e < n; e++) r[e] = orc_sum_bf16(tmp + e, k, n);
+    return orc_encode(r, n, C, dec, out, cap);
+}
+
 /* ------------------------------------------------------------- validate -- */
 /* Full structural check of a stream against the caller's codebook.
  * 0 = ok, -3 = malformed, -4 = codebook differs. */
@@ -336,4 +380,10 @@ void orc_bf16_rne_array(const uint32_t *u, uint64_t n, uint16_t *out)
 void orc_add_bf16_array(const uint16_t *a, const uint16_t *b, uint64_t n, uint16_t *r)
 {
     for (uint64_t i = 0; i < n; i++) r[i] = orc_add_bf16(a[i], b[i]);
+}
+
+/* v holds k rows of n words; r[e] = orc_sum_bf16 of column e. */
+void orc_sum_bf16_array(const uint16_t *v, uint32_t k, uint64_t n, uint16_t *r)
+{
+    for (uint64_t e = 0; e < n; e++) r[e] = orc_sum_bf16(v + e, k, n);
 }

@@ -39,9 +39,16 @@ MUTANTS = {
                              "y[i] = orc_merge(0, in[L.val + j]);"),
     "validate_equal_positions": ("if (j > j0 && p <= get_u16", "if (j > j0 && p < get_u16"),
     "validate_skips_nibble": ("if (code != 0) return -3;", "if (code > 15) return -3;"),
+    "sum_order_reversed": ("volatile float s = orc_bf16_to_f32(v[0]);\n"
+                           "    for (uint32_t i = 1; i < k; i++) s = s + orc_bf16_to_f32(v[(uint64_t)i * stride]);",
+                           "volatile float s = orc_bf16_to_f32(v[(uint64_t)(k - 1) * stride]);\n"
+                           "    for (uint32_t i = k - 1; i-- > 0;) s = s + orc_bf16_to_f32(v[(uint64_t)i * stride]);"),
+    "sum_in_binary64": ("volatile float s = orc_bf16_to_f32(v[0]);", "volatile double s = orc_bf16_to_f32(v[0]);"),
+    "sum_skips_first_input": ("for (uint32_t i = 1; i < k; i++) s = s +", "for (uint32_t i = 2; i < k; i++) s = s +"),
 }
 
-PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py"]
+PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py",
+             "tests/test_oracle_reduce_k.py"]
 
 
 def _run(name, a, b, tmp):
