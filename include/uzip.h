@@ -103,7 +103,7 @@ typedef struct uzip_opts {
  * Returns 0 when n or C is invalid. */
 uint64_t uzip_max_bytes(uint64_t n, uint32_t chunk);
 
-/* Device workspace that uzip_encode / uzip_reduce_add need for (n, C): per-tile
+/* Device workspace that uzip_encode / uzip_reduce_add / uzip_reduce_k need for (n, C): per-tile
  * escape counts and prefixes, and a staging area for each tile's escapes
  * (at most 3 bytes per value). Returns 0 when n or C is invalid. */
 uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk);
@@ -191,6 +191,35 @@ int uzip_reduce_add_ex(const void *d_a, uint64_t a_bytes, const void *d_b, uint6
                        uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
                        void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
                        const uzip_opts_t *opts, hipStream_t s);
+
+/* async. k-input fused reduce: the local step of one GPU after a compressed
+ * exchange, for instance its shard of the reduce-scatter phase of a two-shot
+ * all-reduce ("UCCL-Zip: Lossless Compression Supercharged GPU
+ * Communication", section 5.2 / Figure 9: every received chunk is
+ * decompressed before it is reduced; "ZipCCL: Efficient Lossless Data
+ * Compression of Communication Collectives", adaptive communication
+ * strategies: a zipped all-to-all followed by a local reduction).
+ *   r[i] = bf16_rne( (...((float)X0[i] + (float)X1[i]) + ...) + (float)Xk-1[i] )
+ * The k values are added in binary32 in input order, each add rounded to
+ * nearest even with subnormals kept, and the sum is rounded once,
+ * half-to-even, to BF16; a NaN sum becomes 0x7FC0. k = 2 gives exactly
+ * uzip_reduce_add; k = 1 re-encodes the input with every NaN made 0x7FC0.
+ * d_in is a host array of k device stream pointers (16-byte aligned) and
+ * in_bytes a host array of their readable sizes; both are read during the
+ * call only. 1 <= k <= UZIP_MAX_K. Every input is a stream of n values at
+ * chunk C under codebook cb; the result is encoded with the same n, C and cb
+ * into d_out (out_cap >= uzip_max_bytes), with workspace as for uzip_encode.
+ * Errors: UZIP_EINVAL (k out of range, a null or misaligned pointer, an
+ * input smaller than an escape-free stream) and UZIP_ENOSPC, detected on the
+ * host before any launch; UZIP_EHIP. As for uzip_decode, the input headers
+ * are not checked: use uzip_validate for untrusted input. */
+#define UZIP_MAX_K 16
+int uzip_reduce_k(const void *const *d_in, const uint64_t *in_bytes, uint32_t k, uint64_t n, uint32_t chunk,
+                  const uzip_codebook_t *cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                  hipStream_t s);
+int uzip_reduce_k_ex(const void *const *d_in, const uint64_t *in_bytes, uint32_t k, uint64_t n, uint32_t chunk,
+                     const uzip_codebook_t *cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                     const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Copies a device stream of `bytes` bytes to the host and runs
  * uzip_validate_host on it. */

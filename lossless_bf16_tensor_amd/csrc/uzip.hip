@@ -1190,6 +1190,100 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
+// k-input reduce: the inputs of one call, passed by value.
+struct StreamSet {
+    StreamIn in[UZIP_MAX_K];
+    uint32_t k;
+};
+
+// Dense loads of one input's part of a tile: per group, 8 sign-mantissa
+// bytes and 4 code bytes.
+struct DenseIn {
+    u32x2 sm[kEncGroups];
+    uint32_t cd[kEncGroups];
+};
+
+__device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint32_t rem, const DecParams &p,
+                                           DenseIn &d)
+{
+    const int tid = threadIdx.x;
+    const uint8_t *smt = s.base + kHeader + t0, *cdt = s.base + p.off_codes + t0 / 2;
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        if (lo < rem) {
+            d.sm[k] = ld_stream(reinterpret_cast<const u32x2 *>(smt + lo));
+            d.cd[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdt + lo / 2));
+        } else {
+            d.sm[k] = u32x2{0u, 0u};
+            d.cd[k] = 0u;
+        }
+    }
+}
+
+// One tile of the k-input reduce. Each thread keeps binary32 sums of its
+// 4 groups of 8 words. The inputs are taken in order: input i is decoded,
+// patched through the LDS map, and added to the sums (input 0 sets them),
+// while the chunk offsets and dense bytes of input i + 1 are already in
+// flight. The sums are rounded once to BF16 and encoded like k_reduce_tile.
+__global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uint8_t *__restrict__ out,
+                                                               EncWs ws, EncParams ep, DecParams dp)
+{
+    __shared__ EncShared esh;
+    __shared__ ReduceLds lds;
+    const int tid = threadIdx.x;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kEncTile;
+    const uint32_t rem = enc_tile_words(t0, ep);
+    uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
+    float acc[kEncGroups][8] = {};
+    PatchHead h = patch_begin<kEncTile, kEncThreads>(ss.in[0], t0, dp);
+    DenseIn cur;
+    load_dense(ss.in[0], t0, rem, dp, cur);
+    load_wave_lut(esh, ep.lut);
+    for (uint32_t i = 0; i < ss.k; i++) {
+        const StreamIn si = ss.in[i];
+        const PatchFetch<kRedFetch> f = patch_fetch<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h);
+        PatchHead hn = h;
+        DenseIn nxt = cur;
+        if (i + 1 < ss.k) {
+            hn = patch_begin<kEncTile, kEncThreads>(ss.in[i + 1], t0, dp);
+            load_dense(ss.in[i + 1], t0, rem, dp, nxt);
+        }
+        uint32_t y[kEncGroups][4];
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++) decode8(cur.sm[k].x, cur.sm[k].y, cur.cd[k], dec, y[k]);
+        if (patch_build<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h, f, lds.patch)) {
+#pragma unroll
+            for (int k = 0; k < kEncGroups; k++)
+                apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), y[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float v0 = __uint_as_float(y[k][q] << 16), v1 = __uint_as_float(y[k][q] & 0xFFFF0000u);
+                acc[k][2 * q] = (i == 0) ? v0 : acc[k][2 * q] + v0;
+                acc[k][2 * q + 1] = (i == 0) ? v1 : acc[k][2 * q + 1] + v1;
+            }
+        __syncthreads();       // the map is rebuilt for the next input
+        h = hn;
+        cur = nxt;
+    }
+    uint32_t r[kEncGroups][4];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            r[k][q] = (lo < rem) ? perm(bf16_rne_hi(acc[k][2 * q + 1]), bf16_rne_hi(acc[k][2 * q]), 0x07060302u)
+                                 : 0u;
+    }
+    uint32_t cstart[kEncGroups];
+    const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
+}
+
 // ================================================================ host ====
 thread_local char g_hip_err[160];
 
@@ -1581,6 +1675,41 @@ int uzip_reduce_add(const void *d_a, uint64_t a_bytes, const void *d_b, uint64_t
 {
     return uzip_reduce_add_ex(d_a, a_bytes, d_b, b_bytes, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes,
                               nullptr, s);
+}
+
+int uzip_reduce_k_ex(const void *const *d_in, const uint64_t *in_bytes, uint32_t k, uint64_t n, uint32_t chunk,
+                     const uzip_codebook_t *cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                     const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !in_bytes || !d_out || !d_ws || k == 0 || k > UZIP_MAX_K) return UZIP_EINVAL;
+    if (!aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk);
+    StreamSet ss{};
+    ss.k = k;
+    for (uint32_t i = 0; i < k; i++) {
+        if (!d_in[i] || !aligned16(d_in[i]) || in_bytes[i] < total_of(L, 0)) return UZIP_EINVAL;
+        ss.in[i] = StreamIn{static_cast<const uint8_t *>(d_in[i]), in_bytes[i]};
+    }
+    const EncParams ep = make_enc_params(L, cb);
+    const DecParams dp = make_dec_params(L, cb);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    k_reduce_k_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(ss, static_cast<uint8_t *>(d_out), ws, ep, dp);
+    UZIP_LAUNCH_CHECK("k_reduce_k_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_reduce_k(const void *const *d_in, const uint64_t *in_bytes, uint32_t k, uint64_t n, uint32_t chunk,
+                  const uzip_codebook_t *cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                  hipStream_t s)
+{
+    return uzip_reduce_k_ex(d_in, in_bytes, k, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
 }
 
 int uzip_validate(const void *d_stream, uint64_t bytes, const uzip_codebook_t *cb, hipStream_t s)

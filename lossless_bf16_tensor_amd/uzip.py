@@ -25,8 +25,10 @@ EXPORTS = (
     "uzip_max_bytes", "uzip_workspace_bytes", "uzip_codebook_from_hist", "uzip_validate_host",
     "uzip_parse_header", "uzip_strerror", "uzip_histogram", "uzip_calibrate", "uzip_encode",
     "uzip_encode_ex", "uzip_stream_bytes", "uzip_decode", "uzip_decode_ex", "uzip_reduce_add",
-    "uzip_reduce_add_ex", "uzip_validate",
+    "uzip_reduce_add_ex", "uzip_reduce_k", "uzip_reduce_k_ex", "uzip_validate",
 )
+
+MAX_K = 16                      # UZIP_MAX_K
 
 
 class UzipError(RuntimeError):
@@ -82,6 +84,10 @@ def lib():
         "uzip_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
         "uzip_reduce_add": (i32, [vp, u64, vp, u64, u64, u32, cbp, vp, u64, vp, u64, vp]),
         "uzip_reduce_add_ex": (i32, [vp, u64, vp, u64, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_reduce_k": (i32, [ctypes.POINTER(vp), ctypes.POINTER(u64), u32, u64, u32, cbp, vp, u64, vp, u64,
+                                vp]),
+        "uzip_reduce_k_ex": (i32, [ctypes.POINTER(vp), ctypes.POINTER(u64), u32, u64, u32, cbp, vp, u64, vp,
+                                   u64, op, vp]),
         "uzip_validate": (i32, [vp, u64, cbp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -240,6 +246,25 @@ def reduce_add(a: torch.Tensor, b: torch.Tensor, cb: Codebook, n: int, chunk: in
     _check(lib().uzip_reduce_add_ex(_ptr(a), a.numel(), _ptr(b), b.numel(), n, chunk, ctypes.byref(cb),
                                     _ptr(out), out.numel(), _ptr(ws), ws.numel(),
                                     ctypes.byref(o) if o else None, _stream(stream)), "reduce_add")
+    return out
+
+
+def reduce_k(streams, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
+             ws: torch.Tensor | None = None, events=None, stream=None) -> torch.Tensor:
+    """Fused k-input reduce of uint8 device streams (each tensor's numel bounds
+    its reads): decode all, add in binary32 in list order, round once to BF16,
+    encode."""
+    k = len(streams)
+    if out is None:
+        out = torch.empty(max_bytes(n, chunk), dtype=torch.uint8, device=streams[0].device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=streams[0].device)
+    ptrs = (ctypes.c_void_p * max(k, 1))(*[_ptr(t) for t in streams])
+    sizes = (ctypes.c_uint64 * max(k, 1))(*[t.numel() for t in streams])
+    o = _opts(events)
+    _check(lib().uzip_reduce_k_ex(ptrs, sizes, k, n, chunk, ctypes.byref(cb), _ptr(out), out.numel(),
+                                  _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
+           "reduce_k")
     return out
 
 

@@ -138,6 +138,17 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_decode(p, big, 1000, 1024, cbr, mis, None) == -1
     assert L.uzip_reduce_add(p, big, p, big, 1000, 1024, cbr, p, big, p, ws - 1, None) == -2
     assert L.uzip_reduce_add(p, 5, p, big, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    ptrs = (ctypes.c_void_p * 17)(*([p] * 17))
+    sizes = (ctypes.c_uint64 * 17)(*([big] * 17))
+    assert L.uzip_reduce_k(ptrs, sizes, 0, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_reduce_k(ptrs, sizes, 17, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_reduce_k(None, sizes, 2, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_reduce_k(ptrs, sizes, 16, 1000, 1024, cbr, p, big, p, ws - 1, None) == -2
+    sizes[3] = 5
+    assert L.uzip_reduce_k(ptrs, sizes, 4, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    sizes[3] = big
+    ptrs[2] = mis
+    assert L.uzip_reduce_k(ptrs, sizes, 4, 1000, 1024, cbr, p, big, p, ws, None) == -1
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1

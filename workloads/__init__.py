@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "bf16_bits", "config_1", "config_2", "config_3", "config_4",
-    "config_5", "config", "all_patterns", "random_words", "CONFIG_NAMES",
+    "config_5", "config", "reduce_shards", "all_patterns", "random_words", "CONFIG_NAMES",
 ]
 
 CONFIG_NAMES = {
@@ -177,6 +177,19 @@ def config_5(buckets: int = 512, bucket: int = 1 << 20, seed_a: int = 50,
     b = _grad_buffer(seed_b, buckets, bucket)
     return Workload(CONFIG_NAMES[5], (a, b), (a, b), (1024,), (buckets * bucket,),
                     f"seeds {seed_a}/{seed_b}; {buckets} buckets of {bucket}")
+
+
+def reduce_shards(k: int = 8, buckets: int = 64, bucket: int = 1 << 20, seed0: int = 60) -> Workload:
+    """One GPU's share of the gradient-reduce step done as a two-shot
+    all-reduce over k GPUs: the shard of each GPU's buffer that this GPU
+    reduces. Each of the k shards follows the gradient-buffer recipe of
+    config 5 (sigma log-uniform in [1e-5, 1e-2] per 2^20-value bucket) with
+    its own seed, seed0 + i; at the default size a shard is 2^26 values, the
+    eighth of a config-5 buffer. The codebook comes from the k shards'
+    histograms added together."""
+    xs = tuple(_grad_buffer(seed0 + i, buckets, bucket) for i in range(k))
+    return Workload(f"reduce-shards-{k}x{buckets * bucket}", xs, xs, (1024,), (buckets * bucket,),
+                    f"seeds {seed0}..{seed0 + k - 1}; {buckets} buckets of {bucket} per shard")
 
 
 def config(k: int, small: bool = False) -> Workload:
