@@ -239,6 +239,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-oracle-check", action="store_true")
     ap.add_argument("--no-reduce", action="store_true")
+    ap.add_argument("--no-reduce-k", action="store_true")
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
@@ -404,6 +405,50 @@ def main():
                   "GBps_uncompressed_in": round(2 * 2 * n / (t_red * 1e-3) / 1e9, 1),
                   "inputs": "the workload and the same tensor with its K and V halves swapped"}
 
+    # --- k-input fused reduce: one GPU's share of a two-shot all-reduce over
+    # 8 GPUs (8 shards of 2^26 values, gradient recipe) ---
+    reduce_k = None
+    if not args.no_reduce_k:
+        log("reduce_k: generating 8 shards of 2^26")
+        ws_k = workloads.reduce_shards(8)
+        nk = ws_k.x[0].size
+        hist_k = None
+        shards = []
+        for r in ws_k.x:
+            t = torch.from_numpy(r.view(np.int16)).to(dev)
+            hist_k = uzip.histogram(t, hist_k)
+            shards.append(t)
+        cbk = uzip.codebook_from_hist(hist_k.cpu().numpy().astype(np.uint64))
+        streams = []
+        in_bytes = 0
+        for t in shards:
+            o = uzip.encode(t, cbk, C)
+            tt, _ = uzip.stream_bytes(o)
+            streams.append(o[:tt])
+            in_bytes += tt
+        del shards
+        outk = torch.empty(uzip.max_bytes(nk, C), dtype=torch.uint8, device=dev)
+        wsk = torch.empty(uzip.workspace_bytes(nk, C), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            uzip.reduce_k(streams, cbk, nk, C, out=outk, ws=wsk)
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+        for row in kev:
+            for e in row:
+                e.record()
+        for k in range(10):
+            flush()
+            uzip.reduce_k(streams, cbk, nk, C, out=outk, ws=wsk, events=kev[k])
+        torch.cuda.synchronize()
+        t_k = float(np.mean([kev[k][0].elapsed_time(kev[k][3]) for k in range(10)]))
+        t_kt = float(np.mean([kev[k][0].elapsed_time(kev[k][1]) for k in range(10)]))
+        out_bytes, mk = uzip.stream_bytes(outk)
+        reduce_k = {"k": len(streams), "n_per_input": nk, "ms": round(t_k, 4), "k_reduce_k_tile_ms": round(t_kt, 4),
+                    "GBps_uncompressed_in": round(len(streams) * 2 * nk / (t_k * 1e-3) / 1e9, 1),
+                    "stream_roofline_frac": round((in_bytes + out_bytes) / (t_k * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "escape_rate_out": round(mk / nk, 6),
+                    "inputs": f"{ws_k.name}: one GPU's share of a two-shot all-reduce over 8 GPUs"}
+        del streams, outk, wsk
+
     res = {
         "metric": "encode/decode GB/s (uncompressed BF16) + ratio, 2^28-elt KV, 1 MI355X",
         "value": round(value, 1), "unit": "GB/s",
@@ -431,6 +476,7 @@ def main():
         "cache_flush_mib_before_each_call": args.flush_mib,
         "round_trip_bit_exact": round_trip, "oracle_stream_equal": parity,
         "reduce": reduce,
+        "reduce_k": reduce_k,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
