@@ -114,6 +114,12 @@ uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk);
  * fewer than 16 bins are non-zero. Returns UZIP_OK or UZIP_EINVAL (NULL). */
 int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
 
+/* Builds the codebook whose decode table is dec[16] (for instance the one a
+ * stream's header carries, from uzip_parse_header), enc and member from it,
+ * hist and n_cal zero. Enough to decode, validate or reduce that stream.
+ * Returns UZIP_OK, or UZIP_EINVAL (NULL, or entries not distinct). */
+int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
+
 /* Full structural check of a stream held in host memory: header fields,
  * section sizes, zero padding, offsets monotone and ending at M, positions
  * ascending and inside their chunk, every escape value outside the codebook
@@ -135,6 +141,15 @@ const char *uzip_strerror(int code);
  * zeroes d_hist first, or keeps earlier counts to pool several sets (page
  * section 3.3, the histogram step of calibration). */
 int uzip_histogram(const uint16_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s);
+
+/* async. As uzip_histogram, over a sample of d_x: the first `sample` words
+ * of every block of `block` words (the last block may be partial). block and
+ * sample are multiples of 8 with 8 <= sample <= block; block = 0 means all
+ * of d_x. This is the sampled estimate of the exponent distribution that
+ * "CCCL" (section 4.3, localized frequency tables) builds from the first
+ * part of each block's data range (256 KB in its example). */
+int uzip_histogram_sampled(const uint16_t *d_x, uint64_t n, uint64_t block, uint64_t sample,
+                           uint64_t *d_hist, hipStream_t s);
 
 /* blocking. Calibrates a codebook on d_x[0..n) (page section 3.3).
  * It runs the histogram on the device into d_hist_ws (256 x u64 scratch the
@@ -158,6 +173,29 @@ int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_c
 /* blocking. Reads a device stream's header. Returns its size and M.
  * Either output pointer may be NULL. */
 int uzip_stream_bytes(const void *d_stream, uint64_t *total_bytes, uint64_t *m, hipStream_t s);
+
+/* async. Encode with a codebook calibrated on the input itself, entirely on
+ * the device (no host round trip): the exponent histogram of a sample of
+ * d_x (the first `sample` words of every `block` words; block = 0: all of
+ * d_x, as for uzip_histogram_sampled), its Top-16 and tables by the same
+ * rule as uzip_codebook_from_hist, then uzip_encode with those tables. This
+ * is the per-input "dynamic Top-16" that "SplitZip: Ultra Fast Lossless KV
+ * Compression for Disaggregated LLM Serving" measures against offline
+ * calibration (section 4.3, Table 7), with the sampled estimate of "CCCL"
+ * (section 4.3, localized frequency tables) as an option. The stream header
+ * carries dec[16]; a receiver rebuilds the codebook with
+ * uzip_codebook_from_dec. If d_cb is not NULL (8-byte aligned device
+ * memory) the whole codebook is also written there. d_out, d_ws and the
+ * errors are as for uzip_encode; the workspace also holds the histogram.
+ * Events (uzip_opts_t): [0] before the first kernel, [1] after the three
+ * calibration kernels, [2] after the dense pass, [3] after the tile sums,
+ * [4] after the escape placement. */
+int uzip_encode_online(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t block, uint64_t sample,
+                       uzip_codebook_t *d_cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       hipStream_t s);
+int uzip_encode_online_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t block, uint64_t sample,
+                          uzip_codebook_t *d_cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                          const uzip_opts_t *opts, hipStream_t s);
 
 /* async. Decodes a stream of n values at chunk C into d_y[0..n) (page
  * section 3.2: nibble unpack, 16-entry lookup, merge with the sign-mantissa

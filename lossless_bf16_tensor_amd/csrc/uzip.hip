@@ -118,6 +118,9 @@ static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: 
 
 // Encode workspace (see uzip_workspace_bytes).
 struct EncWs {
+    unsigned long long *hist;  // [256] exponent histogram (online calibration)
+    uint8_t *lut;          // [256] code table built on the device (online calibration)
+    uint8_t *dec;          // [16] its decode table
     uint32_t *counts;      // [ntiles] escapes per tile
     uint32_t *gsum;        // [ngroups] escapes per group of 2^gshift tiles
     uint32_t *tpre;        // [ntiles] escapes of the tiles before it inside its group
@@ -127,7 +130,7 @@ struct EncWs {
 };
 
 struct WsLayout {
-    uint64_t counts, gsum, tpre, chunk_pre, stage_pos, stage_val, total;
+    uint64_t hist, lut, dec, counts, gsum, tpre, chunk_pre, stage_pos, stage_val, total;
 };
 
 // Tiles are summed in groups of 2^gshift, with gshift about half of log2(ntiles)
@@ -146,7 +149,10 @@ WsLayout ws_layout(uint64_t n, uint32_t C)
     uint64_t ngroups = (ntiles + (1ull << group_shift(ntiles)) - 1) >> group_shift(ntiles);
     uint64_t nch = (n + C - 1) / C;
     WsLayout w;
-    w.counts = 0;
+    w.hist = 0;
+    w.lut = w.hist + 256 * 8;
+    w.dec = w.lut + 256;
+    w.counts = w.dec + 256;
     w.gsum = w.counts + align256(4 * ntiles);
     w.tpre = w.gsum + align256(4 * ngroups);
     w.chunk_pre = w.tpre + align256(4 * ntiles);
@@ -159,6 +165,8 @@ WsLayout ws_layout(uint64_t n, uint32_t C)
 // Per-launch constants of an encoder (kernel argument, by value).
 struct EncParams {
     uint8_t lut[256];      // code of e in bits 0..3, bit 7 set when e is an escape
+    const uint8_t *dlut;   // if not null: the code table in device memory (used instead of lut)
+    const uint8_t *ddec;   // if not null: dec[16] in device memory, for the stream header
     uint64_t n, nch, ntiles, ngroups;
     uint32_t Cmask, logC, gshift;
     uint64_t off_codes, off_offs, off_pos;
@@ -298,33 +306,94 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
 
 
 // =========================================================== histogram ====
-__global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n,
-                                                   unsigned long long *__restrict__ hist)
+// Exponent histogram of a sample of x: the first S words of every block of
+// B words (S = B: all of x). B and S are multiples of 8 with S <= B. Each
+// wave counts into kHistCopies copies of a 256-bin table in LDS, lane l into
+// copy l % kHistCopies: exponents of neighbouring values are mostly equal,
+// and lanes adding to one LDS word are served one after another. Copies are
+// 257 words apart, so bin e of different copies sits in different banks.
+// Each workgroup adds its counts to hist (one 64-bit atomic per non-empty
+// bin).
+constexpr int kHistCopies = 8;
+constexpr int kHistStride = 257;
+__global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n, uint64_t B,
+                                                   uint64_t S, unsigned long long *__restrict__ hist)
 {
-    __shared__ uint32_t sh[kThreads / 64][256];
-    const int tid = threadIdx.x, wave = tid >> 6;
-    for (int i = tid; i < (kThreads / 64) * 256; i += kThreads) (&sh[0][0])[i] = 0;
+    __shared__ uint32_t sh[kThreads / 64][kHistCopies * kHistStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < (kThreads / 64) * kHistCopies * kHistStride; i += kThreads) (&sh[0][0])[i] = 0;
     __syncthreads();
-    const uint64_t ngroups = n / 8;
+    uint32_t *mine = &sh[wave][(lane % kHistCopies) * kHistStride];
+    const uint64_t nblk = (n + B - 1) / B;
+    const uint64_t gps = S / 8;                              // 8-word groups per block sample
+    const uint64_t ngroups = nblk * gps;
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     for (uint64_t g = (uint64_t)blockIdx.x * kThreads + tid; g < ngroups; g += stride) {
-        const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + 8 * g));
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint64_t w0 = (g / gps) * B + (g % gps) * 8;  // first word of the group
+        if (w0 + 8 <= n) {
+            const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + w0));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            atomicAdd(&sh[wave][(w[q] >> 7) & 0xFFu], 1u);
-            atomicAdd(&sh[wave][(w[q] >> 23) & 0xFFu], 1u);
+            for (int q = 0; q < 4; q++) {
+                atomicAdd(&mine[(w[q] >> 7) & 0xFFu], 1u);
+                atomicAdd(&mine[(w[q] >> 23) & 0xFFu], 1u);
+            }
+        } else {
+            for (uint64_t i = w0; i < n; i++) atomicAdd(&mine[(x[i] >> 7) & 0xFFu], 1u);
         }
-    }
-    if (blockIdx.x == 0) {
-        for (uint64_t i = ngroups * 8 + tid; i < n; i += kThreads)
-            atomicAdd(&sh[wave][(x[i] >> 7) & 0xFFu], 1u);
     }
     __syncthreads();
     for (int b = tid; b < 256; b += kThreads) {
         uint32_t s = 0;
-        for (int q = 0; q < kThreads / 64; q++) s += sh[q][b];
+        for (int q = 0; q < kThreads / 64; q++)
+            for (int c = 0; c < kHistCopies; c++) s += sh[q][c * kHistStride + b];
         if (s) atomicAdd(&hist[b], (unsigned long long)s);
+    }
+}
+
+// Online calibration, step 1: zero the workspace histogram (a kernel, not a
+// memset, so that the call can be captured in a graph).
+__global__ void k_zero_hist(unsigned long long *__restrict__ hist)
+{
+    hist[threadIdx.x] = 0ull;
+}
+
+// Online calibration, step 3 (one workgroup of 256 threads, thread e for
+// exponent e): the Top-16 of the histogram under the total order (count
+// descending, exponent ascending) -- e's rank is the number of exponents
+// before it in that order -- and the tables built from it: lut[e] = code, or
+// 0x80 for an exponent outside the codebook, and dec[16]. If cb is not null
+// the whole codebook (the same fields as on the host) is written there too.
+__global__ __launch_bounds__(256) void k_top16(const unsigned long long *__restrict__ hist,
+                                               uint8_t *__restrict__ lut, uint8_t *__restrict__ dec,
+                                               uzip_codebook_t *__restrict__ cb)
+{
+    __shared__ unsigned long long h[256];
+    __shared__ unsigned long long part[4];
+    const uint32_t e = threadIdx.x;
+    const unsigned long long he = hist[e];
+    h[e] = he;
+    __syncthreads();
+    uint32_t rank = 0;
+    for (uint32_t q = 0; q < 256; q++) {
+        const unsigned long long hq = h[q];
+        rank += (hq > he || (hq == he && q < e)) ? 1u : 0u;
+    }
+    lut[e] = rank < 16 ? (uint8_t)rank : (uint8_t)0x80;
+    if (rank < 16) dec[rank] = (uint8_t)e;
+    if (cb) {
+        cb->enc[e] = rank < 16 ? (uint8_t)rank : (uint8_t)0;
+        cb->member[e] = rank < 16 ? (uint8_t)1 : (uint8_t)0;
+        cb->hist[e] = he;
+        if (rank < 16) cb->dec[rank] = (uint8_t)e;
+        unsigned long long t = he;
+        for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+        if ((e & 63) == 0) part[e >> 6] = t;
+        __syncthreads();
+        if (e == 0) {
+            cb->n_cal = part[0] + part[1] + part[2] + part[3];
+            cb->version = UZIP_VERSION;
+        }
     }
 }
 
@@ -527,7 +596,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
         }
     }
     // the code table goes to LDS after the data loads are in flight
-    load_wave_lut(sh, p.lut);
+    if (p.dlut) load_wave_lut(sh, p.dlut); else load_wave_lut(sh, p.lut);
     uint32_t cstart[kEncGroups];
     const uint32_t m = encode_dense_rank(xw, t0, rem, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
@@ -808,6 +877,7 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     if (lane == 7) w = (uint32_t)(M >> 32);
     if (lane == 8) w = (uint32_t)total;
     if (lane == 9) w = (uint32_t)(total >> 32);
+    if (p.ddec && lane >= 10 && lane < 14) w = reinterpret_cast<const uint32_t *>(p.ddec)[lane - 10];
     reinterpret_cast<uint32_t *>(out)[lane] = w;
     if (lane == 0) offs[p.nch] = (uint32_t)M;
     // zero padding after each section (each gap is under 256 bytes)
@@ -1341,6 +1411,8 @@ EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
     p.off_codes = L.off_codes;
     p.off_offs = L.off_offs;
     p.off_pos = L.off_pos;
+    p.dlut = nullptr;
+    p.ddec = nullptr;
     return p;
 }
 
@@ -1376,6 +1448,9 @@ EncWs make_ws(void *d_ws, uint64_t n, uint32_t C)
     const WsLayout w = ws_layout(n, C);
     uint8_t *b = static_cast<uint8_t *>(d_ws);
     EncWs ws;
+    ws.hist = reinterpret_cast<unsigned long long *>(b + w.hist);
+    ws.lut = b + w.lut;
+    ws.dec = b + w.dec;
     ws.counts = reinterpret_cast<uint32_t *>(b + w.counts);
     ws.gsum = reinterpret_cast<uint32_t *>(b + w.gsum);
     ws.tpre = reinterpret_cast<uint32_t *>(b + w.tpre);
@@ -1398,16 +1473,27 @@ struct Events {
 
 // Scan + placement shared by encode and reduce (kernels 2 and 3 of the call).
 int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &ep, const EncWs &ws,
-                  uint8_t *out, const Events &ev, hipStream_t s)
+                  uint8_t *out, const Events &ev, hipStream_t s, uint32_t ev0 = 2)
 {
     const HeaderParams hp = make_header_params(L, cb);
     k_group_sums<<<(unsigned)ep.ngroups, kThreads, 0, s>>>(ws, ep);
     UZIP_LAUNCH_CHECK("k_group_sums");
-    int rc = ev.record(2);
+    int rc = ev.record(ev0);
     if (rc) return rc;
     k_place_escapes<<<(unsigned)((ep.ntiles + kThreads / 64 - 1) / (kThreads / 64)), kThreads, 0, s>>>(ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
-    return ev.record(3);
+    return ev.record(ev0 + 1);
+}
+
+// Histogram launch: one 8-word group per thread and round, at most 2048
+// workgroups.
+void launch_hist(const uint16_t *d_x, uint64_t n, uint64_t block, uint64_t sample, uint64_t *d_hist,
+                 hipStream_t s)
+{
+    const uint64_t groups = ((n + block - 1) / block) * (sample / 8);
+    const uint64_t wgs = (groups + kThreads - 1) / kThreads;
+    const unsigned grid = (unsigned)(wgs < 2048 ? (wgs ? wgs : 1) : 2048);
+    k_hist<<<grid, kThreads, 0, s>>>(d_x, n, block, sample, reinterpret_cast<unsigned long long *>(d_hist));
 }
 
 // Host-side structural check (same rules as the header comment of
@@ -1431,6 +1517,22 @@ uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk)
 {
     if (!valid_nc(n, chunk)) return 0;
     return ws_layout(n, chunk).total;
+}
+
+int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb)
+{
+    if (!dec || !cb) return UZIP_EINVAL;
+    uzip_codebook_t c;
+    memset(&c, 0, sizeof c);
+    c.version = UZIP_VERSION;
+    for (int k = 0; k < 16; k++) {
+        if (c.member[dec[k]]) return UZIP_EINVAL;          // entries must be distinct
+        c.dec[k] = dec[k];
+        c.member[dec[k]] = 1;
+        c.enc[dec[k]] = (uint8_t)k;
+    }
+    *cb = c;
+    return UZIP_OK;
 }
 
 int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb)
@@ -1546,15 +1648,21 @@ const char *uzip_strerror(int code)
     }
 }
 
-int uzip_histogram(const uint16_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s)
+int uzip_histogram_sampled(const uint16_t *d_x, uint64_t n, uint64_t block, uint64_t sample, uint64_t *d_hist,
+                           hipStream_t s)
 {
     if (!d_x || !d_hist || !aligned16(d_x) || ((uintptr_t)d_hist & 7u)) return UZIP_EINVAL;
     if (n == 0 || n >= (1ull << 32)) return UZIP_EINVAL;
-    uint64_t groups = (n / 8 + kThreads - 1) / kThreads;
-    unsigned grid = (unsigned)(groups < 2048 ? (groups ? groups : 1) : 2048);
-    k_hist<<<grid, kThreads, 0, s>>>(d_x, n, reinterpret_cast<unsigned long long *>(d_hist));
+    if (block == 0) block = sample = (n + 7) & ~7ull;      // the whole of x
+    if (sample == 0 || sample > block || (block & 7) || (sample & 7)) return UZIP_EINVAL;
+    launch_hist(d_x, n, block, sample, d_hist, s);
     UZIP_LAUNCH_CHECK("k_hist");
     return UZIP_OK;
+}
+
+int uzip_histogram(const uint16_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s)
+{
+    return uzip_histogram_sampled(d_x, n, 0, 0, d_hist, s);
 }
 
 int uzip_calibrate(const uint16_t *d_x, uint64_t n, uint64_t *d_hist_ws, uzip_codebook_t *cb, hipStream_t s)
@@ -1590,6 +1698,46 @@ int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_c
     UZIP_LAUNCH_CHECK("k_encode_tile");
     if ((rc = ev.record(1))) return rc;
     return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_encode_online_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t block, uint64_t sample,
+                          uzip_codebook_t *d_cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                          const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (d_cb && ((uintptr_t)d_cb & 7u)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    if (block == 0) block = sample = (n + 7) & ~7ull;
+    if (sample == 0 || sample > block || (block & 7) || (sample & 7)) return UZIP_EINVAL;
+    if (out_cap < uzip_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk);
+    uzip_codebook_t none;                  // the tables come from the device
+    memset(&none, 0, sizeof none);
+    EncParams ep = make_enc_params(L, &none);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    ep.dlut = ws.lut;
+    ep.ddec = ws.dec;
+    const Events ev{opts, s};
+    int rc;
+    if ((rc = ev.record(0))) return rc;
+    k_zero_hist<<<1, 256, 0, s>>>(ws.hist);
+    UZIP_LAUNCH_CHECK("k_zero_hist");
+    launch_hist(d_x, n, block, sample, reinterpret_cast<uint64_t *>(ws.hist), s);
+    UZIP_LAUNCH_CHECK("k_hist");
+    k_top16<<<1, 256, 0, s>>>(ws.hist, ws.lut, ws.dec, d_cb);
+    UZIP_LAUNCH_CHECK("k_top16");
+    if ((rc = ev.record(1))) return rc;
+    k_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("k_encode_tile");
+    if ((rc = ev.record(2))) return rc;
+    return finish_encode(L, &none, ep, ws, static_cast<uint8_t *>(d_out), ev, s, 3);
+}
+
+int uzip_encode_online(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t block, uint64_t sample,
+                       uzip_codebook_t *d_cb, void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       hipStream_t s)
+{
+    return uzip_encode_online_ex(d_x, n, chunk, block, sample, d_cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
 }
 
 int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,

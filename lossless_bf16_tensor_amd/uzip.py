@@ -22,10 +22,11 @@ ERRORS = {0: "UZIP_OK", -1: "UZIP_EINVAL", -2: "UZIP_ENOSPC", -3: "UZIP_ECORRUPT
 
 # every symbol include/uzip.h declares
 EXPORTS = (
-    "uzip_max_bytes", "uzip_workspace_bytes", "uzip_codebook_from_hist", "uzip_validate_host",
-    "uzip_parse_header", "uzip_strerror", "uzip_histogram", "uzip_calibrate", "uzip_encode",
-    "uzip_encode_ex", "uzip_stream_bytes", "uzip_decode", "uzip_decode_ex", "uzip_reduce_add",
-    "uzip_reduce_add_ex", "uzip_reduce_k", "uzip_reduce_k_ex", "uzip_validate",
+    "uzip_max_bytes", "uzip_workspace_bytes", "uzip_codebook_from_hist", "uzip_codebook_from_dec",
+    "uzip_validate_host", "uzip_parse_header", "uzip_strerror", "uzip_histogram", "uzip_histogram_sampled",
+    "uzip_calibrate", "uzip_encode", "uzip_encode_ex", "uzip_encode_online", "uzip_encode_online_ex",
+    "uzip_stream_bytes", "uzip_decode", "uzip_decode_ex", "uzip_reduce_add", "uzip_reduce_add_ex",
+    "uzip_reduce_k", "uzip_reduce_k_ex", "uzip_validate",
 )
 
 MAX_K = 16                      # UZIP_MAX_K
@@ -72,13 +73,17 @@ def lib():
         "uzip_max_bytes": (u64, [u64, u32]),
         "uzip_workspace_bytes": (u64, [u64, u32]),
         "uzip_codebook_from_hist": (i32, [vp, cbp]),
+        "uzip_codebook_from_dec": (i32, [vp, cbp]),
         "uzip_validate_host": (i32, [vp, u64, cbp]),
         "uzip_parse_header": (i32, [vp, vp, vp, vp, vp, vp]),
         "uzip_strerror": (ctypes.c_char_p, [i32]),
         "uzip_histogram": (i32, [vp, u64, vp, vp]),
+        "uzip_histogram_sampled": (i32, [vp, u64, u64, u64, vp, vp]),
         "uzip_calibrate": (i32, [vp, u64, vp, cbp, vp]),
         "uzip_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
         "uzip_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_encode_online": (i32, [vp, u64, u32, u64, u64, vp, vp, u64, vp, u64, vp]),
+        "uzip_encode_online_ex": (i32, [vp, u64, u32, u64, u64, vp, vp, u64, vp, u64, op, vp]),
         "uzip_stream_bytes": (i32, [vp, vp, vp, vp]),
         "uzip_decode": (i32, [vp, u64, u64, u32, cbp, vp, vp]),
         "uzip_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
@@ -155,6 +160,14 @@ def codebook_from_hist(hist) -> Codebook:
     return cb
 
 
+def codebook_from_dec(dec) -> Codebook:
+    """The codebook with decode table dec[16] (hist and n_cal zero)."""
+    d = (ctypes.c_uint8 * 16)(*[int(v) for v in dec])
+    cb = Codebook()
+    _check(lib().uzip_codebook_from_dec(ctypes.cast(d, ctypes.c_void_p), ctypes.byref(cb)), "codebook_from_dec")
+    return cb
+
+
 def validate_host(buf: bytes, cb: Codebook) -> int:
     """Structural check of a host copy of a stream; returns the C status code."""
     b = bytes(buf)
@@ -173,12 +186,19 @@ def parse_header(buf: bytes):
 
 
 # ---------------------------------------------------------------- device ----
-def histogram(x: torch.Tensor, hist: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Add the exponent histogram of x to hist (int64[256] on the device)."""
+def histogram(x: torch.Tensor, hist: torch.Tensor | None = None, block: int = 0, sample: int = 0,
+              stream=None) -> torch.Tensor:
+    """Add the exponent histogram of x to hist (int64[256] on the device).
+    With block > 0, only the first `sample` words of every `block` words
+    are counted."""
     w = _words(x)
     if hist is None:
         hist = torch.zeros(256, dtype=torch.int64, device=w.device)
-    _check(lib().uzip_histogram(_ptr(w), w.numel(), _ptr(hist), _stream(stream)), "histogram")
+    if block:
+        _check(lib().uzip_histogram_sampled(_ptr(w), w.numel(), block, sample, _ptr(hist), _stream(stream)),
+               "histogram_sampled")
+    else:
+        _check(lib().uzip_histogram(_ptr(w), w.numel(), _ptr(hist), _stream(stream)), "histogram")
     return hist
 
 
@@ -209,6 +229,35 @@ def encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor |
                                 _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
            "encode")
     return out
+
+
+def encode_online(x: torch.Tensor, chunk: int = 1024, block: int = 0, sample: int = 0,
+                  out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  cb_out: torch.Tensor | None = None, events=None, stream=None) -> torch.Tensor:
+    """Encode with a codebook calibrated on x on the device (block = 0: the
+    whole of x; else the first `sample` words of every `block` words).
+    cb_out, if given, is a uint8 device tensor of ctypes.sizeof(Codebook)
+    bytes that receives the codebook."""
+    w = _words(x)
+    n = w.numel()
+    if out is None:
+        out = torch.empty(max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+    if cb_out is not None and cb_out.numel() < ctypes.sizeof(Codebook):
+        raise ValueError("cb_out is smaller than a codebook")
+    o = _opts(events)
+    _check(lib().uzip_encode_online_ex(_ptr(w), n, chunk, block, sample,
+                                       _ptr(cb_out) if cb_out is not None else None, _ptr(out), out.numel(),
+                                       _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
+           "encode_online")
+    return out
+
+
+def codebook_of_device(cb_out: torch.Tensor) -> Codebook:
+    """Host copy of a codebook that encode_online wrote to a device buffer."""
+    b = bytes(cb_out[:ctypes.sizeof(Codebook)].cpu().numpy().tobytes())
+    return Codebook.from_buffer_copy(b)
 
 
 def stream_bytes(buf: torch.Tensor, stream=None):

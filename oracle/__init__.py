@@ -197,6 +197,18 @@ def reduce_add(sa, sb, n: int, chunk: int, dec) -> np.ndarray:
     return out[:total].copy()
 
 
+def sample_words(x, block: int, sample: int) -> np.ndarray:
+    """The calibration sample of x: the first `sample` words of every block
+    of `block` words, the last block possibly partial ("CCCL", section 4.3,
+    localized frequency tables: a table from the first part of each block's
+    range). block = 0 means all of x."""
+    x = _u16(x).reshape(-1)
+    if block == 0:
+        return x.copy()
+    parts = [x[b:b + sample] for b in range(0, x.size, block)]
+    return np.concatenate(parts) if parts else x[:0].copy()
+
+
 def reduce_k(streams, n: int, chunk: int, dec) -> np.ndarray:
     """k-input reduce of compressed streams (same n, chunk and codebook)."""
     arrs = [np.ascontiguousarray(x, dtype=np.uint8) for x in streams]

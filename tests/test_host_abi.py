@@ -80,6 +80,18 @@ def _stream():
     return oracle.encode(w.x, 1024, ocb.dec), cb, ocb
 
 
+def test_codebook_from_dec_matches_from_hist():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        hist = rng.integers(0, 1000, 256).astype(np.uint64)
+        a = uzip.codebook_from_hist(hist)
+        b = uzip.codebook_from_dec(list(a.dec))
+        assert list(b.dec) == list(a.dec) and list(b.enc) == list(a.enc) and list(b.member) == list(a.member)
+        assert b.version == a.version and b.n_cal == 0
+    with pytest.raises(uzip.UzipError):
+        uzip.codebook_from_dec([1] * 16)
+
+
 def test_parse_header():
     s, cb, ocb = _stream()
     h = uzip.parse_header(s.tobytes())
@@ -149,6 +161,12 @@ def test_device_calls_reject_bad_args_without_gpu():
     sizes[3] = big
     ptrs[2] = mis
     assert L.uzip_reduce_k(ptrs, sizes, 4, 1000, 1024, cbr, p, big, p, ws, None) == -1
+    assert L.uzip_encode_online(p, 1000, 1024, 64, 72, None, p, big, p, ws, None) == -1    # sample > block
+    assert L.uzip_encode_online(p, 1000, 1024, 64, 12, None, p, big, p, ws, None) == -1    # not a multiple of 8
+    assert L.uzip_encode_online(p, 1000, 1024, 0, 0, mis, p, big, p, ws, None) == -1       # misaligned codebook
+    assert L.uzip_encode_online(p, 1000, 1024, 0, 0, None, p, big, p, ws - 1, None) == -2
+    assert L.uzip_histogram_sampled(p, 1000, 16, 24, p, None) == -1
+    assert L.uzip_histogram_sampled(p, 1000, 16, 0, p, None) == -1
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1
