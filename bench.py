@@ -240,6 +240,7 @@ def main():
     ap.add_argument("--no-oracle-check", action="store_true")
     ap.add_argument("--no-reduce", action="store_true")
     ap.add_argument("--no-reduce-k", action="store_true")
+    ap.add_argument("--no-online", action="store_true")
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
@@ -405,6 +406,31 @@ def main():
                   "GBps_uncompressed_in": round(2 * 2 * n / (t_red * 1e-3) / 1e9, 1),
                   "inputs": "the workload and the same tensor with its K and V halves swapped"}
 
+    # --- online calibration: codebook built on the device from the input
+    # itself (whole input, or 256 KiB of every 2 MiB), then the encode ---
+    online = None
+    if not args.no_online:
+        online = {}
+        for label, blk, smp in (("whole_input", 0, 0), ("sample_256KiB_per_2MiB", 1 << 20, 1 << 17)):
+            for _ in range(2):
+                uzip.encode_online(x, C, blk, smp, out=out, ws=ws)
+            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+            for row in oev:
+                for e in row:
+                    e.record()
+            for k in range(10):
+                flush()
+                uzip.encode_online(x, C, blk, smp, out=out, ws=ws, events=oev[k])
+            torch.cuda.synchronize()
+            t_on = float(np.mean([oev[k][0].elapsed_time(oev[k][4]) for k in range(10)]))
+            t_oncal = float(np.mean([oev[k][0].elapsed_time(oev[k][1]) for k in range(10)]))
+            tot_on, m_on = uzip.stream_bytes(out)
+            online[label] = {"ms": round(t_on, 4), "calibration_ms": round(t_oncal, 4),
+                             "GBps": round(2 * n / (t_on * 1e-3) / 1e9, 1),
+                             "slowdown_vs_offline_encode": round(t_on / t_enc, 3),
+                             "escape_rate": round(m_on / n, 6), "ratio_total": round(2 * n / tot_on, 4)}
+        uzip.encode(x, cb, C, out=out, ws=ws)      # leave the offline stream in place
+
     # --- k-input fused reduce: one GPU's share of a two-shot all-reduce over
     # 8 GPUs (8 shards of 2^26 values, gradient recipe) ---
     reduce_k = None
@@ -477,6 +503,7 @@ def main():
         "round_trip_bit_exact": round_trip, "oracle_stream_equal": parity,
         "reduce": reduce,
         "reduce_k": reduce_k,
+        "online_calibration": online,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

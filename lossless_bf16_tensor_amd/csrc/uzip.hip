@@ -316,6 +316,7 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
 // bin).
 constexpr int kHistCopies = 8;
 constexpr int kHistStride = 257;
+constexpr int kHistUnroll = 4;
 __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n, uint64_t B,
                                                    uint64_t S, unsigned long long *__restrict__ hist)
 {
@@ -324,22 +325,36 @@ __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ 
     for (int i = tid; i < (kThreads / 64) * kHistCopies * kHistStride; i += kThreads) (&sh[0][0])[i] = 0;
     __syncthreads();
     uint32_t *mine = &sh[wave][(lane % kHistCopies) * kHistStride];
-    const uint64_t nblk = (n + B - 1) / B;
-    const uint64_t gps = S / 8;                              // 8-word groups per block sample
-    const uint64_t ngroups = nblk * gps;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + tid; g < ngroups; g += stride) {
-        const uint64_t w0 = (g / gps) * B + (g % gps) * 8;  // first word of the group
-        if (w0 + 8 <= n) {
-            const u32x4 v = ld_stream(reinterpret_cast<const u32x4 *>(x + w0));
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // 8-word groups, numbered block by block (n < 2^32, so 32 bits hold them);
+    // kHistUnroll groups per thread and round, all loads issued first
+    const uint32_t nblk = (uint32_t)((n + B - 1) / B);
+    const uint32_t gps = (uint32_t)(S / 8);                  // groups per block sample
+    const uint32_t ngroups = nblk * gps;
+    const uint32_t stride = gridDim.x * kThreads * kHistUnroll;
+    for (uint32_t g0 = blockIdx.x * kThreads * kHistUnroll + tid; g0 < ngroups; g0 += stride) {
+        u32x4 v[kHistUnroll];
+        uint64_t w0[kHistUnroll];
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                atomicAdd(&mine[(w[q] >> 7) & 0xFFu], 1u);
-                atomicAdd(&mine[(w[q] >> 23) & 0xFFu], 1u);
+        for (int u = 0; u < kHistUnroll; u++) {
+            const uint32_t g = g0 + u * kThreads;
+            w0[u] = (uint64_t)(g / gps) * B + (uint64_t)(g % gps) * 8;   // first word of the group
+            v[u] = u32x4{0u, 0u, 0u, 0u};
+            if (g < ngroups && w0[u] + 8 <= n) v[u] = ld_stream(reinterpret_cast<const u32x4 *>(x + w0[u]));
+        }
+#pragma unroll
+        for (int u = 0; u < kHistUnroll; u++) {
+            const uint32_t g = g0 + u * kThreads;
+            if (g >= ngroups) continue;
+            if (w0[u] + 8 <= n) {
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    atomicAdd(&mine[(w[q] >> 7) & 0xFFu], 1u);
+                    atomicAdd(&mine[(w[q] >> 23) & 0xFFu], 1u);
+                }
+            } else {
+                for (uint64_t i = w0[u]; i < n; i++) atomicAdd(&mine[(x[i] >> 7) & 0xFFu], 1u);
             }
-        } else {
-            for (uint64_t i = w0; i < n; i++) atomicAdd(&mine[(x[i] >> 7) & 0xFFu], 1u);
         }
     }
     __syncthreads();
@@ -1490,8 +1505,12 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
 void launch_hist(const uint16_t *d_x, uint64_t n, uint64_t block, uint64_t sample, uint64_t *d_hist,
                  hipStream_t s)
 {
+    // a block longer than x is x: keeps the kernel's group numbers in 32 bits
+    const uint64_t n8 = (n + 7) & ~7ull;
+    if (block > n8) block = n8;
+    if (sample > block) sample = block;
     const uint64_t groups = ((n + block - 1) / block) * (sample / 8);
-    const uint64_t wgs = (groups + kThreads - 1) / kThreads;
+    const uint64_t wgs = (groups + kThreads * kHistUnroll - 1) / (kThreads * kHistUnroll);
     const unsigned grid = (unsigned)(wgs < 2048 ? (wgs ? wgs : 1) : 2048);
     k_hist<<<grid, kThreads, 0, s>>>(d_x, n, block, sample, reinterpret_cast<unsigned long long *>(d_hist));
 }
