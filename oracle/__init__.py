@@ -73,6 +73,15 @@ def _load():
         "orc_bf16_rne_array": (None, [ctypes.POINTER(ctypes.c_uint32), c64, u16p]),
         "orc_add_bf16_array": (None, [u16p, u16p, c64, u16p]),
         "orc_sum_bf16": (ctypes.c_uint16, [u16p, c32, c64]),
+        "orc8_exponent": (ctypes.c_uint8, [ctypes.c_uint8]),
+        "orc8_signmant": (ctypes.c_uint8, [ctypes.c_uint8]),
+        "orc8_merge": (ctypes.c_uint8, [ctypes.c_uint8, ctypes.c_uint8]),
+        "orc8_histogram": (None, [u8p, c64, u64p]),
+        "orc8_max_bytes": (c64, [c64, c32]),
+        "orc8_payload_bytes": (c64, [c64, c64]),
+        "orc8_encode": (c64, [u8p, c64, c32, u8p, u8p, c64]),
+        "orc8_decode": (ctypes.c_int, [u8p, c64, c64, c32, u8p, u8p]),
+        "orc8_validate": (ctypes.c_int, [u8p, c64, u8p]),
         "orc_reduce_k": (c64, [ctypes.POINTER(u8p), u64p, c32, c64, c32, u8p, u8p, c64, u16p]),
         "orc_sum_bf16_array": (None, [u16p, c32, c64, u16p]),
     }
@@ -287,3 +296,70 @@ def sections(stream) -> dict:
         "pos": s[pos:pos + 2 * m].view(np.uint16), "val": s[val:val + m],
         "dec": s[40:56].copy(), "total": int(s[32:40].view(np.uint64)[0]),
     }
+
+
+# ----------------------------------------------------------- FP8 E5M2 ----
+def _u8(x):
+    return np.ascontiguousarray(x, dtype=np.uint8)
+
+
+def fp8_exponent(x: int) -> int:
+    return int(_load().orc8_exponent(x))
+
+
+def fp8_signmant(x: int) -> int:
+    return int(_load().orc8_signmant(x))
+
+
+def fp8_merge(a: int, e: int) -> int:
+    return int(_load().orc8_merge(a, e))
+
+
+def fp8_histogram(*sets) -> np.ndarray:
+    """Pooled 256-bin histogram of the 5-bit exponents of E5M2 values."""
+    hist = np.zeros(256, dtype=np.uint64)
+    for x in sets:
+        x = _u8(x).reshape(-1)
+        _load().orc8_histogram(_p(x, ctypes.c_uint8), x.size, _p(hist, ctypes.c_uint64))
+    return hist
+
+
+def fp8_calibrate(*sets) -> Codebook:
+    return top16(fp8_histogram(*sets))
+
+
+def fp8_max_bytes(n: int, chunk: int) -> int:
+    return int(_load().orc8_max_bytes(n, chunk))
+
+
+def fp8_payload_bytes(n: int, m: int) -> int:
+    return int(_load().orc8_payload_bytes(n, m))
+
+
+def fp8_encode(x, chunk: int, dec) -> np.ndarray:
+    x = _u8(x).reshape(-1)
+    dec = _u8(dec)
+    cap = fp8_max_bytes(x.size, chunk)
+    out = np.empty(cap, dtype=np.uint8)
+    total = _load().orc8_encode(_p(x, ctypes.c_uint8), x.size, chunk, _p(dec, ctypes.c_uint8),
+                                _p(out, ctypes.c_uint8), cap)
+    if total == 0:
+        raise ValueError("oracle fp8 encode failed")
+    return out[:total].copy()
+
+
+def fp8_decode(stream, n: int, chunk: int, dec) -> np.ndarray:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    y = np.empty(n, dtype=np.uint8)
+    rc = _load().orc8_decode(_p(stream, ctypes.c_uint8), stream.size, n, chunk, _p(dec, ctypes.c_uint8),
+                             _p(y, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle fp8 decode failed")
+    return y
+
+
+def fp8_validate(stream, dec) -> int:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    return int(_load().orc8_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))

@@ -45,10 +45,15 @@ MUTANTS = {
                            "    for (uint32_t i = k - 1; i-- > 0;) s = s + orc_bf16_to_f32(v[(uint64_t)i * stride]);"),
     "sum_in_binary64": ("volatile float s = orc_bf16_to_f32(v[0]);", "volatile double s = orc_bf16_to_f32(v[0]);"),
     "sum_skips_first_input": ("for (uint32_t i = 1; i < k; i++) s = s +", "for (uint32_t i = 2; i < k; i++) s = s +"),
+    "fp8_sign_shift": ("(uint8_t)(((x >> 5) & 0x4u) | (x & 0x3u))", "(uint8_t)(((x >> 4) & 0x4u) | (x & 0x3u))"),
+    "fp8_exponent_width": ("(uint8_t)((x >> 2) & 0x1fu)", "(uint8_t)((x >> 2) & 0x0fu)"),
+    "fp8_msb_first_bits": ("sec[b / 8] |= (uint8_t)(1u << (b % 8));", "sec[b / 8] |= (uint8_t)(0x80u >> (b % 8));"),
+    "fp8_sm_section_length": ("static uint64_t orc8_sm_bytes(uint64_t n) { return (3 * n + 7) / 8; }",
+                              "static uint64_t orc8_sm_bytes(uint64_t n) { return (3 * n) / 8 + 1; }"),
 }
 
 PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py",
-             "tests/test_oracle_reduce_k.py"]
+             "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py"]
 
 
 def _run(name, a, b, tmp):

@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "bf16_bits", "config_1", "config_2", "config_3", "config_4",
-    "config_5", "config", "reduce_shards", "all_patterns", "random_words", "CONFIG_NAMES",
+    "config_5", "config", "reduce_shards", "kv_cache_e5m2", "e5m2_bits", "all_patterns", "random_words", "CONFIG_NAMES",
 ]
 
 CONFIG_NAMES = {
@@ -59,6 +59,19 @@ def bf16_bits(f) -> np.ndarray:
     for s in range(0, f32.size, step):
         t = torch.from_numpy(f32[s:s + step]).to(torch.bfloat16)
         out[s:s + step] = t.view(torch.int16).numpy().view(np.uint16)
+    return out
+
+
+def e5m2_bits(f) -> np.ndarray:
+    """float64/float32 array -> uint8 FP8 E5M2 bit patterns (torch CPU cast,
+    round to nearest even)."""
+    import torch
+    f32 = np.ascontiguousarray(np.asarray(f, dtype=np.float32)).reshape(-1)
+    out = np.empty(f32.size, dtype=np.uint8)
+    step = 1 << 24
+    for s in range(0, f32.size, step):
+        t = torch.from_numpy(f32[s:s + step]).to(torch.float8_e5m2)
+        out[s:s + step] = t.view(torch.uint8).numpy()
     return out
 
 
@@ -98,21 +111,24 @@ def config_2(tokens: int = 16384, seed: int = 2, calib_tokens: int = 1024) -> Wo
                     f"seed {seed}; {n_out} outlier tokens x64; calib first {calib_tokens} tokens")
 
 
-def _kv_cache(seed: int, layers: int, tokens: int, only_layer0: bool = False):
-    """KV cache [2, layers, tokens, 8, 128] drawn block by block.
+def _kv_cache(seed: int, layers: int, tokens: int, only_layer0: bool = False, cast=None):
+    """KV cache [2, layers, tokens, 8, 128] drawn block by block, cast to BF16
+    (or by `cast`, e.g. e5m2_bits).
 
     Draw order: per-layer scale, per-channel scale, K bias, then for kv in
     (K, V) and each layer a [tokens, 8, 128] block of N(0,1).
     """
+    cast = cast or bf16_bits
+    dt = np.uint8 if cast is e5m2_bits else np.uint16
     rng = np.random.default_rng(seed)
     sl = np.exp(rng.uniform(math.log(0.05), math.log(20.0), layers))
     ch = np.exp(0.8 * rng.standard_normal((2, layers, 8, 128)))
     b = rng.standard_normal((layers, 8, 128))
     blk = tokens * 8 * 128
     if only_layer0:
-        out = np.empty(2 * blk, dtype=np.uint16)
+        out = np.empty(2 * blk, dtype=dt)
     else:
-        out = np.empty(2 * layers * blk, dtype=np.uint16)
+        out = np.empty(2 * layers * blk, dtype=dt)
     for kv in (0, 1):
         for l in range(layers):
             z = rng.standard_normal((tokens, 8, 128))
@@ -121,10 +137,10 @@ def _kv_cache(seed: int, layers: int, tokens: int, only_layer0: bool = False):
             block = z * sl[l] * ch[kv, l]
             if only_layer0:
                 if l == 0:
-                    out[kv * blk:(kv + 1) * blk] = bf16_bits(block)
+                    out[kv * blk:(kv + 1) * blk] = cast(block)
             else:
                 o = (kv * layers + l) * blk
-                out[o:o + blk] = bf16_bits(block)
+                out[o:o + blk] = cast(block)
     return out
 
 
@@ -141,6 +157,15 @@ def config_3(tokens: int = 2048, layers: int = 64, seed: int = 3,
     cal = _kv_cache(calib_seed, layers, tokens, only_layer0=True)
     return Workload(CONFIG_NAMES[3], x, cal, (1024,), (2, layers, tokens, 8, 128),
                     f"seed {seed}; calib layer 0 of seed {calib_seed}")
+
+
+def kv_cache_e5m2(tokens: int = 2048, layers: int = 64, seed: int = 3, calib_seed: int = 103) -> Workload:
+    """Config 3's KV cache recipe cast to FP8 E5M2 (one byte per value), the
+    FP8 variant's workload; the codebook again from layer 0 of another seed."""
+    x = _kv_cache(seed, layers, tokens, cast=e5m2_bits)
+    cal = _kv_cache(calib_seed, layers, tokens, only_layer0=True, cast=e5m2_bits)
+    return Workload(f"kv-cache-e5m2-2x{layers}x{tokens}x8x128", x, cal, (1024,), (2, layers, tokens, 8, 128),
+                    f"seed {seed}; calib layer 0 of seed {calib_seed}; FP8 E5M2")
 
 
 def config_4(n: int = 1 << 26, seed: int = 4, block: int = 4096,
