@@ -241,6 +241,7 @@ def main():
     ap.add_argument("--no-reduce", action="store_true")
     ap.add_argument("--no-reduce-k", action="store_true")
     ap.add_argument("--no-online", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
@@ -431,6 +432,46 @@ def main():
                              "escape_rate": round(m_on / n, 6), "ratio_total": round(2 * n / tot_on, 4)}
         uzip.encode(x, cb, C, out=out, ws=ws)      # leave the offline stream in place
 
+    # --- FP8 E5M2 variant on the same KV-cache recipe cast to E5M2 (2^28 bytes) ---
+    fp8 = None
+    if not args.no_fp8:
+        log("fp8: generating the E5M2 KV cache")
+        w8 = workloads.kv_cache_e5m2()
+        x8 = torch.from_numpy(w8.x).to(dev)
+        cb8 = uzip.fp8_calibrate(torch.from_numpy(w8.calib).to(dev))
+        out8 = torch.empty(uzip.fp8_max_bytes(n, C), dtype=torch.uint8, device=dev)
+        y8 = torch.empty_like(x8)
+        uzip.fp8_encode(x8, cb8, C, out=out8, ws=ws)
+        tot8, m8 = uzip.stream_bytes(out8)
+        uzip.fp8_decode(out8, cb8, n, C, out=y8, in_bytes=tot8)
+        torch.cuda.synchronize()
+        if not torch.equal(y8, x8):
+            log("CORRECTNESS FAILURE fp8 round trip")
+            sys.exit(1)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(10)]
+        for row in fev:
+            for e in row:
+                e.record()
+        for k in range(10):
+            flush()
+            uzip.fp8_encode(x8, cb8, C, out=out8, ws=ws, events=fev[k][:4])
+            flush()
+            uzip.fp8_decode(out8, cb8, n, C, out=y8, in_bytes=tot8, events=fev[k][4:])
+        torch.cuda.synchronize()
+        te8 = float(np.mean([fev[k][0].elapsed_time(fev[k][3]) for k in range(10)]))
+        td8 = float(np.mean([fev[k][4].elapsed_time(fev[k][5]) for k in range(10)]))
+        nch = (n + C - 1) // C
+        alg8 = n + (3 * n + 7) // 8 + (n + 1) // 2 + 3 * m8 + 4 * (nch + 1) + 256
+        fp8 = {"workload": w8.name, "n": n, "escape_rate": round(m8 / n, 6),
+               "ratio_payload": round(n / ((3 * n + 7) // 8 + (n + 1) // 2 + 3 * m8), 4),
+               "ratio_total": round(n / tot8, 4),
+               "encode_ms": round(te8, 4), "decode_ms": round(td8, 4),
+               "encode_GBps": round(n / (te8 * 1e-3) / 1e9, 1), "decode_GBps": round(n / (td8 * 1e-3) / 1e9, 1),
+               "op_roofline_frac": {"encode": round(alg8 / (te8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                    "decode": round(alg8 / (td8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+               "k8_encode_tile_ms": round(float(np.mean([fev[k][0].elapsed_time(fev[k][1]) for k in range(10)])), 4)}
+        del x8, y8, out8
+
     # --- k-input fused reduce: one GPU's share of a two-shot all-reduce over
     # 8 GPUs (8 shards of 2^26 values, gradient recipe) ---
     reduce_k = None
@@ -504,6 +545,7 @@ def main():
         "reduce": reduce,
         "reduce_k": reduce_k,
         "online_calibration": online,
+        "fp8_e5m2": fp8,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

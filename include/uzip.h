@@ -120,7 +120,8 @@ int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
  * Returns UZIP_OK, or UZIP_EINVAL (NULL, or entries not distinct). */
 int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
 
-/* Full structural check of a stream held in host memory: header fields,
+/* Full structural check of a stream held in host memory (BF16 or, with
+ * header flags 1, FP8 E5M2): header fields,
  * section sizes, zero padding, offsets monotone and ending at M, positions
  * ascending and inside their chunk, every escape value outside the codebook
  * with code 0 in the dense stream. Returns UZIP_OK, UZIP_ECORRUPT,
@@ -169,6 +170,46 @@ int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_code
 int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
                    const uzip_opts_t *opts, hipStream_t s);
+
+/* ------------------------------------------------ FP8 E5M2 variant ---- */
+/* "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+ * Serving", section 4.2 / appendix C: FP8 E5M2 values (1 sign, 5 exponent,
+ * 2 mantissa bits; one byte each) in the same framework. The 5-bit exponent
+ * e = (x >> 2) & 0x1f takes a 4-bit Top-16 code, two per byte as above; the
+ * other three bits a = ((x >> 5) & 4) | (x & 3) are packed 3 bits per value
+ * (value i at bits 3i..3i+2 of the section, least significant bit first:
+ * every 8 values fill 3 bytes; unused bits 0); escapes are the BF16 ones
+ * (u16 in-chunk position + u8 raw exponent). Stream: the BF16 container with
+ * header flags (offset 6) = 1 and a sign-mantissa section of ceil(3n/8)
+ * bytes. Payload ceil(3n/8) + ceil(n/2) + 3M bytes: 8/7 with no escape.
+ * Codebooks are built from an FP8 exponent histogram; every entry of dec
+ * must be below 32 (else UZIP_EINVAL). The workspace is uzip_workspace_bytes. */
+
+/* Largest E5M2 stream for n values at chunk C (M = n); 0 if n or C is invalid. */
+uint64_t uzip_fp8_max_bytes(uint64_t n, uint32_t chunk);
+
+/* async. Adds the 5-bit exponent histogram of d_x[0..n) (bytes, 16-byte
+ * aligned) to d_hist[256], as uzip_histogram does for BF16. */
+int uzip_fp8_histogram(const uint8_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s);
+
+/* blocking. As uzip_calibrate, on E5M2 values. */
+int uzip_fp8_calibrate(const uint8_t *d_x, uint64_t n, uint64_t *d_hist_ws, uzip_codebook_t *cb,
+                       hipStream_t s);
+
+/* async. Encodes n E5M2 values; arguments, ownership and errors as for
+ * uzip_encode (out_cap >= uzip_fp8_max_bytes). */
+int uzip_fp8_encode(const uint8_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s);
+int uzip_fp8_encode_ex(const uint8_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s);
+
+/* async. Decodes an E5M2 stream of n values into d_y[0..n) (16-byte
+ * aligned); bounds and errors as for uzip_decode (fused patch only). */
+int uzip_fp8_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                    const uzip_codebook_t *cb, uint8_t *d_y, hipStream_t s);
+int uzip_fp8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                       const uzip_codebook_t *cb, uint8_t *d_y, const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Reads a device stream's header. Returns its size and M.
  * Either output pointer may be NULL. */

@@ -55,21 +55,26 @@ __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~
 struct Layout {
     uint64_t n, nch;
     uint32_t C, logC;
+    bool fp8;                                // E5M2 variant: 3-bit sign-mantissa fields
     uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader
 };
 
 __host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m) { return L.off_pos + align256(2 * m); }
 __host__ __device__ inline uint64_t total_of(const Layout &L, uint64_t m) { return off_val_of(L, m) + m; }
 
-Layout make_layout(uint64_t n, uint32_t C)
+// fp8: the E5M2 variant, whose sign-mantissa section holds 3 bits per value.
+__host__ __device__ inline uint64_t sm_bytes_of(uint64_t n, bool fp8) { return fp8 ? (3 * n + 7) / 8 : n; }
+
+Layout make_layout(uint64_t n, uint32_t C, bool fp8 = false)
 {
     Layout L;
     L.n = n;
     L.C = C;
+    L.fp8 = fp8;
     L.logC = 0;
     while ((1u << L.logC) < C) L.logC++;
     L.nch = (n + C - 1) / C;
-    L.off_codes = kHeader + align256(n);
+    L.off_codes = kHeader + align256(sm_bytes_of(n, fp8));
     L.off_offs = L.off_codes + align256((n + 1) / 2);
     L.off_pos = L.off_offs + align256(4 * (L.nch + 1));
     return L;
@@ -167,6 +172,7 @@ struct EncParams {
     uint8_t lut[256];      // code of e in bits 0..3, bit 7 set when e is an escape
     const uint8_t *dlut;   // if not null: the code table in device memory (used instead of lut)
     const uint8_t *ddec;   // if not null: dec[16] in device memory, for the stream header
+    uint64_t sm_bytes;     // length of the sign-mantissa section
     uint64_t n, nch, ntiles, ngroups;
     uint32_t Cmask, logC, gshift;
     uint64_t off_codes, off_offs, off_pos;
@@ -306,29 +312,38 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
 
 
 // =========================================================== histogram ====
-// Exponent histogram of a sample of x: the first S words of every block of
-// B words (S = B: all of x). B and S are multiples of 8 with S <= B. Each
-// wave counts into kHistCopies copies of a 256-bin table in LDS, lane l into
-// copy l % kHistCopies: exponents of neighbouring values are mostly equal,
-// and lanes adding to one LDS word are served one after another. Copies are
-// 257 words apart, so bin e of different copies sits in different banks.
-// Each workgroup adds its counts to hist (one 64-bit atomic per non-empty
-// bin).
+// Exponent histogram of a sample of x: the first S values of every block of
+// B values (S = B: all of x). EB is the element width: 2 for BF16 (exponent
+// bits 7..14), 1 for FP8 E5M2 (bits 2..6). B and S are multiples of the
+// values per 16 bytes (VG = 16 / EB) with S <= B. Each wave counts into
+// kHistCopies copies of a 256-bin table in LDS, lane l into copy
+// l % kHistCopies: exponents of neighbouring values are mostly equal, and
+// lanes adding to one LDS word are served one after another. Copies are 257
+// words apart, so bin e of different copies sits in different banks. Each
+// workgroup adds its counts to hist (one 64-bit atomic per non-empty bin).
 constexpr int kHistCopies = 8;
 constexpr int kHistStride = 257;
 constexpr int kHistUnroll = 4;
-__global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ x, uint64_t n, uint64_t B,
+template <int EB>
+__device__ __forceinline__ uint32_t hist_exponent(uint32_t v)
+{
+    return EB == 2 ? (v >> 7) & 0xFFu : (v >> 2) & 0x1Fu;
+}
+
+template <int EB>
+__global__ __launch_bounds__(kThreads) void k_hist(const uint8_t *__restrict__ x, uint64_t n, uint64_t B,
                                                    uint64_t S, unsigned long long *__restrict__ hist)
 {
+    constexpr uint32_t VG = 16 / EB;                         // values per 16-byte group
     __shared__ uint32_t sh[kThreads / 64][kHistCopies * kHistStride];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < (kThreads / 64) * kHistCopies * kHistStride; i += kThreads) (&sh[0][0])[i] = 0;
     __syncthreads();
     uint32_t *mine = &sh[wave][(lane % kHistCopies) * kHistStride];
-    // 8-word groups, numbered block by block (n < 2^32, so 32 bits hold them);
-    // kHistUnroll groups per thread and round, all loads issued first
+    // groups of VG values, numbered block by block (n < 2^32, so 32 bits hold
+    // them); kHistUnroll groups per thread and round, all loads issued first
     const uint32_t nblk = (uint32_t)((n + B - 1) / B);
-    const uint32_t gps = (uint32_t)(S / 8);                  // groups per block sample
+    const uint32_t gps = (uint32_t)(S / VG);                 // groups per block sample
     const uint32_t ngroups = nblk * gps;
     const uint32_t stride = gridDim.x * kThreads * kHistUnroll;
     for (uint32_t g0 = blockIdx.x * kThreads * kHistUnroll + tid; g0 < ngroups; g0 += stride) {
@@ -337,23 +352,25 @@ __global__ __launch_bounds__(kThreads) void k_hist(const uint16_t *__restrict__ 
 #pragma unroll
         for (int u = 0; u < kHistUnroll; u++) {
             const uint32_t g = g0 + u * kThreads;
-            w0[u] = (uint64_t)(g / gps) * B + (uint64_t)(g % gps) * 8;   // first word of the group
+            w0[u] = (uint64_t)(g / gps) * B + (uint64_t)(g % gps) * VG;   // first value of the group
             v[u] = u32x4{0u, 0u, 0u, 0u};
-            if (g < ngroups && w0[u] + 8 <= n) v[u] = ld_stream(reinterpret_cast<const u32x4 *>(x + w0[u]));
+            if (g < ngroups && w0[u] + VG <= n) v[u] = ld_stream(reinterpret_cast<const u32x4 *>(x + EB * w0[u]));
         }
 #pragma unroll
         for (int u = 0; u < kHistUnroll; u++) {
             const uint32_t g = g0 + u * kThreads;
             if (g >= ngroups) continue;
-            if (w0[u] + 8 <= n) {
+            if (w0[u] + VG <= n) {
                 const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    atomicAdd(&mine[(w[q] >> 7) & 0xFFu], 1u);
-                    atomicAdd(&mine[(w[q] >> 23) & 0xFFu], 1u);
-                }
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int h = 0; h < 4 / EB; h++) atomicAdd(&mine[hist_exponent<EB>(w[q] >> (8 * EB * h))], 1u);
             } else {
-                for (uint64_t i = w0[u]; i < n; i++) atomicAdd(&mine[(x[i] >> 7) & 0xFFu], 1u);
+                for (uint64_t i = w0[u]; i < n; i++) {
+                    const uint32_t val = EB == 2 ? reinterpret_cast<const uint16_t *>(x)[i] : x[i];
+                    atomicAdd(&mine[hist_exponent<EB>(val)], 1u);
+                }
             }
         }
     }
@@ -562,7 +579,10 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
 // slot is scratch and only its first m entries are read). The stores are
 // temporal: the placement kernel reads the slot back right away, from the
 // Infinity Cache.
-__device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[kEncGroups], uint64_t t0,
+// G groups of GW values per thread (group k of thread tid starts at tile
+// value k*kEncThreads*GW + tid*GW).
+template <int G = kEncGroups, int GW = 8>
+__device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[G], uint64_t t0,
                                               uint64_t tile, const EncWs &ws, const EncParams &p, const EscBuf &eb)
 {
     const int tid = threadIdx.x;
@@ -570,8 +590,8 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
     if (p.Cmask + 1 < (uint32_t)kEncTile) {
         uint32_t *cpt = ws.chunk_pre + (t0 >> p.logC);     // chunks no larger than the tile start at t0
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) {
-            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        for (int k = 0; k < G; k++) {
+            const uint32_t lo = (uint32_t)(k * (kEncThreads * GW) + tid * GW);
             if (cstart[k] != ~0u) cpt[lo >> p.logC] = cstart[k];
         }
     }
@@ -897,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     if (lane == 0) offs[p.nch] = (uint32_t)M;
     // zero padding after each section (each gap is under 256 bytes)
     for (int i = lane; i < 256; i += 64) {
-        const uint64_t sm_end = kHeader + p.n;
+        const uint64_t sm_end = kHeader + p.sm_bytes;
         if (sm_end + i < p.off_codes) out[sm_end + i] = 0;
         const uint64_t codes_end = p.off_codes + (p.n + 1) / 2;
         if (codes_end + i < p.off_offs) out[codes_end + i] = 0;
@@ -1369,6 +1389,233 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
+// ============================================================ FP8 E5M2 ====
+// The E5M2 variant ("SplitZip: Ultra Fast Lossless KV Compression for
+// Disaggregated LLM Serving", section 4.2 / appendix C): the 5-bit exponent
+// of each byte, e = (x >> 2) & 0x1f, takes a 4-bit Top-16 code; the other
+// three bits, a = sign << 2 | mantissa, are packed 3 bits per value (value i
+// at bits 3i..3i+2 of the section, least significant bit first). Escapes,
+// offsets, placement and container are the BF16 ones.
+constexpr int k8Vals = 32;                 // values per thread: 32 B of input
+static_assert(kEncThreads * k8Vals == kEncTile, "the FP8 encode tile is the BF16 one (staging slots)");
+constexpr int k8DecThreads = 128;
+constexpr int k8DecTile = k8DecThreads * k8Vals;
+
+// Code-table entries of 4 exponents (one per byte, each < 32) from the 32
+// entries of T (8 dwords, in registers): one byte permute per 8-entry slice,
+// then two permutes choose the slice by bits 3 and 4 of the exponent.
+__device__ __forceinline__ uint32_t lut32(const uint32_t T[8], uint32_t e)
+{
+    const uint32_t sel = e & 0x07070707u;
+    const uint32_t c0 = perm(T[1], T[0], sel), c1 = perm(T[3], T[2], sel);
+    const uint32_t c2 = perm(T[5], T[4], sel), c3 = perm(T[7], T[6], sel);
+    const uint32_t p3 = ((e >> 1) & 0x04040404u) | 0x03020100u;
+    const uint32_t p4 = ((e >> 2) & 0x04040404u) | 0x03020100u;
+    return perm(perm(c3, c2, p3), perm(c1, c0, p3), p4);
+}
+
+// Three bits (sign, mantissa) of each byte of w, one per byte.
+__device__ __forceinline__ uint32_t signmant8x4(uint32_t w)
+{
+    return bfi(0x03030303u, w, w >> 5) & 0x07070707u;
+}
+
+// 4 three-bit values held one per byte -> a0 | a1 << 3 | a2 << 6 | a3 << 9.
+__device__ __forceinline__ uint32_t pack12(uint32_t a)
+{
+    const uint32_t t = (a | (a >> 5)) & 0x003F003Fu;
+    return (t | (t >> 10)) & 0xFFFu;
+}
+
+// Inverse of pack12.
+__device__ __forceinline__ uint32_t unpack12(uint32_t c)
+{
+    const uint32_t t = (c & 0x3Fu) | ((c & 0xFC0u) << 10);
+    return (t & 0x00070007u) | ((t & 0x00380038u) << 5);
+}
+
+// Rebuild 4 E5M2 bytes from their 3 kept bits (a) and exponents (e), one per byte.
+__device__ __forceinline__ uint32_t merge8x4(uint32_t a, uint32_t e)
+{
+    return ((a & 0x04040404u) << 5) | ((e & 0x1F1F1F1Fu) << 2) | (a & 0x03030303u);
+}
+
+__global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__restrict__ x,
+                                                              uint8_t *__restrict__ out, EncWs ws, EncParams p)
+{
+    __shared__ uint32_t wtot[kEncThreads / 64];
+    __shared__ EscBuf eb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t tile = blockIdx.x;
+    const uint64_t t0 = tile * kEncTile;
+    const uint32_t rem = enc_tile_words(t0, p);
+    const uint32_t lo = (uint32_t)tid * k8Vals;               // this thread's first value in the tile
+    uint32_t w[8];
+    if (lo + k8Vals <= rem) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(x + t0 + lo);
+        const u32x4 v0 = ld_stream(src), v1 = ld_stream(src + 1);
+        w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+        w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const uint32_t i = lo + 4 * q + b;
+                if (i < rem) v |= (uint32_t)x[t0 + i] << (8 * b);
+            }
+            w[q] = v;
+        }
+    }
+    uint32_t T[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) T[q] = reinterpret_cast<const uint32_t *>(p.lut)[q];
+    uint32_t L[8], E[8], A[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        E[q] = (w[q] >> 2) & 0x1F1F1F1Fu;
+        L[q] = lut32(T, E[q]);
+        A[q] = signmant8x4(w[q]);
+    }
+    if (lo + k8Vals > rem) {                     // tail: values past n are not escapes and take code 0
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                if (lo + 4 * q + b >= rem) L[q] &= ~(0xFFu << (8 * b));
+    }
+    if (lo < rem) {
+        u32x4 cw;
+        cw.x = pack_codes8(L[0], L[1]);
+        cw.y = pack_codes8(L[2], L[3]);
+        cw.z = pack_codes8(L[4], L[5]);
+        cw.w = pack_codes8(L[6], L[7]);
+        st_stream(cw, reinterpret_cast<u32x4 *>(out + p.off_codes + t0 / 2 + lo / 2));
+        uint32_t c[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) c[q] = pack12(A[q]);
+        const uint32_t sw[3] = {c[0] | (c[1] << 12) | (c[2] << 24),
+                                (c[2] >> 8) | (c[3] << 4) | (c[4] << 16) | (c[5] << 28),
+                                (c[5] >> 4) | (c[6] << 8) | (c[7] << 20)};
+        uint8_t *smb = out + kHeader + (t0 + lo) / 8 * 3;
+        if (lo + k8Vals <= rem) {
+            uint32_t *smw = reinterpret_cast<uint32_t *>(smb);
+            st_stream(sw[0], smw);
+            st_stream(sw[1], smw + 1);
+            st_stream(sw[2], smw + 2);
+        } else {
+            // the 12 bytes may run past the section (its end is a multiple of
+            // 256, not of 12) into the codes that tile 0 writes: store only the
+            // bytes that hold valid values
+            const uint32_t nb = (3 * (rem - lo) + 7) / 8;
+            for (uint32_t b = 0; b < nb; b++) smb[b] = (uint8_t)(sw[b >> 2] >> (8 * (b & 3)));
+        }
+    }
+    // escapes: the lane's count, its rank in the tile (values are in lane
+    // order), the list in LDS
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 8; q++) cnt += __builtin_popcount(L[q] & 0x80808080u);
+    uint32_t pre = 0, wt = 0;
+    if (__ballot(cnt != 0) != 0ull) {
+        const uint32_t inc = wave_inclusive_sum(cnt);
+        pre = inc - cnt;
+        wt = __builtin_amdgcn_readlane(inc, 63);
+    }
+    if (lane == 0) wtot[wave] = wt;
+    __syncthreads();
+    uint32_t base = 0, m = 0;
+#pragma unroll
+    for (int v = 0; v < kEncThreads / 64; v++) {
+        if (v < wave) base += wtot[v];
+        m += wtot[v];
+    }
+    uint32_t rank = base + pre;
+    const uint32_t g0m = ((uint32_t)(t0 & p.Cmask) + lo) & p.Cmask;   // a multiple of 32, below C
+    uint32_t cstart[1];
+    cstart[0] = (lo < rem && g0m == 0) ? rank : ~0u;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        uint32_t mask = L[q] & 0x80808080u;
+        while (mask) {
+            const uint32_t bit = __builtin_ctz(mask);          // 7, 15, 23 or 31
+            eb.pos[rank] = (uint16_t)(g0m + 4 * q + (bit >> 3));
+            eb.val[rank] = (uint8_t)(E[q] >> (bit - 7));
+            rank++;
+            mask &= mask - 1;
+        }
+    }
+    stage_escapes<1, k8Vals>(m, cstart, t0, tile, ws, p, eb);
+}
+
+// Merge the LDS patch of a thread's 32 values (li0 a multiple of 32): each
+// dword of 4 values takes the exponent bytes whose patch bits are set.
+template <int TILE>
+__device__ __forceinline__ void apply_patch32(const PatchShared<TILE> &sh, uint32_t li0, uint32_t y[8])
+{
+    const uint32_t bits = sh.mask[li0 >> 5];
+    if (bits == 0) return;
+    const u32x4 va = *reinterpret_cast<const u32x4 *>(&sh.val[li0]);
+    const u32x4 vb = *reinterpret_cast<const u32x4 *>(&sh.val[li0 + 16]);
+    const uint32_t v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const uint32_t b = (bits >> (4 * q)) & 0xFu;
+        const uint32_t spread = (b * 0x00204081u) & 0x01010101u;      // bit j -> byte j
+        const uint32_t m = perm(0u, 0u, 0x0C0C0C0Cu + spread) & 0x7C7C7C7Cu;   // 0x00 / 0xFF per byte
+        y[q] = bfi(m, v[q] << 2, y[q]);
+    }
+}
+
+template <bool kPatch>
+__global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8_t *__restrict__ y, DecParams p)
+{
+    __shared__ PatchShared<k8DecTile> sh;
+    const int tid = threadIdx.x;
+    const uint64_t t0 = (uint64_t)blockIdx.x * k8DecTile;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)k8DecTile) ? p.n - t0 : (uint64_t)k8DecTile);
+    const uint32_t lo = (uint32_t)tid * k8Vals;
+    uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
+    PatchHead ph;
+    if (kPatch) ph = patch_begin<k8DecTile, k8DecThreads>(s, t0, p);
+    uint32_t sm[3] = {0u, 0u, 0u};
+    u32x4 cd = {0u, 0u, 0u, 0u};
+    if (lo < rem) {
+        // sections are padded to 256 bytes, so a tail group's full loads stay inside them
+        const uint32_t *smw = reinterpret_cast<const uint32_t *>(s.base + kHeader + (t0 + lo) / 8 * 3);
+        sm[0] = ld_stream(smw);
+        sm[1] = ld_stream(smw + 1);
+        sm[2] = ld_stream(smw + 2);
+        cd = ld_stream(reinterpret_cast<const u32x4 *>(s.base + p.off_codes + t0 / 2 + lo / 2));
+    }
+    PatchFetch<kDecFetch> pf;
+    if (kPatch) pf = patch_fetch<k8DecTile, k8DecThreads, kDecFetch>(s, t0, p, ph);
+    const uint32_t c[8] = {sm[0] & 0xFFFu, (sm[0] >> 12) & 0xFFFu, (sm[0] >> 24) | ((sm[1] & 0xFu) << 8),
+                           (sm[1] >> 4) & 0xFFFu, (sm[1] >> 16) & 0xFFFu, (sm[1] >> 28) | ((sm[2] & 0xFFu) << 4),
+                           (sm[2] >> 8) & 0xFFFu, sm[2] >> 20};
+    const uint32_t cw[4] = {cd.x, cd.y, cd.z, cd.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const uint32_t lo4 = cw[h] & 0x0F0F0F0Fu;             // codes of values 8h + 0, 2, 4, 6
+        const uint32_t hi4 = (cw[h] >> 4) & 0x0F0F0F0Fu;      // 8h + 1, 3, 5, 7
+        out[2 * h] = merge8x4(unpack12(c[2 * h]), dec4(dec, perm(hi4, lo4, 0x05010400u)));
+        out[2 * h + 1] = merge8x4(unpack12(c[2 * h + 1]), dec4(dec, perm(hi4, lo4, 0x07030602u)));
+    }
+    if (kPatch) {
+        if (patch_build<k8DecTile, k8DecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) apply_patch32(sh, lo, out);
+    }
+    uint8_t *yt = y + t0;
+    if (lo + k8Vals <= rem) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(yt + lo);
+        st_stream(u32x4{out[0], out[1], out[2], out[3]}, dst);
+        st_stream(u32x4{out[4], out[5], out[6], out[7]}, dst + 1);
+    } else if (lo < rem) {
+        for (uint32_t i = 0; i < k8Vals && lo + i < rem; i++) yt[lo + i] = (uint8_t)(out[i >> 2] >> (8 * (i & 3)));
+    }
+}
+
 // ================================================================ host ====
 thread_local char g_hip_err[160];
 
@@ -1411,6 +1658,16 @@ int check_codebook(const uzip_codebook_t *cb)
     return UZIP_OK;
 }
 
+// A codebook for FP8 E5M2 streams: consistent, and every exponent below 32.
+int check_codebook8(const uzip_codebook_t *cb)
+{
+    const int rc = check_codebook(cb);
+    if (rc) return rc;
+    for (int k = 0; k < 16; k++)
+        if (cb->dec[k] > 31) return UZIP_EINVAL;
+    return UZIP_OK;
+}
+
 EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
 {
     EncParams p;
@@ -1428,6 +1685,7 @@ EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
     p.off_pos = L.off_pos;
     p.dlut = nullptr;
     p.ddec = nullptr;
+    p.sm_bytes = sm_bytes_of(L.n, L.fp8);
     return p;
 }
 
@@ -1452,6 +1710,7 @@ HeaderParams make_header_params(const Layout &L, const uzip_codebook_t *cb)
     h.tmpl[0] = 0x55; h.tmpl[1] = 0x5A; h.tmpl[2] = 0x42; h.tmpl[3] = 0x31;
     const uint16_t ver = 1;
     memcpy(h.tmpl + 4, &ver, 2);
+    h.tmpl[6] = L.fp8 ? 1 : 0;                // element type: 0 BF16, 1 FP8 E5M2
     memcpy(h.tmpl + 8, &L.C, 4);
     memcpy(h.tmpl + 16, &L.n, 8);
     memcpy(h.tmpl + 40, cb->dec, 16);
@@ -1502,17 +1761,23 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
 
 // Histogram launch: one 8-word group per thread and round, at most 2048
 // workgroups.
-void launch_hist(const uint16_t *d_x, uint64_t n, uint64_t block, uint64_t sample, uint64_t *d_hist,
-                 hipStream_t s)
+// eb: element bytes (2 BF16, 1 FP8 E5M2); block and sample are multiples of
+// 16 / eb values.
+void launch_hist(const void *d_x, uint64_t n, uint64_t block, uint64_t sample, uint64_t *d_hist,
+                 hipStream_t s, int eb = 2)
 {
+    const uint64_t vg = 16 / eb;
     // a block longer than x is x: keeps the kernel's group numbers in 32 bits
-    const uint64_t n8 = (n + 7) & ~7ull;
-    if (block > n8) block = n8;
+    const uint64_t nr = (n + vg - 1) / vg * vg;
+    if (block > nr) block = nr;
     if (sample > block) sample = block;
-    const uint64_t groups = ((n + block - 1) / block) * (sample / 8);
+    const uint64_t groups = ((n + block - 1) / block) * (sample / vg);
     const uint64_t wgs = (groups + kThreads * kHistUnroll - 1) / (kThreads * kHistUnroll);
     const unsigned grid = (unsigned)(wgs < 2048 ? (wgs ? wgs : 1) : 2048);
-    k_hist<<<grid, kThreads, 0, s>>>(d_x, n, block, sample, reinterpret_cast<unsigned long long *>(d_hist));
+    const uint8_t *x = static_cast<const uint8_t *>(d_x);
+    unsigned long long *h = reinterpret_cast<unsigned long long *>(d_hist);
+    if (eb == 2) k_hist<2><<<grid, kThreads, 0, s>>>(x, n, block, sample, h);
+    else k_hist<1><<<grid, kThreads, 0, s>>>(x, n, block, sample, h);
 }
 
 // Host-side structural check (same rules as the header comment of
@@ -1610,17 +1875,19 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     uint32_t C;
     uint8_t dec[16];
     if (uzip_parse_header(s, &n, &C, &m, &total, dec) != UZIP_OK) return UZIP_ECORRUPT;
-    if (rd16(s + 6) != 0 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    const uint16_t etype = rd16(s + 6);                // 0 BF16, 1 FP8 E5M2
+    if (etype > 1 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    const bool fp8 = etype == 1;
     for (uint64_t i = 56; i < kHeader; i++)
         if (s[i]) return UZIP_ECORRUPT;
     if (!valid_nc(n, C) || m > n) return UZIP_ECORRUPT;
-    const Layout L = make_layout(n, C);
+    const Layout L = make_layout(n, C, fp8);
     const uint64_t off_val = off_val_of(L, m);
     if (total != off_val + m || bytes < total) return UZIP_ECORRUPT;
     if (memcmp(dec, cb->dec, 16) != 0) return UZIP_ECODEBOOK;
     bool in_book[256] = {false};
     for (int k = 0; k < 16; k++) {
-        if (in_book[dec[k]]) return UZIP_ECORRUPT;
+        if (in_book[dec[k]] || (fp8 && dec[k] > 31)) return UZIP_ECORRUPT;
         in_book[dec[k]] = true;
     }
     auto zero = [&](uint64_t a, uint64_t b) {
@@ -1629,7 +1896,9 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
         return true;
     };
     const uint64_t codes_bytes = (n + 1) / 2;
-    if (!zero(kHeader + n, L.off_codes)) return UZIP_ECORRUPT;
+    const uint64_t smb = sm_bytes_of(n, fp8);
+    if (!zero(kHeader + smb, L.off_codes)) return UZIP_ECORRUPT;
+    if (fp8 && (3 * n) % 8 && (s[kHeader + smb - 1] >> ((3 * n) % 8))) return UZIP_ECORRUPT;   // unused bits
     if ((n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
     if (!zero(L.off_codes + codes_bytes, L.off_offs)) return UZIP_ECORRUPT;
     if (!zero(L.off_offs + 4 * (L.nch + 1), L.off_pos)) return UZIP_ECORRUPT;
@@ -1645,7 +1914,7 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
             const uint32_t p = rd16(s + L.off_pos + 2 * j);
             if (p >= len || (j > j0 && p <= prev)) return UZIP_ECORRUPT;
             prev = p;
-            if (in_book[s[off_val + j]]) return UZIP_ECORRUPT;
+            if (in_book[s[off_val + j]] || (fp8 && s[off_val + j] > 31)) return UZIP_ECORRUPT;
             const uint64_t i = c * C + p;
             const uint8_t b = s[L.off_codes + i / 2];
             if (((i & 1) ? (b >> 4) : (b & 0xF)) != 0) return UZIP_ECORRUPT;
@@ -1757,6 +2026,88 @@ int uzip_encode_online(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t
                        hipStream_t s)
 {
     return uzip_encode_online_ex(d_x, n, chunk, block, sample, d_cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+uint64_t uzip_fp8_max_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk)) return 0;
+    return total_of(make_layout(n, chunk, true), n);
+}
+
+int uzip_fp8_histogram(const uint8_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s)
+{
+    if (!d_x || !d_hist || !aligned16(d_x) || ((uintptr_t)d_hist & 7u)) return UZIP_EINVAL;
+    if (n == 0 || n >= (1ull << 32)) return UZIP_EINVAL;
+    const uint64_t all = (n + 15) & ~15ull;
+    launch_hist(d_x, n, all, all, d_hist, s, 1);
+    UZIP_LAUNCH_CHECK("k_hist");
+    return UZIP_OK;
+}
+
+int uzip_fp8_calibrate(const uint8_t *d_x, uint64_t n, uint64_t *d_hist_ws, uzip_codebook_t *cb, hipStream_t s)
+{
+    if (!cb || !d_hist_ws) return UZIP_EINVAL;
+    hipError_t e = hipMemsetAsync(d_hist_ws, 0, 256 * sizeof(uint64_t), s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    int rc = uzip_fp8_histogram(d_x, n, d_hist_ws, s);
+    if (rc) return rc;
+    uint64_t h[256];
+    e = hipMemcpyAsync(h, d_hist_ws, sizeof h, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return uzip_codebook_from_hist(h, cb);
+}
+
+int uzip_fp8_encode_ex(const uint8_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook8(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_fp8_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk, true);
+    const EncParams ep = make_enc_params(L, cb);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    k8_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("k8_encode_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_fp8_encode(const uint8_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_fp8_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_fp8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       uint8_t *d_y, const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !d_y || !aligned16(d_in) || !aligned16(d_y)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook8(cb);
+    if (rc) return rc;
+    const Layout L = make_layout(n, chunk, true);
+    if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;   // smaller than any stream of n values
+    const DecParams dp = make_dec_params(L, cb);
+    const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    const uint64_t tiles = (n + k8DecTile - 1) / k8DecTile;
+    k8_decode_tile<true><<<(unsigned)tiles, k8DecThreads, 0, s>>>(si, d_y, dp);
+    UZIP_LAUNCH_CHECK("k8_decode_tile");
+    return ev.record(1);
+}
+
+int uzip_fp8_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    uint8_t *d_y, hipStream_t s)
+{
+    return uzip_fp8_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
 }
 
 int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,

@@ -26,7 +26,8 @@ EXPORTS = (
     "uzip_validate_host", "uzip_parse_header", "uzip_strerror", "uzip_histogram", "uzip_histogram_sampled",
     "uzip_calibrate", "uzip_encode", "uzip_encode_ex", "uzip_encode_online", "uzip_encode_online_ex",
     "uzip_stream_bytes", "uzip_decode", "uzip_decode_ex", "uzip_reduce_add", "uzip_reduce_add_ex",
-    "uzip_reduce_k", "uzip_reduce_k_ex", "uzip_validate",
+    "uzip_reduce_k", "uzip_reduce_k_ex", "uzip_validate", "uzip_fp8_max_bytes", "uzip_fp8_histogram",
+    "uzip_fp8_calibrate", "uzip_fp8_encode", "uzip_fp8_encode_ex", "uzip_fp8_decode", "uzip_fp8_decode_ex",
 )
 
 MAX_K = 16                      # UZIP_MAX_K
@@ -94,6 +95,13 @@ def lib():
         "uzip_reduce_k_ex": (i32, [ctypes.POINTER(vp), ctypes.POINTER(u64), u32, u64, u32, cbp, vp, u64, vp,
                                    u64, op, vp]),
         "uzip_validate": (i32, [vp, u64, cbp, vp]),
+        "uzip_fp8_max_bytes": (u64, [u64, u32]),
+        "uzip_fp8_histogram": (i32, [vp, u64, vp, vp]),
+        "uzip_fp8_calibrate": (i32, [vp, u64, vp, cbp, vp]),
+        "uzip_fp8_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
+        "uzip_fp8_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_fp8_decode": (i32, [vp, u64, u64, u32, cbp, vp, vp]),
+        "uzip_fp8_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -322,3 +330,60 @@ def validate(buf: torch.Tensor, cb: Codebook, nbytes: int | None = None, stream=
     if nbytes is None:
         nbytes, _ = stream_bytes(buf, stream)
     return int(lib().uzip_validate(_ptr(buf), nbytes, ctypes.byref(cb), _stream(stream)))
+
+
+# ------------------------------------------------------------ FP8 E5M2 ----
+def _bytes(t: torch.Tensor) -> torch.Tensor:
+    """View a float8_e5m2/uint8/int8 tensor as flat bytes."""
+    if t.dtype == torch.float8_e5m2:
+        t = t.view(torch.uint8)
+    if t.dtype not in (torch.uint8, torch.int8):
+        raise ValueError(f"expected 8-bit values, got {t.dtype}")
+    return t.reshape(-1)
+
+
+def fp8_max_bytes(n: int, chunk: int) -> int:
+    return int(lib().uzip_fp8_max_bytes(n, chunk))
+
+
+def fp8_histogram(x: torch.Tensor, hist: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    b = _bytes(x)
+    if hist is None:
+        hist = torch.zeros(256, dtype=torch.int64, device=b.device)
+    _check(lib().uzip_fp8_histogram(_ptr(b), b.numel(), _ptr(hist), _stream(stream)), "fp8_histogram")
+    return hist
+
+
+def fp8_calibrate(x: torch.Tensor, stream=None) -> Codebook:
+    b = _bytes(x)
+    ws = torch.empty(256, dtype=torch.int64, device=b.device)
+    cb = Codebook()
+    _check(lib().uzip_fp8_calibrate(_ptr(b), b.numel(), _ptr(ws), ctypes.byref(cb), _stream(stream)),
+           "fp8_calibrate")
+    return cb
+
+
+def fp8_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None, events=None, stream=None) -> torch.Tensor:
+    b = _bytes(x)
+    n = b.numel()
+    if out is None:
+        out = torch.empty(fp8_max_bytes(n, chunk), dtype=torch.uint8, device=b.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=b.device)
+    o = _opts(events)
+    _check(lib().uzip_fp8_encode_ex(_ptr(b), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
+                                    ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "fp8_encode")
+    return out
+
+
+def fp8_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
+               in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
+    """Decode n E5M2 values; returns a uint8 tensor."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=buf.device)
+    o = _opts(events)
+    nb = buf.numel() if in_bytes is None else in_bytes
+    _check(lib().uzip_fp8_decode_ex(_ptr(buf), nb, n, chunk, ctypes.byref(cb), _ptr(out),
+                                    ctypes.byref(o) if o else None, _stream(stream)), "fp8_decode")
+    return out

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def header_symbols():
     src = open(os.path.join(ROOT, "include", "uzip.h")).read()
-    return sorted(set(re.findall(r"\b(uzip_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(uzip_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -120,6 +120,34 @@ def test_validate_host_rejects_corruptions():
     assert uzip.validate_host(s.tobytes(), uzip.codebook_from_hist(other)) == -4
 
 
+@pytest.mark.parametrize("n,C", [(1, 64), (1001, 256), (65536, 1024), (70001, 65536)])
+def test_fp8_max_bytes_matches_oracle(n, C):
+    assert uzip.fp8_max_bytes(n, C) == oracle.fp8_max_bytes(n, C)
+
+
+def test_validate_host_fp8_streams():
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 256, 5003).astype(np.uint8)
+    ocb = oracle.fp8_calibrate(x[:700])
+    cb = uzip.codebook_from_hist(ocb.hist)
+    s = oracle.fp8_encode(x, 256, ocb.dec)
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    bad = s.copy(); bad[6] = 0                         # claims BF16: sizes no longer fit
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[6] = 2                         # unknown element type
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[256 + (3 * x.size) // 8] |= 0x80   # an unused bit of the 3-bit section
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    m = int(np.frombuffer(s[24:32].tobytes(), np.uint64)[0])
+    val = s.size - m
+    bad = s.copy(); bad[val] = 0x20                    # not a 5-bit exponent
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    # BF16 streams are still checked as before
+    y = rng.integers(0, 65536, 3001).astype(np.uint16)
+    ocb2 = oracle.calibrate(y)
+    assert uzip.validate_host(oracle.encode(y, 256, ocb2.dec).tobytes(), uzip.codebook_from_hist(ocb2.hist)) == 0
+
+
 def test_strerror_texts():
     L = uzip.lib()
     for code in (0, -1, -2, -3, -4, -5, 7):
@@ -167,6 +195,13 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_encode_online(p, 1000, 1024, 0, 0, None, p, big, p, ws - 1, None) == -2
     assert L.uzip_histogram_sampled(p, 1000, 16, 24, p, None) == -1
     assert L.uzip_histogram_sampled(p, 1000, 16, 0, p, None) == -1
+    cb8 = uzip.codebook_from_hist(np.r_[np.arange(32, 0, -1), np.zeros(224)].astype(np.uint64))
+    b8 = uzip.fp8_max_bytes(1000, 1024)
+    assert L.uzip_fp8_encode(p, 1000, 1024, cbr, p, b8, p, ws, None) == -1        # exponents above 31
+    assert L.uzip_fp8_encode(p, 1000, 1024, ctypes.byref(cb8), p, b8 - 1, p, ws, None) == -2
+    assert L.uzip_fp8_decode(p, 10, 1000, 1024, ctypes.byref(cb8), p, None) == -1   # in_bytes too small
+    assert L.uzip_fp8_decode(p, b8, 1000, 1024, ctypes.byref(cb8), mis, None) == -1
+    assert L.uzip_fp8_histogram(mis, 100, p, None) == -1
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1
