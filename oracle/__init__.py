@@ -73,6 +73,11 @@ def _load():
         "orc_bf16_rne_array": (None, [ctypes.POINTER(ctypes.c_uint32), c64, u16p]),
         "orc_add_bf16_array": (None, [u16p, u16p, c64, u16p]),
         "orc_sum_bf16": (ctypes.c_uint16, [u16p, c32, c64]),
+        "orcs_max_bytes": (c64, [c64, c32]),
+        "orcs_payload_bytes": (c64, [c64, c64]),
+        "orcs_encode": (c64, [u16p, c64, c32, u8p, u8p, c64]),
+        "orcs_decode": (ctypes.c_int, [u8p, c64, c64, c32, u8p, u16p]),
+        "orcs_validate": (ctypes.c_int, [u8p, c64, u8p]),
         "orc8_exponent": (ctypes.c_uint8, [ctypes.c_uint8]),
         "orc8_signmant": (ctypes.c_uint8, [ctypes.c_uint8]),
         "orc8_merge": (ctypes.c_uint8, [ctypes.c_uint8, ctypes.c_uint8]),
@@ -363,3 +368,41 @@ def fp8_validate(stream, dec) -> int:
     stream = _u8(stream)
     dec = _u8(dec)
     return int(_load().orc8_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))
+
+
+# ------------------------------------------------ Top-15 + sentinel ----
+def s15_max_bytes(n: int, chunk: int) -> int:
+    return int(_load().orcs_max_bytes(n, chunk))
+
+
+def s15_payload_bytes(n: int, m: int) -> int:
+    return int(_load().orcs_payload_bytes(n, m))
+
+
+def s15_encode(x, chunk: int, dec) -> np.ndarray:
+    x = _u16(x).reshape(-1)
+    dec = _u8(dec)
+    cap = s15_max_bytes(x.size, chunk)
+    out = np.empty(cap, dtype=np.uint8)
+    total = _load().orcs_encode(_p(x, ctypes.c_uint16), x.size, chunk, _p(dec, ctypes.c_uint8),
+                                _p(out, ctypes.c_uint8), cap)
+    if total == 0:
+        raise ValueError("oracle s15 encode failed")
+    return out[:total].copy()
+
+
+def s15_decode(stream, n: int, chunk: int, dec) -> np.ndarray:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    y = np.empty(n, dtype=np.uint16)
+    rc = _load().orcs_decode(_p(stream, ctypes.c_uint8), stream.size, n, chunk, _p(dec, ctypes.c_uint8),
+                             _p(y, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle s15 decode failed")
+    return y
+
+
+def s15_validate(stream, dec) -> int:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    return int(_load().orcs_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))

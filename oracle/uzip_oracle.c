@@ -576,3 +576,151 @@ int orc8_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
     }
     return 0;
 }
+
+/* =========================================== Top-15 + sentinel format === */
+/* [SZ] section 3.4 / Table 6, the alternative the page weighs against
+ * Top-16: one codeword is an explicit escape token, so the decoder finds the
+ * escapes in the code stream and no positions are stored. Readings:
+ *   - codes 0..14 are the 15 most frequent exponents (dec[0..14] of the
+ *     Top-16 ranking); code 15 marks an escape; dec[15] is not used;
+ *   - each chunk's escapes are stored as their raw exponents (u8), in
+ *     ascending position, chunk after chunk, with the u32 chunk offsets;
+ *   - the container is the BF16 one with header flags = 2 and no position
+ *     section: header | sm | codes | offsets | val;
+ *   - payload = N + ceil(N/2) + M bytes. */
+static int orcs_code_of(const uint8_t *dec, uint8_t e)
+{
+    for (int k = 0; k < 15; k++)
+        if (dec[k] == e) return k;
+    return -1;
+}
+
+static orc_layout orcs_layout_of(uint64_t n, uint32_t C, uint64_t m)
+{
+    orc_layout L;
+    uint64_t nch = orc_nchunks(n, C);
+    L.sm = ORC_HEADER;
+    L.codes = L.sm + orc_align(n);
+    L.offs = L.codes + orc_align((n + 1) / 2);
+    L.pos = L.offs + orc_align(4 * (nch + 1));     /* no position section */
+    L.val = L.pos;
+    L.total = L.val + m;
+    return L;
+}
+
+uint64_t orcs_max_bytes(uint64_t n, uint32_t C)
+{
+    if (n == 0 || C == 0) return 0;
+    return orcs_layout_of(n, C, n).total;
+}
+
+uint64_t orcs_payload_bytes(uint64_t n, uint64_t m) { return n + (n + 1) / 2 + m; }
+
+uint64_t orcs_encode(const uint16_t *x, uint64_t n, uint32_t C, const uint8_t *dec, uint8_t *out, uint64_t cap)
+{
+    if (n == 0 || C == 0 || C > 65536u || n >= ((uint64_t)1 << 32)) return 0;
+    if (cap < orcs_max_bytes(n, C)) return 0;
+    uint64_t m = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if (orcs_code_of(dec, orc_exponent(x[i])) < 0) m++;
+    orc_layout L = orcs_layout_of(n, C, m);
+    memset(out, 0, L.total);
+    for (uint64_t i = 0; i < n; i++) {
+        out[L.sm + i] = orc_signmant(x[i]);
+        int k = orcs_code_of(dec, orc_exponent(x[i]));
+        unsigned code = (k < 0) ? 15u : (unsigned)k;          /* the sentinel */
+        if (i % 2 == 0) out[L.codes + i / 2] |= (uint8_t)code;
+        else            out[L.codes + i / 2] |= (uint8_t)(code << 4);
+    }
+    uint64_t nch = orc_nchunks(n, C);
+    uint64_t j = 0;
+    for (uint64_t c = 0; c < nch; c++) {
+        put_u32(out + L.offs + 4 * c, (uint32_t)j);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t e = orc_exponent(x[i]);
+            if (orcs_code_of(dec, e) < 0) out[L.val + j++] = e;
+        }
+    }
+    put_u32(out + L.offs + 4 * nch, (uint32_t)j);
+    out[0] = 0x55; out[1] = 0x5A; out[2] = 0x42; out[3] = 0x31;
+    put_u16(out + 4, 1);
+    put_u16(out + 6, 2);                         /* format: Top-15 + sentinel */
+    put_u32(out + 8, C);
+    put_u32(out + 12, 0);
+    put_u64(out + 16, n);
+    put_u64(out + 24, m);
+    put_u64(out + 32, L.total);
+    memcpy(out + 40, dec, 16);
+    return L.total;
+}
+
+/* Decode: a code below 15 is looked up; a sentinel takes the next raw
+ * exponent of its chunk (the chunk's offset plus the sentinels before it in
+ * the chunk). Returns 0 or -1. */
+int orcs_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint32_t C, const uint8_t *dec, uint16_t *y)
+{
+    if (in_bytes < ORC_HEADER || n == 0 || C == 0) return -1;
+    if (get_u64(in + 16) != n || get_u32(in + 8) != C || get_u16(in + 6) != 2) return -1;
+    if (memcmp(in + 40, dec, 16) != 0) return -1;
+    uint64_t m = get_u64(in + 24);
+    orc_layout L = orcs_layout_of(n, C, m);
+    if (in_bytes < L.total) return -1;
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t c = 0; c < nch; c++) {
+        uint64_t j = get_u32(in + L.offs + 4 * c);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t byte = in[L.codes + i / 2];
+            unsigned code = (i % 2 == 0) ? (byte & 0x0fu) : (byte >> 4);
+            if (code < 15) {
+                y[i] = orc_merge(in[L.sm + i], dec[code]);
+            } else {
+                if (j >= m) return -1;
+                y[i] = orc_merge(in[L.sm + i], in[L.val + j++]);
+            }
+        }
+        if (j != get_u32(in + L.offs + 4 * (c + 1))) return -1;
+    }
+    return 0;
+}
+
+/* Structural check: header (flags 2), sizes, zero padding, offsets from 0
+ * to m, each chunk's sentinel count equal to its offset difference, and
+ * every stored exponent outside dec[0..14]. */
+int orcs_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
+{
+    if (in_bytes < ORC_HEADER) return -3;
+    if (!(in[0] == 0x55 && in[1] == 0x5A && in[2] == 0x42 && in[3] == 0x31)) return -3;
+    if (get_u16(in + 4) != 1 || get_u16(in + 6) != 2 || get_u32(in + 12) != 0) return -3;
+    uint32_t C = get_u32(in + 8);
+    uint64_t n = get_u64(in + 16), m = get_u64(in + 24), total = get_u64(in + 32);
+    if (C == 0 || C > 65536u || n == 0 || n >= ((uint64_t)1 << 32) || m > n) return -3;
+    for (int i = 56; i < 256; i++) if (in[i] != 0) return -3;
+    orc_layout L = orcs_layout_of(n, C, m);
+    if (total != L.total || in_bytes < L.total) return -3;
+    if (memcmp(in + 40, dec, 16) != 0) return -4;
+    for (int k = 0; k < 16; k++)
+        for (int q = k + 1; q < 16; q++)
+            if (dec[k] == dec[q]) return -3;
+    for (uint64_t p = L.sm + n; p < L.codes; p++) if (in[p]) return -3;
+    if (n % 2 == 1 && (in[L.codes + n / 2] >> 4) != 0) return -3;
+    for (uint64_t p = L.codes + (n + 1) / 2; p < L.offs; p++) if (in[p]) return -3;
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t p = L.offs + 4 * (nch + 1); p < L.val; p++) if (in[p]) return -3;
+    if (get_u32(in + L.offs) != 0 || get_u32(in + L.offs + 4 * nch) != m) return -3;
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        uint64_t sentinels = 0;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t byte = in[L.codes + i / 2];
+            unsigned code = (i % 2 == 0) ? (byte & 0x0fu) : (byte >> 4);
+            if (code == 15) sentinels++;
+        }
+        if (j1 < j0 || j1 - j0 != sentinels) return -3;
+        for (uint32_t j = j0; j < j1; j++)
+            if (orcs_code_of(dec, in[L.val + j]) >= 0) return -3;     /* must be an escape */
+    }
+    return 0;
+}

@@ -45,6 +45,12 @@ MUTANTS = {
                            "    for (uint32_t i = k - 1; i-- > 0;) s = s + orc_bf16_to_f32(v[(uint64_t)i * stride]);"),
     "sum_in_binary64": ("volatile float s = orc_bf16_to_f32(v[0]);", "volatile double s = orc_bf16_to_f32(v[0]);"),
     "sum_skips_first_input": ("for (uint32_t i = 1; i < k; i++) s = s +", "for (uint32_t i = 2; i < k; i++) s = s +"),
+    "s15_sentinel_14": ("unsigned code = (k < 0) ? 15u : (unsigned)k;          /* the sentinel */",
+                        "unsigned code = (k < 0) ? 14u : (unsigned)k;          /* the sentinel */"),
+    "s15_uses_16_codes": ("    for (int k = 0; k < 15; k++)\n        if (dec[k] == e) return k;\n    return -1;\n}\n\nstatic orc_layout orcs_layout_of",
+                          "    for (int k = 0; k < 16; k++)\n        if (dec[k] == e) return k;\n    return -1;\n}\n\nstatic orc_layout orcs_layout_of"),
+    "s15_keeps_position_section": ("    L.val = L.pos;\n    L.total = L.val + m;",
+                                   "    L.val = L.pos + orc_align(2 * m);\n    L.total = L.val + m;"),
     "fp8_sign_shift": ("(uint8_t)(((x >> 5) & 0x4u) | (x & 0x3u))", "(uint8_t)(((x >> 4) & 0x4u) | (x & 0x3u))"),
     "fp8_exponent_width": ("(uint8_t)((x >> 2) & 0x1fu)", "(uint8_t)((x >> 2) & 0x0fu)"),
     "fp8_msb_first_bits": ("sec[b / 8] |= (uint8_t)(1u << (b % 8));", "sec[b / 8] |= (uint8_t)(0x80u >> (b % 8));"),
@@ -53,7 +59,7 @@ MUTANTS = {
 }
 
 PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py",
-             "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py"]
+             "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py", "tests/test_oracle_s15.py"]
 
 
 def _run(name, a, b, tmp):
