@@ -120,8 +120,8 @@ int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
  * Returns UZIP_OK, or UZIP_EINVAL (NULL, or entries not distinct). */
 int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
 
-/* Full structural check of a stream held in host memory (BF16 or, with
- * header flags 1, FP8 E5M2): header fields,
+/* Full structural check of a stream held in host memory (any format: BF16,
+ * FP8 E5M2 with header flags 1, Top-15 + sentinel with flags 2): header fields,
  * section sizes, zero padding, offsets monotone and ending at M, positions
  * ascending and inside their chunk, every escape value outside the codebook
  * with code 0 in the dense stream. Returns UZIP_OK, UZIP_ECORRUPT,
@@ -210,6 +210,27 @@ int uzip_fp8_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t ch
                     const uzip_codebook_t *cb, uint8_t *d_y, hipStream_t s);
 int uzip_fp8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
                        const uzip_codebook_t *cb, uint8_t *d_y, const uzip_opts_t *opts, hipStream_t s);
+
+/* ------------------------------------- Top-15 + sentinel (ablation) ---- */
+/* "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+ * Serving", section 3.4 / Table 6: the format the page weighs against
+ * Top-16, kept here to measure that trade-off. Codes 0..14 are dec[0..14];
+ * code 15 marks an escape, whose raw exponent is the next stored one of its
+ * chunk; no positions are stored. Stream: header (flags = 2) | sm | codes |
+ * offsets | values (u8, chunk by chunk, ascending position); payload
+ * N + ceil(N/2) + M. The codebook is a Top-16 one (dec[15] is not used).
+ * chunk must be at most 4096 (a decode tile starts a chunk); otherwise as
+ * uzip_encode / uzip_decode. */
+uint64_t uzip_s15_max_bytes(uint64_t n, uint32_t chunk);
+int uzip_s15_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s);
+int uzip_s15_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s);
+int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                    const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
+int uzip_s15_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                       const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Reads a device stream's header. Returns its size and M.
  * Either output pointer may be NULL. */

@@ -52,25 +52,34 @@ constexpr uint64_t kHeader = 256;
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255u); }
 
+// Stream formats (header flags): Top-16 codes with escape positions on BF16
+// words or on FP8 E5M2 bytes, and Top-15 + sentinel on BF16 words (no
+// position section).
+enum : uint8_t { kFmtBF16 = 0, kFmtFP8 = 1, kFmtS15 = 2 };
+
 struct Layout {
     uint64_t n, nch;
     uint32_t C, logC;
-    bool fp8;                                // E5M2 variant: 3-bit sign-mantissa fields
-    uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader
+    uint8_t fmt;
+    uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader; the S15 values start at off_pos
 };
 
-__host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m) { return L.off_pos + align256(2 * m); }
+__host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m)
+{
+    return L.off_pos + (L.fmt == kFmtS15 ? 0 : align256(2 * m));
+}
 __host__ __device__ inline uint64_t total_of(const Layout &L, uint64_t m) { return off_val_of(L, m) + m; }
 
 // fp8: the E5M2 variant, whose sign-mantissa section holds 3 bits per value.
 __host__ __device__ inline uint64_t sm_bytes_of(uint64_t n, bool fp8) { return fp8 ? (3 * n + 7) / 8 : n; }
 
-Layout make_layout(uint64_t n, uint32_t C, bool fp8 = false)
+Layout make_layout(uint64_t n, uint32_t C, uint8_t fmt = kFmtBF16)
 {
+    const bool fp8 = fmt == kFmtFP8;
     Layout L;
     L.n = n;
     L.C = C;
-    L.fp8 = fp8;
+    L.fmt = fmt;
     L.logC = 0;
     while ((1u << L.logC) < C) L.logC++;
     L.nch = (n + C - 1) / C;
@@ -173,6 +182,7 @@ struct EncParams {
     const uint8_t *dlut;   // if not null: the code table in device memory (used instead of lut)
     const uint8_t *ddec;   // if not null: dec[16] in device memory, for the stream header
     uint64_t sm_bytes;     // length of the sign-mantissa section
+    uint32_t posw;         // bytes per escape position: 2, or 0 for Top-15 + sentinel streams
     uint64_t n, nch, ntiles, ngroups;
     uint32_t Cmask, logC, gshift;
     uint64_t off_codes, off_offs, off_pos;
@@ -841,10 +851,10 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     const uint32_t m = __builtin_amdgcn_readfirstlane(m_l);
     const uint32_t P = __builtin_amdgcn_readfirstlane(before + tp_l);
     const uint64_t M = __builtin_amdgcn_readfirstlane(all);
-    const uint64_t off_val = p.off_pos + align256(2 * M);
+    const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // ---- the copies
-    const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, 2 * (uint64_t)m);
+    const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, p.posw ? 2 * (uint64_t)m : 0);
     const ShiftPlan qv = shift_plan(out + off_val + P, m);
     const uint64_t nb = qp.nblk > qv.nblk ? qp.nblk : qv.nblk;
     // loads of the first round past the prefetch
@@ -923,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
         if (codes_end + i < p.off_offs) out[codes_end + i] = 0;
         const uint64_t offs_end = p.off_offs + 4 * (p.nch + 1);
         if (offs_end + i < p.off_pos) out[offs_end + i] = 0;
-        const uint64_t pos_end = p.off_pos + 2 * M;
+        const uint64_t pos_end = p.off_pos + p.posw * M;
         if (pos_end + i < off_val) out[pos_end + i] = 0;
     }
 }
@@ -1616,6 +1626,114 @@ __global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8
     }
 }
 
+// ================================================= Top-15 + sentinel ====
+// "SplitZip" section 3.4 / Table 6: code 15 marks an escape, whose exponent
+// is the next stored one of its chunk; no positions are stored. Encoding is
+// k_encode_tile with a code table that gives every exponent outside
+// dec[0..14] code 15 and the escape flag, and placement without positions.
+// Decoding needs each sentinel's rank among the sentinels of its chunk: a
+// tile (whose chunks all start inside it: C <= tile) loads M, its chunk
+// offsets and its dense bytes, then its contiguous run of stored exponents
+// into LDS; the sentinels of each group of 8 words are ranked in position
+// order (wave scans, wave totals in LDS), and each takes its exponent from
+// LDS.
+constexpr int kS15Threads = 128;
+constexpr int kS15Groups = 4;              // groups of 8 words per thread
+constexpr int kS15Tile = kS15Threads * kS15Groups * 8;
+
+__global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+{
+    __shared__ uint8_t svals[kS15Tile];
+    __shared__ uint32_t wtot[kS15Groups][kS15Threads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kS15Tile;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kS15Tile) ? p.n - t0 : (uint64_t)kS15Tile);
+    // round 1: M, the tile's chunk offsets (C <= tile: the tile starts a chunk)
+    const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
+    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs) + (t0 >> p.logC);
+    const uint32_t nc = (uint32_t)(((t0 + rem - 1) >> p.logC) - (t0 >> p.logC) + 1);
+    const uint32_t o0 = offs[0], o1 = offs[nc];
+    const uint8_t *smt = s.base + kHeader + t0;
+    const uint8_t *cdt = s.base + p.off_codes + t0 / 2;
+    uint32_t dec[4] = {p.dec[0], p.dec[1], p.dec[2], p.dec[3]};
+    u32x2 sm[kS15Groups];
+    uint32_t cd[kS15Groups];
+#pragma unroll
+    for (int k = 0; k < kS15Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kS15Threads * 8) + tid * 8);
+        sm[k] = u32x2{0u, 0u};
+        cd[k] = 0u;
+        if (lo < rem) {
+            sm[k] = ld_stream(reinterpret_cast<const u32x2 *>(smt + lo));
+            cd[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdt + lo / 2));
+        }
+    }
+    // the tile's stored exponents: [E0, E1), clamped so that a corrupt stream
+    // reads inside the buffer
+    const bool okM = M <= p.n && p.off_pos + M <= s.bytes;
+    uint32_t E1 = okM ? (o1 < (uint32_t)M ? o1 : (uint32_t)M) : 0u;
+    uint32_t E0 = o0 < E1 ? o0 : E1;
+    if (E1 - E0 > rem) E1 = E0 + rem;
+    const uint32_t cnt = E1 - E0;
+    const uint8_t *val = s.base + p.off_pos + E0;
+    for (uint32_t j = tid; j < cnt; j += kS15Threads) svals[j] = val[j];
+    // sentinels: nibbles equal to 15, one flag per word at bit 4i
+    uint32_t f[kS15Groups], pre[kS15Groups];
+#pragma unroll
+    for (int k = 0; k < kS15Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kS15Threads * 8) + tid * 8);
+        uint32_t t = cd[k] & (cd[k] >> 1) & (cd[k] >> 2) & (cd[k] >> 3) & 0x11111111u;
+        if (lo + 8 > rem) t = lo < rem ? t & ((1u << (4 * (rem - lo))) - 1u) : 0u;
+        f[k] = t;
+        const uint32_t c = __builtin_popcount(t);
+        uint32_t pr = 0, wt = 0;
+        if (__ballot(c != 0) != 0ull) {
+            const uint32_t inc = wave_inclusive_sum(c);
+            pr = inc - c;
+            wt = __builtin_amdgcn_readlane(inc, 63);
+        }
+        pre[k] = pr;
+        if (lane == 0) wtot[k][wave] = wt;
+    }
+    uint32_t out[kS15Groups][4];
+#pragma unroll
+    for (int k = 0; k < kS15Groups; k++) decode8(sm[k].x, sm[k].y, cd[k], dec, out[k]);
+    __syncthreads();
+    uint32_t run = 0;
+#pragma unroll
+    for (int k = 0; k < kS15Groups; k++) {
+        uint32_t base = run;
+#pragma unroll
+        for (int w = 0; w < kS15Threads / 64; w++) {
+            if (w < wave) base += wtot[k][w];
+            run += wtot[k][w];
+        }
+        uint32_t r = base + pre[k];
+        uint32_t t = f[k];
+        while (t) {
+            const uint32_t bit = __builtin_ctz(t);     // 4i for word i of the group
+            const uint32_t i = bit >> 2;
+            if (r < cnt) {
+                const uint32_t sh = 7 + 16 * (i & 1);
+                out[k][i >> 1] = (out[k][i >> 1] & ~(0xFFu << sh)) | ((uint32_t)svals[r] << sh);
+            }
+            r++;
+            t &= t - 1;
+        }
+    }
+    uint16_t *yt = y + t0;
+#pragma unroll
+    for (int k = 0; k < kS15Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kS15Threads * 8) + tid * 8);
+        if (lo + 8 <= rem) {
+            st_stream(u32x4{out[k][0], out[k][1], out[k][2], out[k][3]}, reinterpret_cast<u32x4 *>(yt + lo));
+        } else if (lo < rem) {
+            for (uint32_t j = 0; j < 8 && lo + j < rem; j++)
+                yt[lo + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 // ================================================================ host ====
 thread_local char g_hip_err[160];
 
@@ -1685,7 +1803,8 @@ EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
     p.off_pos = L.off_pos;
     p.dlut = nullptr;
     p.ddec = nullptr;
-    p.sm_bytes = sm_bytes_of(L.n, L.fp8);
+    p.sm_bytes = sm_bytes_of(L.n, L.fmt == kFmtFP8);
+    p.posw = L.fmt == kFmtS15 ? 0 : 2;
     return p;
 }
 
@@ -1710,7 +1829,7 @@ HeaderParams make_header_params(const Layout &L, const uzip_codebook_t *cb)
     h.tmpl[0] = 0x55; h.tmpl[1] = 0x5A; h.tmpl[2] = 0x42; h.tmpl[3] = 0x31;
     const uint16_t ver = 1;
     memcpy(h.tmpl + 4, &ver, 2);
-    h.tmpl[6] = L.fp8 ? 1 : 0;                // element type: 0 BF16, 1 FP8 E5M2
+    h.tmpl[6] = L.fmt;                        // format: 0 BF16, 1 FP8 E5M2, 2 BF16 Top-15 + sentinel
     memcpy(h.tmpl + 8, &L.C, 4);
     memcpy(h.tmpl + 16, &L.n, 8);
     memcpy(h.tmpl + 40, cb->dec, 16);
@@ -1875,20 +1994,22 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     uint32_t C;
     uint8_t dec[16];
     if (uzip_parse_header(s, &n, &C, &m, &total, dec) != UZIP_OK) return UZIP_ECORRUPT;
-    const uint16_t etype = rd16(s + 6);                // 0 BF16, 1 FP8 E5M2
-    if (etype > 1 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
-    const bool fp8 = etype == 1;
+    const uint16_t fmt = rd16(s + 6);                  // 0 BF16, 1 FP8 E5M2, 2 BF16 Top-15 + sentinel
+    if (fmt > 2 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    const bool fp8 = fmt == kFmtFP8, s15 = fmt == kFmtS15;
     for (uint64_t i = 56; i < kHeader; i++)
         if (s[i]) return UZIP_ECORRUPT;
     if (!valid_nc(n, C) || m > n) return UZIP_ECORRUPT;
-    const Layout L = make_layout(n, C, fp8);
+    if (s15 && C > (uint32_t)kS15Tile) return UZIP_ECORRUPT;
+    const Layout L = make_layout(n, C, (uint8_t)fmt);
     const uint64_t off_val = off_val_of(L, m);
     if (total != off_val + m || bytes < total) return UZIP_ECORRUPT;
     if (memcmp(dec, cb->dec, 16) != 0) return UZIP_ECODEBOOK;
-    bool in_book[256] = {false};
+    bool in_book[256] = {false}, seen[256] = {false};
     for (int k = 0; k < 16; k++) {
-        if (in_book[dec[k]] || (fp8 && dec[k] > 31)) return UZIP_ECORRUPT;
-        in_book[dec[k]] = true;
+        if (seen[dec[k]] || (fp8 && dec[k] > 31)) return UZIP_ECORRUPT;
+        seen[dec[k]] = true;
+        in_book[dec[k]] = !s15 || k < 15;              // Top-15 + sentinel uses dec[0..14]
     }
     auto zero = [&](uint64_t a, uint64_t b) {
         for (uint64_t i = a; i < b; i++)
@@ -1902,9 +2023,25 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     if ((n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
     if (!zero(L.off_codes + codes_bytes, L.off_offs)) return UZIP_ECORRUPT;
     if (!zero(L.off_offs + 4 * (L.nch + 1), L.off_pos)) return UZIP_ECORRUPT;
-    if (!zero(L.off_pos + 2 * m, off_val)) return UZIP_ECORRUPT;
+    if (!s15 && !zero(L.off_pos + 2 * m, off_val)) return UZIP_ECORRUPT;
     const uint8_t *offs = s + L.off_offs;
     if (rd32(offs) != 0 || rd32(offs + 4 * L.nch) != m) return UZIP_ECORRUPT;
+    if (s15) {
+        // each chunk: as many stored exponents as sentinels (code 15), all outside dec[0..14]
+        for (uint64_t c = 0; c < L.nch; c++) {
+            const uint64_t j0 = rd32(offs + 4 * c), j1 = rd32(offs + 4 * (c + 1));
+            const uint64_t lo = c * C, hi = (lo + C < n) ? lo + C : n;
+            uint64_t sentinels = 0;
+            for (uint64_t i = lo; i < hi; i++) {
+                const uint8_t b = s[L.off_codes + i / 2];
+                sentinels += (((i & 1) ? (b >> 4) : (b & 0xF)) == 15);
+            }
+            if (j1 < j0 || j1 > m || j1 - j0 != sentinels) return UZIP_ECORRUPT;
+            for (uint64_t j = j0; j < j1; j++)
+                if (in_book[s[off_val + j]]) return UZIP_ECORRUPT;
+        }
+        return UZIP_OK;
+    }
     for (uint64_t c = 0; c < L.nch; c++) {
         const uint64_t j0 = rd32(offs + 4 * c), j1 = rd32(offs + 4 * (c + 1));
         const uint64_t len = (c + 1) * C <= n ? C : n - c * C;
@@ -2028,10 +2165,70 @@ int uzip_encode_online(const uint16_t *d_x, uint64_t n, uint32_t chunk, uint64_t
     return uzip_encode_online_ex(d_x, n, chunk, block, sample, d_cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
 }
 
+uint64_t uzip_s15_max_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kS15Tile) return 0;
+    return total_of(make_layout(n, chunk, kFmtS15), n);
+}
+
+int uzip_s15_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                       const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kS15Tile) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_s15_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk, kFmtS15);
+    EncParams ep = make_enc_params(L, cb);
+    ep.lut[cb->dec[15]] = 0x80;                 // the 16th exponent is an escape here
+    for (int e = 0; e < 256; e++)
+        if (ep.lut[e] & 0x80) ep.lut[e] = 0x80 | 15;   // escapes take the sentinel code
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    k_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("k_encode_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_s15_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_s15_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_s15_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                       uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !d_y || !aligned16(d_in) || !aligned16(d_y)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kS15Tile) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    const Layout L = make_layout(n, chunk, kFmtS15);
+    if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;
+    const DecParams dp = make_dec_params(L, cb);
+    const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    const uint64_t tiles = (n + kS15Tile - 1) / kS15Tile;
+    k_s15_decode_tile<<<(unsigned)tiles, kS15Threads, 0, s>>>(si, d_y, dp);
+    UZIP_LAUNCH_CHECK("k_s15_decode_tile");
+    return ev.record(1);
+}
+
+int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                    uint16_t *d_y, hipStream_t s)
+{
+    return uzip_s15_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
+}
+
 uint64_t uzip_fp8_max_bytes(uint64_t n, uint32_t chunk)
 {
     if (!valid_nc(n, chunk)) return 0;
-    return total_of(make_layout(n, chunk, true), n);
+    return total_of(make_layout(n, chunk, kFmtFP8), n);
 }
 
 int uzip_fp8_histogram(const uint8_t *d_x, uint64_t n, uint64_t *d_hist, hipStream_t s)
@@ -2068,7 +2265,7 @@ int uzip_fp8_encode_ex(const uint8_t *d_x, uint64_t n, uint32_t chunk, const uzi
     int rc = check_codebook8(cb);
     if (rc) return rc;
     if (out_cap < uzip_fp8_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
-    const Layout L = make_layout(n, chunk, true);
+    const Layout L = make_layout(n, chunk, kFmtFP8);
     const EncParams ep = make_enc_params(L, cb);
     const EncWs ws = make_ws(d_ws, n, chunk);
     const Events ev{opts, s};
@@ -2092,7 +2289,7 @@ int uzip_fp8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t
     if (!valid_nc(n, chunk)) return UZIP_EINVAL;
     int rc = check_codebook8(cb);
     if (rc) return rc;
-    const Layout L = make_layout(n, chunk, true);
+    const Layout L = make_layout(n, chunk, kFmtFP8);
     if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;   // smaller than any stream of n values
     const DecParams dp = make_dec_params(L, cb);
     const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};

@@ -148,6 +148,29 @@ def test_validate_host_fp8_streams():
     assert uzip.validate_host(oracle.encode(y, 256, ocb2.dec).tobytes(), uzip.codebook_from_hist(ocb2.hist)) == 0
 
 
+@pytest.mark.parametrize("n,C", [(1, 64), (1001, 256), (65536, 1024), (70001, 4096)])
+def test_s15_max_bytes_matches_oracle(n, C):
+    assert uzip.s15_max_bytes(n, C) == oracle.s15_max_bytes(n, C)
+    assert uzip.s15_max_bytes(n, 8192) == 0                # chunk above the decode tile
+
+
+def test_validate_host_s15_streams():
+    w = workloads.config(1)
+    x = w.x[:30001].copy()
+    ocb = oracle.calibrate(w.calib)
+    cb = uzip.codebook_from_hist(ocb.hist)
+    s = oracle.s15_encode(x, 256, ocb.dec)
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    codes = 256 + (x.size + 255) // 256 * 256
+    b = s[codes:codes + (x.size + 1) // 2]
+    nib = np.stack([b & 0xF, b >> 4], 1).reshape(-1)[:x.size]
+    i = int(np.nonzero(nib == 15)[0][0])
+    bad = s.copy(); bad[codes + i // 2] &= (0xF0 if i % 2 == 0 else 0x0F)
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[6] = 3
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+
+
 def test_strerror_texts():
     L = uzip.lib()
     for code in (0, -1, -2, -3, -4, -5, 7):
@@ -202,6 +225,10 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_fp8_decode(p, 10, 1000, 1024, ctypes.byref(cb8), p, None) == -1   # in_bytes too small
     assert L.uzip_fp8_decode(p, b8, 1000, 1024, ctypes.byref(cb8), mis, None) == -1
     assert L.uzip_fp8_histogram(mis, 100, p, None) == -1
+    s15b = uzip.s15_max_bytes(1000, 1024)
+    assert L.uzip_s15_encode(p, 1000, 8192, cbr, p, big, p, ws, None) == -1       # chunk above 4096
+    assert L.uzip_s15_encode(p, 1000, 1024, cbr, p, s15b - 1, p, ws, None) == -2
+    assert L.uzip_s15_decode(p, 10, 1000, 1024, cbr, p, None) == -1
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1
