@@ -242,6 +242,7 @@ def main():
     ap.add_argument("--no-reduce-k", action="store_true")
     ap.add_argument("--no-online", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--small", action="store_true", help="reduced-size workload (smoke)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first, to scale HBM byte counters")
@@ -432,6 +433,50 @@ def main():
                              "escape_rate": round(m_on / n, 6), "ratio_total": round(2 * n / tot_on, 4)}
         uzip.encode(x, cb, C, out=out, ws=ws)      # leave the offline stream in place
 
+    # --- ablation: Top-16 with positions against Top-15 + sentinel, on the
+    # headline tensor, under the offline codebook and one calibrated on the
+    # tensor itself ---
+    ablation = None
+    if not args.no_ablation:
+        ablation = {}
+        cb_self = uzip.codebook_from_hist(uzip.histogram(x).cpu().numpy().astype(np.uint64))
+        outs = torch.empty(uzip.s15_max_bytes(n, C), dtype=torch.uint8, device=dev)
+        for label, cbx in (("offline_codebook", cb), ("self_calibrated_codebook", cb_self)):
+            row = {}
+            for fmt, enc_f, dec_f, buf in (("top16_positions", uzip.encode, uzip.decode, out),
+                                           ("top15_sentinel", uzip.s15_encode, uzip.s15_decode, outs)):
+                enc_f(x, cbx, C, out=buf, ws=ws)
+                tt, mm = uzip.stream_bytes(buf)
+                dec_f(buf, cbx, n, C, out=y, in_bytes=tt)
+                torch.cuda.synchronize()
+                if not torch.equal(y, x):
+                    log(f"CORRECTNESS FAILURE ablation {label} {fmt}")
+                    sys.exit(1)
+                aev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(10)]
+                for rr in aev:
+                    for e in rr:
+                        e.record()
+                for k in range(10):
+                    flush()
+                    aev[k][0].record()
+                    dec_f(buf, cbx, n, C, out=y, in_bytes=tt)
+                    aev[k][1].record()
+                    flush()
+                    aev[k][2].record()
+                    enc_f(x, cbx, C, out=buf, ws=ws)
+                    aev[k][3].record()
+                torch.cuda.synchronize()
+                tdd = float(np.mean([aev[k][0].elapsed_time(aev[k][1]) for k in range(10)]))
+                tee = float(np.mean([aev[k][2].elapsed_time(aev[k][3]) for k in range(10)]))
+                row[fmt] = {"escape_rate": round(mm / n, 6), "ratio_total": round(2 * n / tt, 4),
+                            "encode_ms": round(tee, 4), "decode_ms": round(tdd, 4),
+                            "decode_GBps": round(2 * n / (tdd * 1e-3) / 1e9, 1)}
+            row["decode_slowdown_of_sentinel"] = round(row["top15_sentinel"]["decode_ms"] /
+                                                       row["top16_positions"]["decode_ms"], 3)
+            ablation[label] = row
+        del outs
+        uzip.encode(x, cb, C, out=out, ws=ws)      # leave the headline stream in place
+
     # --- FP8 E5M2 variant on the same KV-cache recipe cast to E5M2 (2^28 bytes) ---
     fp8 = None
     if not args.no_fp8:
@@ -546,6 +591,7 @@ def main():
         "reduce_k": reduce_k,
         "online_calibration": online,
         "fp8_e5m2": fp8,
+        "ablation_top15_sentinel": ablation,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
