@@ -10,8 +10,9 @@ for the passages each function follows and the readings taken where the pages
 leave a point open.
 
 Parity status: split/merge, histogram, Top-16, encode, decode, the reduce's
-rounding and the k-input reduce's summation order are pinned by the tests
-under ``tests/test_oracle_*.py``. The one
+rounding, the k-input reduce's summation order, and the FP8, Top-15 +
+sentinel and Top-7 3-bit + zero-point formats are pinned by the tests under
+``tests/test_oracle_*.py``. The one
 choice the pages do not fix at all -- a NaN sum in the reduce becomes 0x7FC0 --
 is "parity unpinned" (it is our own convention).
 """
@@ -73,6 +74,11 @@ def _load():
         "orc_bf16_rne_array": (None, [ctypes.POINTER(ctypes.c_uint32), c64, u16p]),
         "orc_add_bf16_array": (None, [u16p, u16p, c64, u16p]),
         "orc_sum_bf16": (ctypes.c_uint16, [u16p, c32, c64]),
+        "orcz_max_bytes": (c64, [c64, c32]),
+        "orcz_payload_bytes": (c64, [c64, c64]),
+        "orcz_encode": (c64, [u16p, c64, c32, u8p, u8p, c64]),
+        "orcz_decode": (ctypes.c_int, [u8p, c64, c64, c32, u8p, u16p]),
+        "orcz_validate": (ctypes.c_int, [u8p, c64, u8p]),
         "orcs_max_bytes": (c64, [c64, c32]),
         "orcs_payload_bytes": (c64, [c64, c64]),
         "orcs_encode": (c64, [u16p, c64, c32, u8p, u8p, c64]),
@@ -406,3 +412,41 @@ def s15_validate(stream, dec) -> int:
     stream = _u8(stream)
     dec = _u8(dec)
     return int(_load().orcs_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))
+
+
+# --------------------------------------- Top-7 3-bit + zero-point ------
+def z7_max_bytes(n: int, chunk: int) -> int:
+    return int(_load().orcz_max_bytes(n, chunk))
+
+
+def z7_payload_bytes(n: int, m: int) -> int:
+    return int(_load().orcz_payload_bytes(n, m))
+
+
+def z7_encode(x, chunk: int, dec) -> np.ndarray:
+    x = _u16(x).reshape(-1)
+    dec = _u8(dec)
+    cap = z7_max_bytes(x.size, chunk)
+    out = np.empty(cap, dtype=np.uint8)
+    total = _load().orcz_encode(_p(x, ctypes.c_uint16), x.size, chunk, _p(dec, ctypes.c_uint8),
+                                _p(out, ctypes.c_uint8), cap)
+    if total == 0:
+        raise ValueError("oracle z7 encode failed")
+    return out[:total].copy()
+
+
+def z7_decode(stream, n: int, chunk: int, dec) -> np.ndarray:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    y = np.empty(n, dtype=np.uint16)
+    rc = _load().orcz_decode(_p(stream, ctypes.c_uint8), stream.size, n, chunk, _p(dec, ctypes.c_uint8),
+                             _p(y, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle z7 decode failed")
+    return y
+
+
+def z7_validate(stream, dec) -> int:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    return int(_load().orcz_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))

@@ -22,7 +22,9 @@
  *         decompresses every received chunk before reducing it.
  *   [ZC]  "ZipCCL: Efficient Lossless Data Compression of Communication
  *         Collectives", adaptive communication strategies: a zipped
- *         all-to-all followed by a local reduction.
+ *         all-to-all followed by a local reduction; exponent coding: the top
+ *         7 exponents as 3-bit codes, code 000 a zero-point whose exponent
+ *         is stored whole in a separate array (the Top-7 section below).
  *
  * Readings where the pages leave a point open (each is the plainest reading;
  * the same list stands in the design notes):
@@ -721,6 +723,166 @@ int orcs_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
         if (j1 < j0 || j1 - j0 != sentinels) return -3;
         for (uint32_t j = j0; j < j1; j++)
             if (orcs_code_of(dec, in[L.val + j]) >= 0) return -3;     /* must be an escape */
+    }
+    return 0;
+}
+
+/* ======================================== Top-7 3-bit + zero-point ====== */
+/* "ZipCCL: Efficient Lossless Data Compression of Communication
+ * Collectives", exponent coding: the exponents among the 7 most frequent
+ * take 3-bit codes 001..111; every other exponent takes the zero-point code
+ * 000 and is stored whole in a separate zero-point array; 16 bits become 11
+ * for most values. The same page's kernel section keeps the 3-bit codes as
+ * three separate 1-bit arrays. Readings (the page gives the scheme, not the
+ * stream):
+ *   - code k + 1 for the k-th most frequent exponent (the Top-16 ranking,
+ *     ties to the smaller exponent), k = 0..6; dec[7..15] are not used;
+ *   - the codes are stored as three bit planes, one section each: bit b of
+ *     value i's code is bit i % 8 of byte i / 8 of plane b;
+ *   - the zero-point array holds the raw exponents chunk by chunk in
+ *     ascending position, with u32 chunk offsets (no positions);
+ *   - stream: header (flags = 3) | sm (N bytes) | plane 0 | plane 1 |
+ *     plane 2 (ceil(N/8) bytes each) | offsets | values; payload
+ *     N + 3 ceil(N/8) + M, so 16/11 with no zero-points. */
+static int orcz_code_of(const uint8_t *dec, uint8_t e)
+{
+    for (int k = 0; k < 7; k++)
+        if (dec[k] == e) return k + 1;
+    return 0;
+}
+
+static uint64_t orcz_plane_bytes(uint64_t n) { return (n + 7) / 8; }
+static unsigned orcz_bit(uint64_t i) { return (unsigned)(i % 8); }  /* least significant bit first */
+
+static orc_layout orcz_layout_of(uint64_t n, uint32_t C, uint64_t m)
+{
+    orc_layout L;
+    uint64_t nch = orc_nchunks(n, C);
+    L.sm = ORC_HEADER;
+    L.codes = L.sm + orc_align(n);                   /* plane 0; planes 1 and 2 follow */
+    L.offs = L.codes + 3 * orc_align(orcz_plane_bytes(n));
+    L.pos = L.offs + orc_align(4 * (nch + 1));      /* no position section */
+    L.val = L.pos;
+    L.total = L.val + m;
+    return L;
+}
+
+static unsigned orcz_get_code(const uint8_t *in, const orc_layout *L, uint64_t n, uint64_t i)
+{
+    uint64_t P = orc_align(orcz_plane_bytes(n));
+    unsigned code = 0;
+    for (int b = 0; b < 3; b++)
+        code |= ((in[L->codes + b * P + i / 8] >> orcz_bit(i)) & 1u) << b;
+    return code;
+}
+
+uint64_t orcz_max_bytes(uint64_t n, uint32_t C)
+{
+    if (n == 0 || C == 0) return 0;
+    return orcz_layout_of(n, C, n).total;
+}
+
+uint64_t orcz_payload_bytes(uint64_t n, uint64_t m) { return n + 3 * orcz_plane_bytes(n) + m; }
+
+uint64_t orcz_encode(const uint16_t *x, uint64_t n, uint32_t C, const uint8_t *dec, uint8_t *out, uint64_t cap)
+{
+    if (n == 0 || C == 0 || C > 65536u || n >= ((uint64_t)1 << 32)) return 0;
+    if (cap < orcz_max_bytes(n, C)) return 0;
+    uint64_t m = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if (orcz_code_of(dec, orc_exponent(x[i])) == 0) m++;
+    orc_layout L = orcz_layout_of(n, C, m);
+    uint64_t P = orc_align(orcz_plane_bytes(n));
+    memset(out, 0, L.total);
+    for (uint64_t i = 0; i < n; i++) {
+        out[L.sm + i] = orc_signmant(x[i]);
+        unsigned code = (unsigned)orcz_code_of(dec, orc_exponent(x[i]));
+        for (int b = 0; b < 3; b++)
+            if ((code >> b) & 1u) out[L.codes + b * P + i / 8] |= (uint8_t)(1u << orcz_bit(i));
+    }
+    uint64_t nch = orc_nchunks(n, C);
+    uint64_t j = 0;
+    for (uint64_t c = 0; c < nch; c++) {
+        put_u32(out + L.offs + 4 * c, (uint32_t)j);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t e = orc_exponent(x[i]);
+            if (orcz_code_of(dec, e) == 0) out[L.val + j++] = e;
+        }
+    }
+    put_u32(out + L.offs + 4 * nch, (uint32_t)j);
+    out[0] = 0x55; out[1] = 0x5A; out[2] = 0x42; out[3] = 0x31;
+    put_u16(out + 4, 1);
+    put_u16(out + 6, 3);                         /* format: Top-7 3-bit + zero-point */
+    put_u32(out + 8, C);
+    put_u32(out + 12, 0);
+    put_u64(out + 16, n);
+    put_u64(out + 24, m);
+    put_u64(out + 32, L.total);
+    memcpy(out + 40, dec, 16);
+    return L.total;
+}
+
+int orcz_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint32_t C, const uint8_t *dec, uint16_t *y)
+{
+    if (in_bytes < ORC_HEADER || n == 0 || C == 0) return -1;
+    if (get_u64(in + 16) != n || get_u32(in + 8) != C || get_u16(in + 6) != 3) return -1;
+    if (memcmp(in + 40, dec, 16) != 0) return -1;
+    uint64_t m = get_u64(in + 24);
+    orc_layout L = orcz_layout_of(n, C, m);
+    if (in_bytes < L.total) return -1;
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t c = 0; c < nch; c++) {
+        uint64_t j = get_u32(in + L.offs + 4 * c);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            unsigned code = orcz_get_code(in, &L, n, i);
+            if (code != 0) {
+                y[i] = orc_merge(in[L.sm + i], dec[code - 1]);
+            } else {
+                if (j >= m) return -1;
+                y[i] = orc_merge(in[L.sm + i], in[L.val + j++]);
+            }
+        }
+        if (j != get_u32(in + L.offs + 4 * (c + 1))) return -1;
+    }
+    return 0;
+}
+
+int orcz_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
+{
+    if (in_bytes < ORC_HEADER) return -3;
+    if (!(in[0] == 0x55 && in[1] == 0x5A && in[2] == 0x42 && in[3] == 0x31)) return -3;
+    if (get_u16(in + 4) != 1 || get_u16(in + 6) != 3 || get_u32(in + 12) != 0) return -3;
+    uint32_t C = get_u32(in + 8);
+    uint64_t n = get_u64(in + 16), m = get_u64(in + 24), total = get_u64(in + 32);
+    if (C == 0 || C > 65536u || n == 0 || n >= ((uint64_t)1 << 32) || m > n) return -3;
+    for (int i = 56; i < 256; i++) if (in[i] != 0) return -3;
+    orc_layout L = orcz_layout_of(n, C, m);
+    if (total != L.total || in_bytes < L.total) return -3;
+    if (memcmp(in + 40, dec, 16) != 0) return -4;
+    for (int k = 0; k < 16; k++)
+        for (int q = k + 1; q < 16; q++)
+            if (dec[k] == dec[q]) return -3;
+    for (uint64_t p = L.sm + n; p < L.codes; p++) if (in[p]) return -3;
+    uint64_t P = orc_align(orcz_plane_bytes(n));
+    for (int b = 0; b < 3; b++) {                    /* bits past n, then padding, are zero */
+        const uint8_t *pl = in + L.codes + b * P;
+        for (uint64_t i = n; i < 8 * P; i++)
+            if ((pl[i / 8] >> (i % 8)) & 1u) return -3;
+    }
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t p = L.offs + 4 * (nch + 1); p < L.val; p++) if (in[p]) return -3;
+    if (get_u32(in + L.offs) != 0 || get_u32(in + L.offs + 4 * nch) != m) return -3;
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        uint64_t zeros = 0;
+        for (uint64_t i = lo; i < hi; i++)
+            if (orcz_get_code(in, &L, n, i) == 0) zeros++;
+        if (j1 < j0 || j1 - j0 != zeros) return -3;
+        for (uint32_t j = j0; j < j1; j++)
+            if (orcz_code_of(dec, in[L.val + j]) != 0) return -3;     /* must be outside the top 7 */
     }
     return 0;
 }

@@ -56,10 +56,17 @@ MUTANTS = {
     "fp8_msb_first_bits": ("sec[b / 8] |= (uint8_t)(1u << (b % 8));", "sec[b / 8] |= (uint8_t)(0x80u >> (b % 8));"),
     "fp8_sm_section_length": ("static uint64_t orc8_sm_bytes(uint64_t n) { return (3 * n + 7) / 8; }",
                               "static uint64_t orc8_sm_bytes(uint64_t n) { return (3 * n) / 8 + 1; }"),
+    "z7_codes_from_zero": ("        if (dec[k] == e) return k + 1;", "        if (dec[k] == e) return k;"),
+    "z7_top8_codes": ("    for (int k = 0; k < 7; k++)\n        if (dec[k] == e) return k + 1;",
+                      "    for (int k = 0; k < 8; k++)\n        if (dec[k] == e) return k + 1;"),
+    "z7_msb_first_planes": ("return (unsigned)(i % 8); }", "return 7u - (unsigned)(i % 8); }"),
+    "z7_keeps_position_section": ("/* no position section */\n    L.val = L.pos;\n    L.total = L.val + m;\n    return L;\n}\n\nstatic unsigned orcz_get_code",
+                                  "/* no position section */\n    L.val = L.pos + orc_align(2 * m);\n    L.total = L.val + m;\n    return L;\n}\n\nstatic unsigned orcz_get_code"),
 }
 
 PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py",
-             "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py", "tests/test_oracle_s15.py"]
+             "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py", "tests/test_oracle_s15.py",
+             "tests/test_oracle_z7.py"]
 
 
 def _run(name, a, b, tmp):
