@@ -121,10 +121,12 @@ int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
 int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
 
 /* Full structural check of a stream held in host memory (any format: BF16,
- * FP8 E5M2 with header flags 1, Top-15 + sentinel with flags 2): header fields,
- * section sizes, zero padding, offsets monotone and ending at M, positions
- * ascending and inside their chunk, every escape value outside the codebook
- * with code 0 in the dense stream. Returns UZIP_OK, UZIP_ECORRUPT,
+ * FP8 E5M2 with header flags 1, Top-15 + sentinel with flags 2, Top-7 +
+ * zero-point with flags 3): header fields, section sizes, zero padding,
+ * offsets monotone and ending at M, positions ascending and inside their
+ * chunk, every escape value outside the codebook with code 0 in the dense
+ * stream (for the position-free formats: as many stored values per chunk as
+ * sentinels or zero-points, each outside the codes in use). Returns UZIP_OK, UZIP_ECORRUPT,
  * UZIP_ECODEBOOK or UZIP_EINVAL. */
 int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook_t *cb);
 
@@ -231,6 +233,31 @@ int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t ch
                     const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
 int uzip_s15_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
                        const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
+
+/* ------------------------------ Top-7 3-bit + zero-point (ablation) ---- */
+/* "ZipCCL: Efficient Lossless Data Compression of Communication
+ * Collectives", exponent coding: the seven most frequent exponents take
+ * 3-bit codes 1..7 (code k + 1 for dec[k], k < 7); any other exponent takes
+ * code 0, a zero-point, and its raw exponent is the next stored one of its
+ * chunk; no positions are stored. The page's kernels split the 3-bit codes
+ * into three 1-bit arrays; the stream keeps that split: bit b of value i's
+ * code is bit i % 8 of byte i / 8 of plane b. Stream: header (flags = 3) |
+ * sm (n bytes) | plane 0 | plane 1 | plane 2 (ceil(n/8) bytes each, each
+ * section 256-byte aligned) | offsets | values (u8, chunk by chunk, ascending
+ * position); payload n + 3 ceil(n/8) + M: 16 -> 11 bits per value with no
+ * zero-point. The codebook is a Top-16 one (dec[7..15] are not used). chunk
+ * must be at most 4096 (a decode tile starts a chunk); otherwise as
+ * uzip_encode / uzip_decode. */
+uint64_t uzip_z7_max_bytes(uint64_t n, uint32_t chunk);
+int uzip_z7_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s);
+int uzip_z7_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                      const uzip_opts_t *opts, hipStream_t s);
+int uzip_z7_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                   const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
+int uzip_z7_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                      const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Reads a device stream's header. Returns its size and M.
  * Either output pointer may be NULL. */

@@ -53,20 +53,24 @@ constexpr uint64_t kHeader = 256;
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255u); }
 
 // Stream formats (header flags): Top-16 codes with escape positions on BF16
-// words or on FP8 E5M2 bytes, and Top-15 + sentinel on BF16 words (no
-// position section).
-enum : uint8_t { kFmtBF16 = 0, kFmtFP8 = 1, kFmtS15 = 2 };
+// words or on FP8 E5M2 bytes; Top-15 + sentinel on BF16 words (no position
+// section); Top-7 3-bit codes + zero-points on BF16 words (three bit planes,
+// no position section).
+enum : uint8_t { kFmtBF16 = 0, kFmtFP8 = 1, kFmtS15 = 2, kFmtZ7 = 3 };
 
 struct Layout {
     uint64_t n, nch;
     uint32_t C, logC;
     uint8_t fmt;
-    uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader; the S15 values start at off_pos
+    uint64_t off_codes, off_offs, off_pos;   // off_sm is kHeader; S15 and Z7 values start at off_pos
+    uint64_t code_bytes, plane;              // one code section (or plane) and its 256-aligned stride
+    uint32_t nplanes;                        // 1, or 3 bit planes for Z7
 };
 
+__host__ __device__ inline bool has_pos(uint8_t fmt) { return fmt == kFmtBF16 || fmt == kFmtFP8; }
 __host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m)
 {
-    return L.off_pos + (L.fmt == kFmtS15 ? 0 : align256(2 * m));
+    return L.off_pos + (has_pos(L.fmt) ? align256(2 * m) : 0);
 }
 __host__ __device__ inline uint64_t total_of(const Layout &L, uint64_t m) { return off_val_of(L, m) + m; }
 
@@ -84,7 +88,10 @@ Layout make_layout(uint64_t n, uint32_t C, uint8_t fmt = kFmtBF16)
     while ((1u << L.logC) < C) L.logC++;
     L.nch = (n + C - 1) / C;
     L.off_codes = kHeader + align256(sm_bytes_of(n, fp8));
-    L.off_offs = L.off_codes + align256((n + 1) / 2);
+    L.nplanes = fmt == kFmtZ7 ? 3 : 1;
+    L.code_bytes = fmt == kFmtZ7 ? (n + 7) / 8 : (n + 1) / 2;
+    L.plane = align256(L.code_bytes);
+    L.off_offs = L.off_codes + L.nplanes * L.plane;
     L.off_pos = L.off_offs + align256(4 * (L.nch + 1));
     return L;
 }
@@ -182,7 +189,10 @@ struct EncParams {
     const uint8_t *dlut;   // if not null: the code table in device memory (used instead of lut)
     const uint8_t *ddec;   // if not null: dec[16] in device memory, for the stream header
     uint64_t sm_bytes;     // length of the sign-mantissa section
-    uint32_t posw;         // bytes per escape position: 2, or 0 for Top-15 + sentinel streams
+    uint64_t code_bytes;   // length of a code section (each of nplanes, plane bytes apart)
+    uint64_t plane;
+    uint32_t nplanes;
+    uint32_t posw;         // bytes per escape position: 2, or 0 for streams without positions
     uint64_t n, nch, ntiles, ngroups;
     uint32_t Cmask, logC, gshift;
     uint64_t off_codes, off_offs, off_pos;
@@ -194,6 +204,7 @@ struct DecParams {
     uint64_t n, nch;
     uint32_t C, logC;
     uint64_t off_codes, off_offs, off_pos;
+    uint64_t plane;        // bytes from one code plane to the next (Z7)
 };
 
 struct HeaderParams {
@@ -483,6 +494,34 @@ __device__ __forceinline__ uint32_t enc_tile_words(uint64_t t0, const EncParams 
     return (uint32_t)((p.n - t0 < (uint64_t)kEncTile) ? p.n - t0 : (uint64_t)kEncTile);
 }
 
+// Bit b (b = 0..2) of the 3-bit codes of 8 words (code bytes of words 0..3
+// in L0, 4..7 in L1), gathered into byte b of the result: bit j of byte b is
+// bit b of word j's code. The two code fields of byte i of m8 (word i in bits
+// 0..2, word 4 + i in bits 4..6) put bit b of word i at 8i and of word 4 + i
+// at 8i + 4; one multiply by 2^24 + 2^17 + 2^10 + 2^3 moves word j to bit
+// 24 + j, and no two partial products meet, so nothing carries.
+__device__ __forceinline__ uint32_t plane_bytes8(uint32_t L0, uint32_t L1)
+{
+    const uint32_t m8 = (L0 & 0x07070707u) | ((L1 & 0x07070707u) << 4);
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 3; b++) v |= ((((m8 >> b) & 0x11111111u) * 0x01020408u) >> 24) << (8 * b);
+    return v;
+}
+
+// Quad transpose of plane bytes: lane q of each group of 4 lanes (q < 3)
+// returns the dword of plane q made of byte q of the 4 lanes' v, lane 0's
+// byte lowest (DPP quad broadcasts, then two byte permutes).
+__device__ __forceinline__ uint32_t quad_planes(uint32_t v, uint32_t q)
+{
+    const uint32_t a0 = __builtin_amdgcn_update_dpp(0u, v, 0x00, 0xF, 0xF, false);   // quad_perm [0,0,0,0]
+    const uint32_t a1 = __builtin_amdgcn_update_dpp(0u, v, 0x55, 0xF, 0xF, false);   // quad_perm [1,1,1,1]
+    const uint32_t a2 = __builtin_amdgcn_update_dpp(0u, v, 0xAA, 0xF, 0xF, false);   // quad_perm [2,2,2,2]
+    const uint32_t a3 = __builtin_amdgcn_update_dpp(0u, v, 0xFF, 0xF, 0xF, false);   // quad_perm [3,3,3,3]
+    const uint32_t sel = 0x0C0C0000u | ((4u + q) << 8) | q;
+    return perm(a1, a0, sel) | (perm(a3, a2, sel) << 16);
+}
+
 // Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
 // holds kEncGroups groups of 8 words (group k covers tile words
 // k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
@@ -490,7 +529,10 @@ __device__ __forceinline__ uint32_t enc_tile_words(uint64_t t0, const EncParams 
 // tile's escapes in element order in LDS (eb). Returns the tile's escape
 // count m (the same in every thread). cstart[k] is the number of the tile's
 // escapes before group k when group k starts a chunk, else ~0u. Ends without
-// a barrier after the LDS writes of eb.
+// a barrier after the LDS writes of eb. kPlanes: the codes are 3-bit (lut
+// bits 0..2) and go to three bit planes (p.plane bytes apart) instead of
+// nibbles; every thread of the workgroup must take part (quad exchanges).
+template <bool kPlanes = false>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
                                                       EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
@@ -521,7 +563,8 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         Lw[k][1] = L1;
         sm[k][0] = signmant4(xw[k][0], xw[k][1]);
         sm[k][1] = signmant4(xw[k][2], xw[k][3]);
-        cw[k] = pack_codes8(L0, L1);
+        if constexpr (kPlanes) cw[k] = quad_planes(plane_bytes8(L0, L1), (uint32_t)(lane & 3));
+        else cw[k] = pack_codes8(L0, L1);
     }
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
@@ -531,7 +574,15 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
             smv.x = sm[k][0];
             smv.y = sm[k][1];
             st_stream(smv, reinterpret_cast<u32x2 *>(smt + lo));
-            st_stream(cw[k], reinterpret_cast<uint32_t *>(cdt + lo / 2));
+            if constexpr (!kPlanes) st_stream(cw[k], reinterpret_cast<uint32_t *>(cdt + lo / 2));
+        }
+        if constexpr (kPlanes) {
+            // lane q < 3 of a quad stores the quad's dword of plane q (its
+            // bytes are the 4 lanes' 8-word groups); a quad whose first group
+            // is past the end stores nothing
+            const uint32_t q = (uint32_t)(lane & 3), lq = lo - 8 * q;
+            if (q < 3 && lq < rem)
+                st_stream(cw[k], reinterpret_cast<uint32_t *>(out + p.off_codes + q * p.plane + t0 / 8 + lq / 8));
         }
     }
     // escape count of each group -> exclusive prefix over the wave's lanes
@@ -615,8 +666,9 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
     for (uint32_t q = tid; q < (m + 15) / 16; q += kEncThreads) sv[q] = lv[q];
 }
 
-__global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__restrict__ x,
-                                                             uint8_t *__restrict__ out, EncWs ws, EncParams p)
+template <bool kPlanes>
+__device__ __forceinline__ void encode_tile(const uint16_t *__restrict__ x, uint8_t *__restrict__ out,
+                                            const EncWs &ws, const EncParams &p)
 {
     __shared__ EncShared sh;
     __shared__ EscBuf eb;
@@ -643,8 +695,22 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
     // the code table goes to LDS after the data loads are in flight
     if (p.dlut) load_wave_lut(sh, p.dlut); else load_wave_lut(sh, p.lut);
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank(xw, t0, rem, out, p, sh, eb, cstart);
+    const uint32_t m = encode_dense_rank<kPlanes>(xw, t0, rem, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
+}
+
+__global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__restrict__ x,
+                                                             uint8_t *__restrict__ out, EncWs ws, EncParams p)
+{
+    encode_tile<false>(x, out, ws, p);
+}
+
+// Top-7 3-bit + zero-point streams: the same pass with the codes written as
+// three bit planes.
+__global__ __launch_bounds__(kEncThreads) void kz_encode_tile(const uint16_t *__restrict__ x,
+                                                              uint8_t *__restrict__ out, EncWs ws, EncParams p)
+{
+    encode_tile<true>(x, out, ws, p);
 }
 
 // One workgroup per group of 2^gshift tiles: gsum[g] = escapes in the group,
@@ -929,8 +995,10 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     for (int i = lane; i < 256; i += 64) {
         const uint64_t sm_end = kHeader + p.sm_bytes;
         if (sm_end + i < p.off_codes) out[sm_end + i] = 0;
-        const uint64_t codes_end = p.off_codes + (p.n + 1) / 2;
-        if (codes_end + i < p.off_offs) out[codes_end + i] = 0;
+        for (uint32_t b = 0; b < p.nplanes; b++) {
+            const uint64_t codes_end = p.off_codes + b * p.plane + p.code_bytes;
+            if (codes_end + i < p.off_codes + (b + 1) * p.plane) out[codes_end + i] = 0;
+        }
         const uint64_t offs_end = p.off_offs + 4 * (p.nch + 1);
         if (offs_end + i < p.off_pos) out[offs_end + i] = 0;
         const uint64_t pos_end = p.off_pos + p.posw * M;
@@ -1734,6 +1802,146 @@ __global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uin
     }
 }
 
+// ============================================ Top-7 3-bit + zero-point ====
+// "ZipCCL" exponent coding: codes 1..7 name the seven most frequent
+// exponents (dec[0..6]); code 0 is a zero-point, whose exponent is the next
+// stored one of its chunk. The codes sit in three bit planes. A tile (C <=
+// tile: its chunks start inside it) loads M, its chunk offsets, 16
+// sign-mantissa bytes and 16 bits of each plane per 16 words, and its run of
+// stored exponents into LDS. A 256-entry LDS table spreads a plane byte (8
+// words) over 8 bytes, one bit each; three lookups give 8 code bytes, and one
+// byte permute of the 8-entry table [0, dec0..dec6] turns 4 codes into 4
+// exponents. Zero-points (no bit set in any plane) are ranked like sentinels,
+// with wave scans, and take their exponents from LDS before the merge.
+constexpr int kZ7Threads = 128;
+constexpr int kZ7Groups = 2;               // groups of 16 words per thread
+constexpr int kZ7Tile = kZ7Threads * kZ7Groups * 16;
+
+// Bit j of the nibble b to bit 0 of byte j.
+__device__ __forceinline__ uint32_t spread4(uint32_t b) { return (b * 0x00204081u) & 0x01010101u; }
+
+__global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+{
+    __shared__ uint32_t zv32[kZ7Tile / 4 + 1];     // the tile's stored exponents, from a 4-byte boundary
+    __shared__ u32x2 spread[256];                   // byte j of spread[b] = bit j of b
+    __shared__ uint32_t wtot[kZ7Groups][kZ7Threads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kZ7Tile;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kZ7Tile) ? p.n - t0 : (uint64_t)kZ7Tile);
+    // round 1: M, the tile's chunk offsets, the dense bytes
+    const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
+    const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs) + (t0 >> p.logC);
+    const uint32_t nc = (uint32_t)(((t0 + rem - 1) >> p.logC) - (t0 >> p.logC) + 1);
+    const uint32_t o0 = offs[0], o1 = offs[nc];
+    const uint8_t *smt = s.base + kHeader + t0;
+    const uint8_t *plt = s.base + p.off_codes + t0 / 8;
+    u32x4 sm[kZ7Groups];
+    uint32_t pb[kZ7Groups][3];
+#pragma unroll
+    for (int k = 0; k < kZ7Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kZ7Threads * 16) + tid * 16);
+        sm[k] = u32x4{0u, 0u, 0u, 0u};
+        pb[k][0] = pb[k][1] = pb[k][2] = 0u;
+        if (lo < rem) {
+            sm[k] = ld_stream(reinterpret_cast<const u32x4 *>(smt + lo));
+#pragma unroll
+            for (int b = 0; b < 3; b++)
+                pb[k][b] = ld_stream(reinterpret_cast<const uint16_t *>(plt + b * p.plane + lo / 8));
+        }
+    }
+    for (int b = tid; b < 256; b += kZ7Threads) spread[b] = u32x2{spread4(b & 0xF), spread4(b >> 4)};
+    // the tile's stored exponents: [E0, E1), clamped so that a corrupt stream
+    // reads inside the buffer; whole dwords, then the last partial one
+    const bool okM = M <= p.n && p.off_pos + M <= s.bytes;
+    uint32_t E1 = okM ? (o1 < (uint32_t)M ? o1 : (uint32_t)M) : 0u;
+    uint32_t E0 = o0 < E1 ? o0 : E1;
+    if (E1 - E0 > rem) E1 = E0 + rem;
+    const uint32_t a0 = E0 & ~3u;
+    const uint8_t *val = s.base + p.off_pos;
+    const uint32_t nfull = (E1 - a0) / 4;
+    for (uint32_t w = tid; w < nfull; w += kZ7Threads) zv32[w] = *reinterpret_cast<const uint32_t *>(val + a0 + 4 * w);
+    if (tid == kZ7Threads - 1 && ((E1 - a0) & 3u)) {
+        uint32_t t = 0;
+        for (uint32_t i = a0 + 4 * nfull; i < E1; i++) t |= (uint32_t)val[i] << (8 * (i - a0 - 4 * nfull));
+        zv32[nfull] = t;
+    }
+    // zero-points: no bit in any plane, one flag per word
+    uint32_t z[kZ7Groups], pre[kZ7Groups];
+#pragma unroll
+    for (int k = 0; k < kZ7Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kZ7Threads * 16) + tid * 16);
+        uint32_t t = ~(pb[k][0] | pb[k][1] | pb[k][2]) & 0xFFFFu;
+        if (lo + 16 > rem) t = lo < rem ? t & ((1u << (rem - lo)) - 1u) : 0u;
+        z[k] = t;
+        const uint32_t c = __builtin_popcount(t);
+        uint32_t pr = 0, wt = 0;
+        if (__ballot(c != 0) != 0ull) {
+            const uint32_t inc = wave_inclusive_sum(c);
+            pr = inc - c;
+            wt = __builtin_amdgcn_readlane(inc, 63);
+        }
+        pre[k] = pr;
+        if (lane == 0) wtot[k][wave] = wt;
+    }
+    __syncthreads();
+    const uint32_t T0 = p.dec[0] << 8;                           // [0, dec0, dec1, dec2]
+    const uint32_t T1 = (p.dec[0] >> 24) | (p.dec[1] << 8);      // [dec3 .. dec6]
+    const uint8_t *zb = reinterpret_cast<const uint8_t *>(zv32);
+    uint16_t *yt = y + t0;
+    uint32_t run = 0;
+#pragma unroll
+    for (int k = 0; k < kZ7Groups; k++) {
+        uint32_t base = run;
+#pragma unroll
+        for (int w = 0; w < kZ7Threads / 64; w++) {
+            if (w < wave) base += wtot[k][w];
+            run += wtot[k][w];
+        }
+        // exponents of words 4q..4q+3 in e[q]
+        uint32_t e[4];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const u32x2 s0 = spread[(pb[k][0] >> (8 * h)) & 0xFFu];
+            const u32x2 s1 = spread[(pb[k][1] >> (8 * h)) & 0xFFu];
+            const u32x2 s2 = spread[(pb[k][2] >> (8 * h)) & 0xFFu];
+            e[2 * h] = perm(T1, T0, s0.x | (s1.x << 1) | (s2.x << 2));
+            e[2 * h + 1] = perm(T1, T0, s0.y | (s1.y << 1) | (s2.y << 2));
+        }
+        if (__ballot(z[k] != 0) != 0ull) {
+            // word j's stored exponent (if it is a zero-point) is at rank
+            // r + (zero-points before j); every word reads one, in bounds
+            const uint32_t r = base + pre[k] + (E0 & 3u);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t pd = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int j = 4 * q + i;
+                    const uint32_t rj = r + __builtin_popcount(z[k] & ((1u << j) - 1u));
+                    pd |= (uint32_t)zb[rj] << (8 * i);
+                }
+                const uint32_t mask = perm(0u, 0u, 0x0C0C0C0Cu + spread4((z[k] >> (4 * q)) & 0xFu));
+                e[q] = bfi(mask, pd, e[q]);
+            }
+        }
+        const uint32_t smq[4] = {sm[k].x, sm[k].y, sm[k].z, sm[k].w};
+        uint32_t out[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            out[2 * q] = merge2(perm(e[q], smq[q], 0x05010400u));
+            out[2 * q + 1] = merge2(perm(e[q], smq[q], 0x07030602u));
+        }
+        const uint32_t lo = (uint32_t)(k * (kZ7Threads * 16) + tid * 16);
+        if (lo + 16 <= rem) {
+            st_stream(u32x4{out[0], out[1], out[2], out[3]}, reinterpret_cast<u32x4 *>(yt + lo));
+            st_stream(u32x4{out[4], out[5], out[6], out[7]}, reinterpret_cast<u32x4 *>(yt + lo + 8));
+        } else if (lo < rem) {
+            for (uint32_t j = 0; j < 16 && lo + j < rem; j++)
+                yt[lo + j] = (uint16_t)(out[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 // ================================================================ host ====
 thread_local char g_hip_err[160];
 
@@ -1804,7 +2012,10 @@ EncParams make_enc_params(const Layout &L, const uzip_codebook_t *cb)
     p.dlut = nullptr;
     p.ddec = nullptr;
     p.sm_bytes = sm_bytes_of(L.n, L.fmt == kFmtFP8);
-    p.posw = L.fmt == kFmtS15 ? 0 : 2;
+    p.code_bytes = L.code_bytes;
+    p.plane = L.plane;
+    p.nplanes = L.nplanes;
+    p.posw = has_pos(L.fmt) ? 2 : 0;
     return p;
 }
 
@@ -1819,6 +2030,7 @@ DecParams make_dec_params(const Layout &L, const uzip_codebook_t *cb)
     p.off_codes = L.off_codes;
     p.off_offs = L.off_offs;
     p.off_pos = L.off_pos;
+    p.plane = L.plane;
     return p;
 }
 
@@ -1829,7 +2041,7 @@ HeaderParams make_header_params(const Layout &L, const uzip_codebook_t *cb)
     h.tmpl[0] = 0x55; h.tmpl[1] = 0x5A; h.tmpl[2] = 0x42; h.tmpl[3] = 0x31;
     const uint16_t ver = 1;
     memcpy(h.tmpl + 4, &ver, 2);
-    h.tmpl[6] = L.fmt;                        // format: 0 BF16, 1 FP8 E5M2, 2 BF16 Top-15 + sentinel
+    h.tmpl[6] = L.fmt;                        // format: 0 BF16, 1 FP8 E5M2, 2 Top-15 + sentinel, 3 Top-7 + zero-point
     memcpy(h.tmpl + 8, &L.C, 4);
     memcpy(h.tmpl + 16, &L.n, 8);
     memcpy(h.tmpl + 40, cb->dec, 16);
@@ -1994,13 +2206,14 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     uint32_t C;
     uint8_t dec[16];
     if (uzip_parse_header(s, &n, &C, &m, &total, dec) != UZIP_OK) return UZIP_ECORRUPT;
-    const uint16_t fmt = rd16(s + 6);                  // 0 BF16, 1 FP8 E5M2, 2 BF16 Top-15 + sentinel
-    if (fmt > 2 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
-    const bool fp8 = fmt == kFmtFP8, s15 = fmt == kFmtS15;
+    const uint16_t fmt = rd16(s + 6);       // 0 BF16, 1 FP8 E5M2, 2 Top-15 + sentinel, 3 Top-7 + zero-point
+    if (fmt > 3 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    const bool fp8 = fmt == kFmtFP8, s15 = fmt == kFmtS15, z7 = fmt == kFmtZ7;
     for (uint64_t i = 56; i < kHeader; i++)
         if (s[i]) return UZIP_ECORRUPT;
     if (!valid_nc(n, C) || m > n) return UZIP_ECORRUPT;
     if (s15 && C > (uint32_t)kS15Tile) return UZIP_ECORRUPT;
+    if (z7 && C > (uint32_t)kZ7Tile) return UZIP_ECORRUPT;
     const Layout L = make_layout(n, C, (uint8_t)fmt);
     const uint64_t off_val = off_val_of(L, m);
     if (total != off_val + m || bytes < total) return UZIP_ECORRUPT;
@@ -2009,23 +2222,43 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     for (int k = 0; k < 16; k++) {
         if (seen[dec[k]] || (fp8 && dec[k] > 31)) return UZIP_ECORRUPT;
         seen[dec[k]] = true;
-        in_book[dec[k]] = !s15 || k < 15;              // Top-15 + sentinel uses dec[0..14]
+        in_book[dec[k]] = z7 ? k < 7 : (!s15 || k < 15);   // Top-15 uses dec[0..14], Top-7 dec[0..6]
     }
     auto zero = [&](uint64_t a, uint64_t b) {
         for (uint64_t i = a; i < b; i++)
             if (s[i]) return false;
         return true;
     };
-    const uint64_t codes_bytes = (n + 1) / 2;
     const uint64_t smb = sm_bytes_of(n, fp8);
     if (!zero(kHeader + smb, L.off_codes)) return UZIP_ECORRUPT;
     if (fp8 && (3 * n) % 8 && (s[kHeader + smb - 1] >> ((3 * n) % 8))) return UZIP_ECORRUPT;   // unused bits
-    if ((n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
-    if (!zero(L.off_codes + codes_bytes, L.off_offs)) return UZIP_ECORRUPT;
+    if (!z7 && (n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
+    for (uint32_t b = 0; b < L.nplanes; b++) {
+        const uint64_t pl = L.off_codes + b * L.plane;
+        if (z7 && (n & 7) && (s[pl + n / 8] >> (n & 7))) return UZIP_ECORRUPT;     // plane bits past n
+        if (!zero(pl + L.code_bytes, pl + L.plane)) return UZIP_ECORRUPT;
+    }
     if (!zero(L.off_offs + 4 * (L.nch + 1), L.off_pos)) return UZIP_ECORRUPT;
-    if (!s15 && !zero(L.off_pos + 2 * m, off_val)) return UZIP_ECORRUPT;
+    if (has_pos(L.fmt) && !zero(L.off_pos + 2 * m, off_val)) return UZIP_ECORRUPT;
     const uint8_t *offs = s + L.off_offs;
     if (rd32(offs) != 0 || rd32(offs + 4 * L.nch) != m) return UZIP_ECORRUPT;
+    if (z7) {
+        // each chunk: as many stored exponents as zero-points (code 0), all outside dec[0..6]
+        for (uint64_t c = 0; c < L.nch; c++) {
+            const uint64_t j0 = rd32(offs + 4 * c), j1 = rd32(offs + 4 * (c + 1));
+            const uint64_t lo = c * C, hi = (lo + C < n) ? lo + C : n;
+            uint64_t zeros = 0;
+            for (uint64_t i = lo; i < hi; i++) {
+                uint32_t code = 0;
+                for (uint32_t b = 0; b < 3; b++) code |= ((s[L.off_codes + b * L.plane + i / 8] >> (i & 7)) & 1u) << b;
+                zeros += code == 0;
+            }
+            if (j1 < j0 || j1 > m || j1 - j0 != zeros) return UZIP_ECORRUPT;
+            for (uint64_t j = j0; j < j1; j++)
+                if (in_book[s[off_val + j]]) return UZIP_ECORRUPT;
+        }
+        return UZIP_OK;
+    }
     if (s15) {
         // each chunk: as many stored exponents as sentinels (code 15), all outside dec[0..14]
         for (uint64_t c = 0; c < L.nch; c++) {
@@ -2223,6 +2456,65 @@ int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t ch
                     uint16_t *d_y, hipStream_t s)
 {
     return uzip_s15_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
+}
+
+uint64_t uzip_z7_max_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kZ7Tile) return 0;
+    return total_of(make_layout(n, chunk, kFmtZ7), n);
+}
+
+int uzip_z7_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                      const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kZ7Tile) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_z7_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk, kFmtZ7);
+    EncParams ep = make_enc_params(L, cb);
+    for (int e = 0; e < 256; e++) ep.lut[e] = 0x80;       // zero-point: code 0, escape flag
+    for (int k = 0; k < 7; k++) ep.lut[cb->dec[k]] = (uint8_t)(k + 1);
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    kz_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("kz_encode_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_z7_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_z7_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_z7_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !d_y || !aligned16(d_in) || !aligned16(d_y)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk) || chunk > (uint32_t)kZ7Tile) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    const Layout L = make_layout(n, chunk, kFmtZ7);
+    if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;
+    const DecParams dp = make_dec_params(L, cb);
+    const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    const uint64_t tiles = (n + kZ7Tile - 1) / kZ7Tile;
+    kz_decode_tile<<<(unsigned)tiles, kZ7Threads, 0, s>>>(si, d_y, dp);
+    UZIP_LAUNCH_CHECK("kz_decode_tile");
+    return ev.record(1);
+}
+
+int uzip_z7_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   uint16_t *d_y, hipStream_t s)
+{
+    return uzip_z7_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
 }
 
 uint64_t uzip_fp8_max_bytes(uint64_t n, uint32_t chunk)

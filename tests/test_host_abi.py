@@ -171,6 +171,37 @@ def test_validate_host_s15_streams():
     assert uzip.validate_host(bad.tobytes(), cb) == -3
 
 
+@pytest.mark.parametrize("n,C", [(1, 64), (1001, 256), (65536, 1024), (70001, 4096)])
+def test_z7_max_bytes_matches_oracle(n, C):
+    assert uzip.z7_max_bytes(n, C) == oracle.z7_max_bytes(n, C)
+    assert uzip.z7_max_bytes(n, 8192) == 0                 # chunk above the decode tile
+
+
+def test_validate_host_z7_streams():
+    w = workloads.config(1)
+    x = w.x[:30001].copy()
+    ocb = oracle.calibrate(w.calib)
+    cb = uzip.codebook_from_hist(ocb.hist)
+    s = oracle.z7_encode(x, 256, ocb.dec)
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    A = lambda v: (v + 255) // 256 * 256
+    codes, P = 256 + A(x.size), A((x.size + 7) // 8)
+    planes = [np.unpackbits(s[codes + b * P:codes + b * P + (x.size + 7) // 8], bitorder="little")[:x.size]
+              for b in range(3)]
+    code = planes[0] | (planes[1] << 1) | (planes[2] << 2)
+    i = int(np.nonzero(code == 0)[0][0])
+    bad = s.copy(); bad[codes + P + i // 8] |= 1 << (i % 8)       # a zero-point becomes code 2
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[codes + x.size // 8] |= 0x80                # plane 0 bit past n
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[codes + 2 * P + P - 1] = 1                  # plane 2 padding
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[s.size - 1] = ocb.dec[6]                     # a stored exponent among the seven
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[6] = 4
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+
+
 def test_strerror_texts():
     L = uzip.lib()
     for code in (0, -1, -2, -3, -4, -5, 7):
@@ -229,6 +260,14 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_s15_encode(p, 1000, 8192, cbr, p, big, p, ws, None) == -1       # chunk above 4096
     assert L.uzip_s15_encode(p, 1000, 1024, cbr, p, s15b - 1, p, ws, None) == -2
     assert L.uzip_s15_decode(p, 10, 1000, 1024, cbr, p, None) == -1
+    z7b = uzip.z7_max_bytes(1000, 1024)
+    assert L.uzip_z7_encode(p, 1000, 8192, cbr, p, big, p, ws, None) == -1        # chunk above 4096
+    assert L.uzip_z7_encode(mis, 1000, 1024, cbr, p, z7b, p, ws, None) == -1
+    assert L.uzip_z7_encode(p, 1000, 1024, cbr, p, z7b - 1, p, ws, None) == -2
+    assert L.uzip_z7_encode(p, 1000, 1024, cbr, p, z7b, p, ws - 1, None) == -2
+    assert L.uzip_z7_decode(p, 10, 1000, 1024, cbr, p, None) == -1                # in_bytes too small
+    assert L.uzip_z7_decode(p, z7b, 1000, 1024, cbr, mis, None) == -1
+    assert L.uzip_z7_decode(p, z7b, 1000, 8192, cbr, p, None) == -1
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1
