@@ -246,6 +246,14 @@ __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b)
     return (a & mask) | (b & ~mask);
 }
 
+// Bit j of the nibble b to bit 0 of byte j (the four shifted copies of b
+// that the multiply adds occupy disjoint bits, so nothing carries).
+__device__ __forceinline__ uint32_t spread4(uint32_t b) { return (b * 0x00204081u) & 0x01010101u; }
+
+// 0xFF in byte j where bit j of the nibble b is set, else 0 (byte permute
+// selectors 12 and 13 give 0x00 and 0xFF).
+__device__ __forceinline__ uint32_t bytemask4(uint32_t b) { return perm(0u, 0u, 0x0C0C0C0Cu + spread4(b)); }
+
 // Sign-mantissa bytes of 4 words held in two dwords (word 2i in the low half).
 __device__ __forceinline__ uint32_t signmant4(uint32_t v0, uint32_t v1)
 {
@@ -296,30 +304,51 @@ __device__ __forceinline__ uint32_t merge2(uint32_t w)
     return bfi(0x7F807F80u, w >> 1, t);
 }
 
+// Exponents of 8 words from their 8 code nibbles, one per byte: e[0] holds
+// words 0..3, e[1] words 4..7.
+__device__ __forceinline__ void decode8_e(uint32_t codes, const uint32_t dec[4], uint32_t e[2])
+{
+    const uint32_t lo = codes & 0x0F0F0F0Fu;          // nibbles of words 0,2,4,6
+    const uint32_t hi = (codes >> 4) & 0x0F0F0F0Fu;   // nibbles of words 1,3,5,7
+    e[0] = dec4(dec, perm(hi, lo, 0x05010400u));      // [c0, c1, c2, c3]
+    e[1] = dec4(dec, perm(hi, lo, 0x07030602u));      // [c4, c5, c6, c7]
+}
+
+// 8 words from their sign-mantissa bytes (2 dwords) and exponents (e[2]).
+__device__ __forceinline__ void merge8(uint32_t sm0, uint32_t sm1, const uint32_t e[2], uint32_t y[4])
+{
+    y[0] = merge2(perm(e[0], sm0, 0x05010400u));
+    y[1] = merge2(perm(e[0], sm0, 0x07030602u));
+    y[2] = merge2(perm(e[1], sm1, 0x05010400u));
+    y[3] = merge2(perm(e[1], sm1, 0x07030602u));
+}
+
 // Decode 8 words: sm (8 sign-mantissa bytes in 2 dwords), codes (8 nibbles).
 __device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t codes,
                                         const uint32_t dec[4], uint32_t y[4])
 {
-    uint32_t lo = codes & 0x0F0F0F0Fu;          // nibbles of words 0,2,4,6
-    uint32_t hi = (codes >> 4) & 0x0F0F0F0Fu;   // nibbles of words 1,3,5,7
-    uint32_t n03 = perm(hi, lo, 0x05010400u);   // [c0, c1, c2, c3]
-    uint32_t n47 = perm(hi, lo, 0x07030602u);   // [c4, c5, c6, c7]
-    uint32_t e03 = dec4(dec, n03);
-    uint32_t e47 = dec4(dec, n47);
-    y[0] = merge2(perm(e03, sm0, 0x05010400u));
-    y[1] = merge2(perm(e03, sm0, 0x07030602u));
-    y[2] = merge2(perm(e47, sm1, 0x05010400u));
-    y[3] = merge2(perm(e47, sm1, 0x07030602u));
+    uint32_t e[2];
+    decode8_e(codes, dec, e);
+    merge8(sm0, sm1, e, y);
 }
 
-// binary32 sum -> BF16 in the high half, round half to even (a carry out
-// of the mantissa rounds up into the exponent, up to infinity); NaN ->
-// 0x7FC0. The low half is left over.
-__device__ __forceinline__ uint32_t bf16_rne_hi(float s)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values rounded to BF16, s0 in the low half, NaN -> 0x7FC0.
+// Rounding is half to even on the bit pattern: add 0x7FFF plus the lowest
+// kept bit, keep the high 16 bits (a carry out of the mantissa rounds up
+// into the exponent, up to infinity). One v_cvt_pk_bf16_f32 does exactly
+// that for every non-NaN binary32 pattern (checked on MI355X over all 2^32
+// patterns in both halves) but keeps a NaN's payload, so NaNs are fixed
+// after it.
+__device__ __forceinline__ uint32_t bf16x2_rne(float s0, float s1)
 {
-    const uint32_t u = __float_as_uint(s);
-    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
-    return (s != s) ? 0x7FC00000u : r;
+    const f32x2 v = {s0, s1};
+    uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    if (s0 != s0) r = (r & 0xFFFF0000u) | 0x7FC0u;
+    if (s1 != s1) r = (r & 0x0000FFFFu) | 0x7FC00000u;
+    return r;
 }
 
 // Sum of the two BF16 words in each half of a and b: binary32 add, then
@@ -328,7 +357,7 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
 {
     const float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
     const float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
-    return perm(bf16_rne_hi(a1 + b1), bf16_rne_hi(a0 + b0), 0x07060302u);
+    return bf16x2_rne(a0 + b0, a1 + b1);
 }
 
 
@@ -1197,25 +1226,19 @@ __device__ bool patch_build(const StreamIn &s, uint64_t t0, const DecParams &p, 
     return true;
 }
 
-// Apply the patch map to the 8 words of a thread's group starting at tile
-// word li0 (a multiple of 8; y holds 4 dwords, word 2q in the low half of
-// y[q]). The group's 8 exponent bytes come in one LDS read; each dword takes
-// its two new exponent fields through one byte permute and one bitfield
-// insert under a mask built from the group's 2 patch bits.
+// Apply the patch map to the exponents of the 8 words of a thread's group
+// starting at tile word li0 (a multiple of 8; e[0] holds words 0..3 and e[1]
+// words 4..7, one exponent per byte), before they are merged. The group's 8
+// recorded exponents come in one LDS read, and each dword takes its patched
+// bytes through one bitfield insert under a byte mask.
 template <int TILE>
-__device__ __forceinline__ void apply_patch8(const PatchShared<TILE> &sh, uint32_t li0, uint32_t y[4])
+__device__ __forceinline__ void apply_patch8e(const PatchShared<TILE> &sh, uint32_t li0, uint32_t e[2])
 {
     const uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & 0xFFu;
     if (bits == 0) return;
     const u32x2 v = *reinterpret_cast<const u32x2 *>(&sh.val[li0]);
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const uint32_t t = (bits >> (2 * q)) & 3u;                 // patch bits of words 2q, 2q+1
-        const uint32_t m = (((t * 0x8001u) & 0x10001u) * 0x7F80u);  // their exponent fields
-        const uint32_t src = (q < 2) ? v.x : v.y;
-        const uint32_t e2 = perm(0u, src, (q & 1) ? 0x0C030C02u : 0x0C010C00u) << 7;
-        y[q] = bfi(m, e2, y[q]);
-    }
+    e[0] = bfi(bytemask4(bits & 0xFu), v.x, e[0]);
+    e[1] = bfi(bytemask4(bits >> 4), v.y, e[1]);
 }
 
 template <bool kPatch>
@@ -1249,28 +1272,30 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_
     }
     PatchFetch<kDecFetch> pf;
     if (kPatch) pf = patch_fetch<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph);
-    uint32_t out[kG][4];
+    uint32_t ex[kG][2];
 #pragma unroll
     for (int k = 0; k < kG; k++) {
         const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
-        if (lo < rem) decode8(sm[k].x, sm[k].y, cd[k], dec, out[k]);
+        if (lo < rem) decode8_e(cd[k], dec, ex[k]);
     }
     if (kPatch) {
         if (patch_build<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) {
 #pragma unroll
             for (int k = 0; k < kG; k++)
-                apply_patch8(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), out[k]);
+                apply_patch8e(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), ex[k]);
         }
     }
 #pragma unroll
     for (int k = 0; k < kG; k++) {
         const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+        uint32_t out[4];
+        if (lo < rem) merge8(sm[k].x, sm[k].y, ex[k], out);
         if (lo + 8 <= rem) {
-            u32x4 v = {out[k][0], out[k][1], out[k][2], out[k][3]};
+            u32x4 v = {out[0], out[1], out[2], out[3]};
             st_stream(v, reinterpret_cast<u32x4 *>(yt + lo));
         } else if (lo < rem) {
             for (uint32_t j = 0; j < 8 && lo + j < rem; j++)
-                yt[lo + j] = (uint16_t)(out[k][j >> 1] >> (16 * (j & 1)));
+                yt[lo + j] = (uint16_t)(out[j >> 1] >> (16 * (j & 1)));
         }
     }
 }
@@ -1336,16 +1361,17 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     }
     const PatchFetch<kRedFetch> fa = patch_fetch<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha);
     const PatchFetch<kRedFetch> fb = patch_fetch<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb);
-    uint32_t ya[kEncGroups][4], yb[kEncGroups][4];
+    // exponents of both inputs; groups past the end decode to the word 0
+    uint32_t ea[kEncGroups][2], eb[kEncGroups][2];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         if (lo < rem) {
-            decode8(sma[k].x, sma[k].y, cda[k], dec, ya[k]);
-            decode8(smb[k].x, smb[k].y, cdb[k], dec, yb[k]);
+            decode8_e(cda[k], dec, ea[k]);
+            decode8_e(cdb[k], dec, eb[k]);
         } else {
-#pragma unroll
-            for (int q = 0; q < 4; q++) ya[k][q] = yb[k][q] = 0;
+            sma[k] = smb[k] = u32x2{0u, 0u};
+            ea[k][0] = ea[k][1] = eb[k][0] = eb[k][1] = 0u;
         }
     }
     // the code table goes to LDS after the data loads are in flight
@@ -1353,19 +1379,23 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     if (patch_build<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha, fa, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ya[k]);
+            apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ea[k]);
     }
     __syncthreads();       // the map is rebuilt for the second input
     if (patch_build<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb, fb, lds.patch)) {
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++)
-            apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), yb[k]);
+            apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), eb[k]);
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++)
+    for (int k = 0; k < kEncGroups; k++) {
+        uint32_t ya[4], yb[4];
+        merge8(sma[k].x, sma[k].y, ea[k], ya);
+        merge8(smb[k].x, smb[k].y, eb[k], yb);
 #pragma unroll
-        for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[k][q], yb[k][q]);
+        for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[q], yb[q]);
+    }
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
@@ -1433,22 +1463,25 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
             hn = patch_begin<kEncTile, kEncThreads>(ss.in[i + 1], t0, dp);
             load_dense(ss.in[i + 1], t0, rem, dp, nxt);
         }
-        uint32_t y[kEncGroups][4];
+        uint32_t ex[kEncGroups][2];
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) decode8(cur.sm[k].x, cur.sm[k].y, cur.cd[k], dec, y[k]);
+        for (int k = 0; k < kEncGroups; k++) decode8_e(cur.cd[k], dec, ex[k]);
         if (patch_build<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h, f, lds.patch)) {
 #pragma unroll
             for (int k = 0; k < kEncGroups; k++)
-                apply_patch8(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), y[k]);
+                apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
         }
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++)
+        for (int k = 0; k < kEncGroups; k++) {
+            uint32_t y[4];
+            merge8(cur.sm[k].x, cur.sm[k].y, ex[k], y);
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const float v0 = __uint_as_float(y[k][q] << 16), v1 = __uint_as_float(y[k][q] & 0xFFFF0000u);
+                const float v0 = __uint_as_float(y[q] << 16), v1 = __uint_as_float(y[q] & 0xFFFF0000u);
                 acc[k][2 * q] = (i == 0) ? v0 : acc[k][2 * q] + v0;
                 acc[k][2 * q + 1] = (i == 0) ? v1 : acc[k][2 * q + 1] + v1;
             }
+        }
         __syncthreads();       // the map is rebuilt for the next input
         h = hn;
         cur = nxt;
@@ -1459,8 +1492,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
 #pragma unroll
         for (int q = 0; q < 4; q++)
-            r[k][q] = (lo < rem) ? perm(bf16_rne_hi(acc[k][2 * q + 1]), bf16_rne_hi(acc[k][2 * q]), 0x07060302u)
-                                 : 0u;
+            r[k][q] = (lo < rem) ? bf16x2_rne(acc[k][2 * q], acc[k][2 * q + 1]) : 0u;
     }
     uint32_t cstart[kEncGroups];
     const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
@@ -1816,9 +1848,6 @@ __global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uin
 constexpr int kZ7Threads = 128;
 constexpr int kZ7Groups = 2;               // groups of 16 words per thread
 constexpr int kZ7Tile = kZ7Threads * kZ7Groups * 16;
-
-// Bit j of the nibble b to bit 0 of byte j.
-__device__ __forceinline__ uint32_t spread4(uint32_t b) { return (b * 0x00204081u) & 0x01010101u; }
 
 __global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
 {
