@@ -1226,6 +1226,97 @@ __device__ bool patch_build(const StreamIn &s, uint64_t t0, const DecParams &p, 
     return true;
 }
 
+// The exponent form of the patch, for BF16 tiles: each thread writes the
+// exponents it decoded (one byte per word) into an LDS copy of the tile,
+// every escape then overwrites its word's byte in place, and each thread
+// reads its bytes back before the merge. In order:
+//   the threads' exponent bytes and patch_put_offs, a barrier,
+//   patch_scatter, a barrier, the threads' reads.
+// Only for tiles with escapes (PatchFetch::live, the same in every thread).
+template <int TILE>
+struct ExpTile {
+    uint8_t ex[TILE];
+    uint32_t offs[TILE / 64 + 1];
+};
+
+template <int TILE, int FB>
+__device__ __forceinline__ void patch_put_offs(uint64_t t0, const DecParams &p, const PatchHead &h,
+                                               const PatchFetch<FB> &f, ExpTile<TILE> &sh)
+{
+    const uint32_t tid = threadIdx.x;
+    if (p.C > (uint32_t)TILE) return;
+    const uint32_t nc = (uint32_t)tile_chunks<TILE>(t0, p), E1 = f.E0 + f.cnt;
+    if (tid <= nc) sh.offs[tid] = h.mine > E1 ? E1 : h.mine;
+}
+
+// Escape j (position ps, exponent v) overwrites its word's exponent byte.
+template <int TILE>
+__device__ __forceinline__ void patch_mark_ex(ExpTile<TILE> &sh, uint64_t t0, uint32_t rem, const DecParams &p,
+                                              uint32_t nc, uint32_t j, uint32_t ps, uint32_t v)
+{
+    uint32_t li;
+    if (p.C <= (uint32_t)TILE) {
+        uint32_t a = 0, b = nc;             // offs[a] <= j < offs[b]
+        while (b - a > 1) {
+            const uint32_t mid = (a + b) >> 1;
+            if (sh.offs[mid] <= j) a = mid; else b = mid;
+        }
+        li = (a << p.logC) + ps;
+    } else {
+        li = ps - (uint32_t)(t0 & (uint64_t)(p.C - 1));   // wraps for a position before the tile
+    }
+    if (ps < p.C && li < rem) sh.ex[li] = (uint8_t)v;
+}
+
+template <int TILE, int NT, int FB>
+__device__ void patch_scatter(const StreamIn &s, uint64_t t0, const DecParams &p, const PatchHead &h,
+                              const PatchFetch<FB> &f, ExpTile<TILE> &sh)
+{
+    const int tid = threadIdx.x;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)TILE) ? p.n - t0 : (uint64_t)TILE);
+    const uint32_t nc = (p.C <= (uint32_t)TILE) ? (uint32_t)tile_chunks<TILE>(t0, p) : 0u;
+#pragma unroll
+    for (int u = 0; u < FB; u++) {
+        const uint32_t d = (uint32_t)(u * NT + tid);
+        if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, f.E0 + d, f.ps[u], f.vv[u]);
+    }
+    if (f.cnt > (uint32_t)(FB * NT)) {
+        const uint64_t M = h.M;
+        const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos) + f.E0;
+        const uint8_t *val = s.base + p.off_pos + align256(2 * M) + f.E0;
+        for (uint32_t db = FB * NT; db < f.cnt; db += 4 * NT) {
+            uint32_t ps[4], vv[4];
+            // issue the loads of 4 escapes per thread before using any of them
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t d = db + (uint32_t)(u * NT + tid);
+                ps[u] = (d < f.cnt) ? pos[d] : 0xFFFFFFFFu;
+                vv[u] = (d < f.cnt) ? val[d] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t d = db + (uint32_t)(u * NT + tid);
+                if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, f.E0 + d, ps[u], vv[u]);
+            }
+        }
+    }
+}
+
+// A thread's exponent bytes of the group at tile word li0 (a multiple of 8)
+// to and from the LDS tile.
+template <int TILE>
+__device__ __forceinline__ void ex_put8(ExpTile<TILE> &sh, uint32_t li0, const uint32_t e[2])
+{
+    *reinterpret_cast<u32x2 *>(&sh.ex[li0]) = u32x2{e[0], e[1]};
+}
+template <int TILE>
+__device__ __forceinline__ void ex_get8(const ExpTile<TILE> &sh, uint32_t li0, uint32_t e[2])
+{
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(&sh.ex[li0]);
+    e[0] = v.x;
+    e[1] = v.y;
+}
+
 // Apply the patch map to the exponents of the 8 words of a thread's group
 // starting at tile word li0 (a multiple of 8; e[0] holds words 0..3 and e[1]
 // words 4..7, one exponent per byte), before they are merged. The group's 8
@@ -1244,7 +1335,7 @@ __device__ __forceinline__ void apply_patch8e(const PatchShared<TILE> &sh, uint3
 template <bool kPatch>
 __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
 {
-    __shared__ PatchShared<kDecTile> sh;
+    __shared__ ExpTile<kDecTile> sh;
     const int tid = threadIdx.x;
     const uint64_t t0 = (uint64_t)blockIdx.x * kDecTile;
     // words of this tile (scalar), and the tile's bases: lanes index them
@@ -1278,11 +1369,20 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_tile(StreamIn s, uint16_
         const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
         if (lo < rem) decode8_e(cd[k], dec, ex[k]);
     }
-    if (kPatch) {
-        if (patch_build<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) {
+    if (kPatch && pf.live) {
 #pragma unroll
-            for (int k = 0; k < kG; k++)
-                apply_patch8e(sh, (uint32_t)(k * (kDecThreads * 8) + tid * 8), ex[k]);
+        for (int k = 0; k < kG; k++) {
+            const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+            if (lo < rem) ex_put8(sh, lo, ex[k]);
+        }
+        patch_put_offs(t0, p, ph, pf, sh);
+        __syncthreads();
+        patch_scatter<kDecTile, kDecThreads, kDecFetch>(s, t0, p, ph, pf, sh);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kG; k++) {
+            const uint32_t lo = (uint32_t)(k * (kDecThreads * 8) + tid * 8);
+            if (lo < rem) ex_get8(sh, lo, ex[k]);
         }
     }
 #pragma unroll
@@ -1326,10 +1426,13 @@ __global__ __launch_bounds__(kThreads) void k_patch(StreamIn s, uint16_t *__rest
 }
 
 // ============================================================== reduce ====
-// LDS: the patch map (used while decoding) and the escape list (used while
-// encoding) are never live at the same time.
+// LDS: the exponent tiles (used while decoding) and the escape list (used
+// while encoding) are never live at the same time.
+struct ExpTile2 {
+    ExpTile<kEncTile> a, b;
+};
 union ReduceLds {
-    PatchShared<kEncTile> patch;
+    ExpTile2 ex;
     EscBuf esc;
 };
 
@@ -1376,16 +1479,26 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
     }
     // the code table goes to LDS after the data loads are in flight
     load_wave_lut(esh, ep.lut);
-    if (patch_build<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha, fa, lds.patch)) {
+    // both inputs' escapes patched in one pass over two exponent tiles
+    if (fa.live || fb.live) {
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++)
-            apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ea[k]);
-    }
-    __syncthreads();       // the map is rebuilt for the second input
-    if (patch_build<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb, fb, lds.patch)) {
+        for (int k = 0; k < kEncGroups; k++) {
+            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            if (fa.live) ex_put8(lds.ex.a, lo, ea[k]);
+            if (fb.live) ex_put8(lds.ex.b, lo, eb[k]);
+        }
+        if (fa.live) patch_put_offs(t0, dp, ha, fa, lds.ex.a);
+        if (fb.live) patch_put_offs(t0, dp, hb, fb, lds.ex.b);
+        __syncthreads();
+        if (fa.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(sa, t0, dp, ha, fa, lds.ex.a);
+        if (fb.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(sb, t0, dp, hb, fb, lds.ex.b);
+        __syncthreads();
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++)
-            apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), eb[k]);
+        for (int k = 0; k < kEncGroups; k++) {
+            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            if (fa.live) ex_get8(lds.ex.a, lo, ea[k]);
+            if (fb.live) ex_get8(lds.ex.b, lo, eb[k]);
+        }
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
@@ -1466,10 +1579,17 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         uint32_t ex[kEncGroups][2];
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++) decode8_e(cur.cd[k], dec, ex[k]);
-        if (patch_build<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h, f, lds.patch)) {
+        if (f.live) {
+            // each thread rewrites only its own bytes here, which no thread
+            // reads after the previous input's second barrier but itself
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++)
-                apply_patch8e(lds.patch, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
+            for (int k = 0; k < kEncGroups; k++) ex_put8(lds.ex.a, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
+            patch_put_offs(t0, dp, h, f, lds.ex.a);
+            __syncthreads();
+            patch_scatter<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h, f, lds.ex.a);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kEncGroups; k++) ex_get8(lds.ex.a, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
         }
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++) {
@@ -1482,7 +1602,6 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
                 acc[k][2 * q + 1] = (i == 0) ? v1 : acc[k][2 * q + 1] + v1;
             }
         }
-        __syncthreads();       // the map is rebuilt for the next input
         h = hn;
         cur = nxt;
     }
