@@ -1234,7 +1234,7 @@ __device__ bool patch_build(const StreamIn &s, uint64_t t0, const DecParams &p, 
 //   patch_scatter, a barrier, the threads' reads.
 // Only for tiles with escapes (PatchFetch::live, the same in every thread).
 template <int TILE>
-struct ExpTile {
+struct alignas(16) ExpTile {
     uint8_t ex[TILE];
     uint32_t offs[TILE / 64 + 1];
 };
@@ -1250,16 +1250,28 @@ __device__ __forceinline__ void patch_put_offs(uint64_t t0, const DecParams &p, 
 }
 
 // Escape j (position ps, exponent v) overwrites its word's exponent byte.
+// Its chunk in the tile is the number of chunk offsets 1..nc-1 at or below
+// j: counted against the offsets held in scalar registers (S, unused entries
+// ~0) when the tile has at most kLinChunks chunks, else found by a binary
+// search over the offsets in LDS.
+constexpr int kLinChunks = 8;
 template <int TILE>
 __device__ __forceinline__ void patch_mark_ex(ExpTile<TILE> &sh, uint64_t t0, uint32_t rem, const DecParams &p,
-                                              uint32_t nc, uint32_t j, uint32_t ps, uint32_t v)
+                                              uint32_t nc, const uint32_t S[kLinChunks - 1], uint32_t j,
+                                              uint32_t ps, uint32_t v)
 {
     uint32_t li;
     if (p.C <= (uint32_t)TILE) {
-        uint32_t a = 0, b = nc;             // offs[a] <= j < offs[b]
-        while (b - a > 1) {
-            const uint32_t mid = (a + b) >> 1;
-            if (sh.offs[mid] <= j) a = mid; else b = mid;
+        uint32_t a = 0;
+        if (nc <= (uint32_t)kLinChunks) {
+#pragma unroll
+            for (int q = 0; q < kLinChunks - 1; q++) a += (j >= S[q]) ? 1u : 0u;
+        } else {
+            uint32_t b = nc;                // offs[a] <= j < offs[b]
+            while (b - a > 1) {
+                const uint32_t mid = (a + b) >> 1;
+                if (sh.offs[mid] <= j) a = mid; else b = mid;
+            }
         }
         li = (a << p.logC) + ps;
     } else {
@@ -1275,10 +1287,23 @@ __device__ void patch_scatter(const StreamIn &s, uint64_t t0, const DecParams &p
     const int tid = threadIdx.x;
     const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)TILE) ? p.n - t0 : (uint64_t)TILE);
     const uint32_t nc = (p.C <= (uint32_t)TILE) ? (uint32_t)tile_chunks<TILE>(t0, p) : 0u;
+    // offsets 1..nc-1 to scalar registers: two 16-byte LDS reads of the
+    // same words in every lane (entries past nc are not used)
+    static_assert(TILE / 64 + 1 >= kLinChunks, "the first kLinChunks offsets fit the table");
+    uint32_t S[kLinChunks - 1];
+    {
+        const u32x4 o0 = *reinterpret_cast<const u32x4 *>(&sh.offs[0]);
+        const u32x4 o1 = *reinterpret_cast<const u32x4 *>(&sh.offs[4]);
+        const uint32_t o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int q = 0; q < kLinChunks - 1; q++)
+            S[q] = (uint32_t)(q + 1) < nc && nc <= (uint32_t)kLinChunks
+                       ? __builtin_amdgcn_readfirstlane(o[q + 1]) : 0xFFFFFFFFu;
+    }
 #pragma unroll
     for (int u = 0; u < FB; u++) {
         const uint32_t d = (uint32_t)(u * NT + tid);
-        if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, f.E0 + d, f.ps[u], f.vv[u]);
+        if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, S, f.E0 + d, f.ps[u], f.vv[u]);
     }
     if (f.cnt > (uint32_t)(FB * NT)) {
         const uint64_t M = h.M;
@@ -1296,7 +1321,7 @@ __device__ void patch_scatter(const StreamIn &s, uint64_t t0, const DecParams &p
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const uint32_t d = db + (uint32_t)(u * NT + tid);
-                if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, f.E0 + d, ps[u], vv[u]);
+                if (d < f.cnt) patch_mark_ex<TILE>(sh, t0, rem, p, nc, S, f.E0 + d, ps[u], vv[u]);
             }
         }
     }
