@@ -1826,7 +1826,8 @@ template <bool kPatch>
 __global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8_t *__restrict__ y, DecParams p)
 {
     __shared__ PatchShared<k8DecTile> sh;
-    const int tid = threadIdx.x;
+    __shared__ u32x4 xp[k8DecThreads / 64][128];     // one wave's 2 KiB of output, for contiguous stores
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t t0 = (uint64_t)blockIdx.x * k8DecTile;
     const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)k8DecTile) ? p.n - t0 : (uint64_t)k8DecTile);
     const uint32_t lo = (uint32_t)tid * k8Vals;
@@ -1861,7 +1862,20 @@ __global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8
         if (patch_build<k8DecTile, k8DecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) apply_patch32(sh, lo, out);
     }
     uint8_t *yt = y + t0;
-    if (lo + k8Vals <= rem) {
+    const uint32_t wlo = (uint32_t)wave * 64u * k8Vals;          // the wave's first value in the tile
+    if (wlo + 64u * k8Vals <= rem) {
+        // the wave's 2 KiB go through LDS so that each store instruction
+        // covers 1 KiB without gaps: lane l writes its 32 bytes at 32 l,
+        // then stores the 16 bytes at 16 l and at 1024 + 16 l
+        xp[wave][2 * lane] = u32x4{out[0], out[1], out[2], out[3]};
+        xp[wave][2 * lane + 1] = u32x4{out[4], out[5], out[6], out[7]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        u32x4 *dst = reinterpret_cast<u32x4 *>(yt + wlo);
+        st_stream(xp[wave][lane], dst + lane);
+        st_stream(xp[wave][64 + lane], dst + 64 + lane);
+    } else if (lo + k8Vals <= rem) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(yt + lo);
         st_stream(u32x4{out[0], out[1], out[2], out[3]}, dst);
         st_stream(u32x4{out[4], out[5], out[6], out[7]}, dst + 1);
