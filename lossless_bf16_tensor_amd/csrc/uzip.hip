@@ -2012,6 +2012,7 @@ __global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_
     __shared__ uint32_t zv32[kZ7Tile / 4 + 1];     // the tile's stored exponents, from a 4-byte boundary
     __shared__ u32x2 spread[256];                   // byte j of spread[b] = bit j of b
     __shared__ uint32_t wtot[kZ7Groups][kZ7Threads / 64];
+    __shared__ u32x4 xp[kZ7Threads / 64][128];      // one wave's 2 KiB of a group's output
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t t0 = (uint64_t)blockIdx.x * kZ7Tile;
     const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kZ7Tile) ? p.n - t0 : (uint64_t)kZ7Tile);
@@ -2119,7 +2120,23 @@ __global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_
             out[2 * q + 1] = merge2(perm(e[q], smq[q], 0x07030602u));
         }
         const uint32_t lo = (uint32_t)(k * (kZ7Threads * 16) + tid * 16);
-        if (lo + 16 <= rem) {
+        const uint32_t wlo = (uint32_t)(k * (kZ7Threads * 16) + wave * 1024);   // the wave's first word
+        if (wlo + 1024 <= rem) {
+            // through LDS, so that each store instruction covers 1 KiB
+            // without gaps: lane l writes its 32 bytes at 32 l, then stores
+            // the 16 bytes at 16 l and at 1024 + 16 l of the wave's span
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            xp[wave][2 * lane] = u32x4{out[0], out[1], out[2], out[3]};
+            xp[wave][2 * lane + 1] = u32x4{out[4], out[5], out[6], out[7]};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            u32x4 *dst = reinterpret_cast<u32x4 *>(yt + wlo);
+            st_stream(xp[wave][lane], dst + lane);
+            st_stream(xp[wave][64 + lane], dst + 64 + lane);
+        } else if (lo + 16 <= rem) {
             st_stream(u32x4{out[0], out[1], out[2], out[3]}, reinterpret_cast<u32x4 *>(yt + lo));
             st_stream(u32x4{out[4], out[5], out[6], out[7]}, reinterpret_cast<u32x4 *>(yt + lo + 8));
         } else if (lo < rem) {
