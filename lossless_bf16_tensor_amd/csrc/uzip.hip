@@ -1953,11 +1953,12 @@ __global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uin
         pre[k] = pr;
         if (lane == 0) wtot[k][wave] = wt;
     }
-    uint32_t out[kS15Groups][4];
+    uint32_t ex[kS15Groups][2];
 #pragma unroll
-    for (int k = 0; k < kS15Groups; k++) decode8(sm[k].x, sm[k].y, cd[k], dec, out[k]);
+    for (int k = 0; k < kS15Groups; k++) decode8_e(cd[k], dec, ex[k]);
     __syncthreads();
     uint32_t run = 0;
+    uint32_t out[kS15Groups][4];
 #pragma unroll
     for (int k = 0; k < kS15Groups; k++) {
         uint32_t base = run;
@@ -1966,18 +1967,34 @@ __global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uin
             if (w < wave) base += wtot[k][w];
             run += wtot[k][w];
         }
-        uint32_t r = base + pre[k];
-        uint32_t t = f[k];
-        while (t) {
-            const uint32_t bit = __builtin_ctz(t);     // 4i for word i of the group
-            const uint32_t i = bit >> 2;
-            if (r < cnt) {
-                const uint32_t sh = 7 + 16 * (i & 1);
-                out[k][i >> 1] = (out[k][i >> 1] & ~(0xFFu << sh)) | ((uint32_t)svals[r] << sh);
+        if (__ballot(f[k] != 0) != 0ull) {
+            // word i's stored exponent (if it is a sentinel) is at rank
+            // r + (sentinels before it); every word reads one, in bounds
+            // (at most the tile's word count), kept only for sentinels
+            const uint32_t r = base + pre[k];
+            uint32_t z = (f[k] | (f[k] >> 3)) & 0x03030303u;      // flag 4i -> bit i
+            z = (z | (z >> 6)) & 0x000F000Fu;
+            z = (z | (z >> 12)) & 0xFFu;
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                uint32_t pd = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int j = 4 * q + i;
+                    const uint32_t rj = r + __builtin_popcount(f[k] & ((1u << (4 * j)) - 1u));
+                    const uint32_t v = rj < cnt ? (uint32_t)svals[rj] : 0u;
+                    pd |= v << (8 * i);
+                }
+                // sentinels with no stored exponent (a corrupt stream) keep
+                // the looked-up one
+                uint32_t zq = (z >> (4 * q)) & 0xFu;
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (r + __builtin_popcount(f[k] & ((1u << (4 * (4 * q + i))) - 1u)) >= cnt) zq &= ~(1u << i);
+                ex[k][q] = bfi(bytemask4(zq), pd, ex[k][q]);
             }
-            r++;
-            t &= t - 1;
         }
+        merge8(sm[k].x, sm[k].y, ex[k], out[k]);
     }
     uint16_t *yt = y + t0;
 #pragma unroll
