@@ -1574,7 +1574,9 @@ __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint3
 
 // One tile of the k-input reduce. Each thread keeps binary32 sums of its
 // 4 groups of 8 words. The inputs are taken in order: input i is decoded,
-// patched through the LDS map, and added to the sums (input 0 sets them),
+// patched through the LDS map, and added to the sums, which start at -0.0
+// (-0.0 + x is x for every binary32 x but a NaN, which stays a NaN: the
+// first add sets them exactly),
 // while the chunk offsets and dense bytes of input i + 1 are already in
 // flight. The sums are rounded once to BF16 and encoded like k_reduce_tile.
 __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uint8_t *__restrict__ out,
@@ -1587,7 +1589,11 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     const uint64_t t0 = tile * kEncTile;
     const uint32_t rem = enc_tile_words(t0, ep);
     uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
-    float acc[kEncGroups][8] = {};
+    float acc[kEncGroups][8];
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++)
+#pragma unroll
+        for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
     PatchHead h = patch_begin<kEncTile, kEncThreads>(ss.in[0], t0, dp);
     DenseIn cur;
     load_dense(ss.in[0], t0, rem, dp, cur);
@@ -1623,8 +1629,8 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const float v0 = __uint_as_float(y[q] << 16), v1 = __uint_as_float(y[q] & 0xFFFF0000u);
-                acc[k][2 * q] = (i == 0) ? v0 : acc[k][2 * q] + v0;
-                acc[k][2 * q + 1] = (i == 0) ? v1 : acc[k][2 * q + 1] + v1;
+                acc[k][2 * q] += v0;
+                acc[k][2 * q + 1] += v1;
             }
         }
         h = hn;
