@@ -29,14 +29,19 @@
 //                   16-byte shifted block copies, and the offsets of its
 //                   chunks. Tile 0 also writes the header, the last chunk
 //                   offset and the zero padding.
-//   k_decode_tile   one pass: 16-byte sign-mantissa loads, 8-byte code loads,
-//                   16-entry lookup in registers (v_perm), merge. The tile's
-//                   escapes go into an LDS bitmap and are applied in registers
-//                   before the single store of the output.
+//   k_decode_tile   one pass: 8-byte sign-mantissa loads, 4-byte code loads,
+//                   16-entry lookup in registers (v_perm). A tile with
+//                   escapes writes its exponent bytes to LDS, each escape
+//                   overwrites its own byte, and the bytes are read back
+//                   before the merge and the single store of the output.
 //   k_patch         standalone sparse patch (the two-kernel decode variant).
 //   k_reduce_tile   decodes both inputs of a tile as above, adds in binary32,
 //                   rounds to BF16 (half to even), then encodes like
 //                   k_encode_tile.
+//   k_reduce_k_tile the same for k inputs summed in order, one rounding.
+//   k8_encode_tile, k8_decode_tile   the FP8 E5M2 variant.
+//   k_s15_decode_tile, kz_encode_tile, kz_decode_tile   the Top-15 +
+//                   sentinel and Top-7 3-bit + zero-point formats.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -1042,8 +1047,8 @@ struct StreamIn {
     uint64_t bytes;       // readable bytes at base
 };
 
-// Patch map of a tile of TILE words: escape bitmap + each escape's exponent,
-// and the tile's chunk offsets.
+// Patch map of a tile of TILE values (the FP8 decode's form of the patch):
+// escape bitmap + each escape's exponent, and the tile's chunk offsets.
 template <int TILE>
 struct PatchShared {
     uint32_t mask[TILE / 32];
@@ -1340,21 +1345,6 @@ __device__ __forceinline__ void ex_get8(const ExpTile<TILE> &sh, uint32_t li0, u
     const u32x2 v = *reinterpret_cast<const u32x2 *>(&sh.ex[li0]);
     e[0] = v.x;
     e[1] = v.y;
-}
-
-// Apply the patch map to the exponents of the 8 words of a thread's group
-// starting at tile word li0 (a multiple of 8; e[0] holds words 0..3 and e[1]
-// words 4..7, one exponent per byte), before they are merged. The group's 8
-// recorded exponents come in one LDS read, and each dword takes its patched
-// bytes through one bitfield insert under a byte mask.
-template <int TILE>
-__device__ __forceinline__ void apply_patch8e(const PatchShared<TILE> &sh, uint32_t li0, uint32_t e[2])
-{
-    const uint32_t bits = (sh.mask[li0 >> 5] >> (li0 & 31)) & 0xFFu;
-    if (bits == 0) return;
-    const u32x2 v = *reinterpret_cast<const u32x2 *>(&sh.val[li0]);
-    e[0] = bfi(bytemask4(bits & 0xFu), v.x, e[0]);
-    e[1] = bfi(bytemask4(bits >> 4), v.y, e[1]);
 }
 
 template <bool kPatch>
