@@ -11,7 +11,7 @@ leave a point open.
 
 Parity status: split/merge, histogram, Top-16, encode, decode, the reduce's
 rounding, the k-input reduce's summation order, and the FP8, Top-15 +
-sentinel and Top-7 3-bit + zero-point formats are pinned by the tests under
+sentinel, Top-7 3-bit + zero-point and Top-8 3-bit formats are pinned by the tests under
 ``tests/test_oracle_*.py``. The one
 choice the pages do not fix at all -- a NaN sum in the reduce becomes 0x7FC0 --
 is "parity unpinned" (it is our own convention).
@@ -74,6 +74,11 @@ def _load():
         "orc_bf16_rne_array": (None, [ctypes.POINTER(ctypes.c_uint32), c64, u16p]),
         "orc_add_bf16_array": (None, [u16p, u16p, c64, u16p]),
         "orc_sum_bf16": (ctypes.c_uint16, [u16p, c32, c64]),
+        "orct8_max_bytes": (c64, [c64, c32]),
+        "orct8_payload_bytes": (c64, [c64, c64]),
+        "orct8_encode": (c64, [u16p, c64, c32, u8p, u8p, c64]),
+        "orct8_decode": (ctypes.c_int, [u8p, c64, c64, c32, u8p, u16p]),
+        "orct8_validate": (ctypes.c_int, [u8p, c64, u8p]),
         "orcz_max_bytes": (c64, [c64, c32]),
         "orcz_payload_bytes": (c64, [c64, c64]),
         "orcz_encode": (c64, [u16p, c64, c32, u8p, u8p, c64]),
@@ -450,3 +455,41 @@ def z7_validate(stream, dec) -> int:
     stream = _u8(stream)
     dec = _u8(dec)
     return int(_load().orcz_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))
+
+
+# ---------------------------------------- Top-8 3-bit with positions ----
+def t8_max_bytes(n: int, chunk: int) -> int:
+    return int(_load().orct8_max_bytes(n, chunk))
+
+
+def t8_payload_bytes(n: int, m: int) -> int:
+    return int(_load().orct8_payload_bytes(n, m))
+
+
+def t8_encode(x, chunk: int, dec) -> np.ndarray:
+    x = _u16(x).reshape(-1)
+    dec = _u8(dec)
+    cap = t8_max_bytes(x.size, chunk)
+    out = np.empty(cap, dtype=np.uint8)
+    total = _load().orct8_encode(_p(x, ctypes.c_uint16), x.size, chunk, _p(dec, ctypes.c_uint8),
+                                 _p(out, ctypes.c_uint8), cap)
+    if total == 0:
+        raise ValueError("oracle t8 encode failed")
+    return out[:total].copy()
+
+
+def t8_decode(stream, n: int, chunk: int, dec) -> np.ndarray:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    y = np.empty(n, dtype=np.uint16)
+    rc = _load().orct8_decode(_p(stream, ctypes.c_uint8), stream.size, n, chunk, _p(dec, ctypes.c_uint8),
+                              _p(y, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle t8 decode failed")
+    return y
+
+
+def t8_validate(stream, dec) -> int:
+    stream = _u8(stream)
+    dec = _u8(dec)
+    return int(_load().orct8_validate(_p(stream, ctypes.c_uint8), stream.size, _p(dec, ctypes.c_uint8)))

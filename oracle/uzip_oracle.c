@@ -14,7 +14,8 @@
  *         plus the raw 8-bit exponent, size B = N + N/2 + 3M), section 3.3
  *         (offline calibration: histogram, Top-16, three lookup tables),
  *         section 3.4 (all 16 codes are real exponents; escapes carry a dummy
- *         code and are overwritten from the position list).
+ *         code and are overwritten from the position list), section 4.3
+ *         Table 3 (Top-8 3-bit codes; the Top-8 section below).
  *   [UZ]  "UCCL-Zip: Lossless Compression Supercharged GPU Communication",
  *         section 3.4 / Figure 6: a receiver decompresses a slice, reduces it
  *         with its own slice, and recompresses the result; section 5.2 /
@@ -883,6 +884,148 @@ int orcz_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
         if (j1 < j0 || j1 - j0 != zeros) return -3;
         for (uint32_t j = j0; j < j1; j++)
             if (orcz_code_of(dec, in[L.val + j]) != 0) return -3;     /* must be outside the top 7 */
+    }
+    return 0;
+}
+
+/* ======================================== Top-8 3-bit with positions ==== */
+/* "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+ * Serving", section 4.3, Table 3 (Top-k exponent coding): the Top-16 codec
+ * with 3-bit codes for the 8 most frequent exponents instead of 4-bit codes
+ * for 16. Readings (the page gives the code width and the numbers, not the
+ * stream): code k is dec[k] of the Top-16 ranking for k < 8; an escape is
+ * every other exponent, with the dummy code 0 and the same chunked
+ * (u16 position, u8 exponent) arrays; the page's 3-bit codes are not
+ * byte-aligned, so they are packed back to back: value i's code at bits
+ * 3i..3i+2 of the section, least significant bit first (the packing of the
+ * E5M2 sign-mantissa bits); header flags = 4; payload N + ceil(3N/8) + 3M. */
+static int orct8_code_of(const uint8_t *dec, uint8_t e)
+{
+    for (int k = 0; k < 8; k++)
+        if (dec[k] == e) return k;
+    return -1;
+}
+
+static orc_layout orct8_layout_of(uint64_t n, uint32_t C, uint64_t m)
+{
+    orc_layout L;
+    uint64_t nch = orc_nchunks(n, C);
+    L.sm = ORC_HEADER;
+    L.codes = L.sm + orc_align(n);
+    L.offs = L.codes + orc_align((3 * n + 7) / 8);
+    L.pos = L.offs + orc_align(4 * (nch + 1));
+    L.val = L.pos + orc_align(2 * m);
+    L.total = L.val + m;
+    return L;
+}
+
+uint64_t orct8_max_bytes(uint64_t n, uint32_t C)
+{
+    if (n == 0 || C == 0) return 0;
+    return orct8_layout_of(n, C, n).total;
+}
+
+uint64_t orct8_payload_bytes(uint64_t n, uint64_t m) { return n + (3 * n + 7) / 8 + 3 * m; }
+
+uint64_t orct8_encode(const uint16_t *x, uint64_t n, uint32_t C, const uint8_t *dec, uint8_t *out, uint64_t cap)
+{
+    if (n == 0 || C == 0 || C > 65536u || n >= ((uint64_t)1 << 32)) return 0;
+    if (cap < orct8_max_bytes(n, C)) return 0;
+    uint64_t m = 0;
+    for (uint64_t i = 0; i < n; i++)
+        if (orct8_code_of(dec, orc_exponent(x[i])) < 0) m++;
+    orc_layout L = orct8_layout_of(n, C, m);
+    memset(out, 0, L.total);
+    /* stage 1: dense sections */
+    for (uint64_t i = 0; i < n; i++) {
+        out[L.sm + i] = orc_signmant(x[i]);
+        int k = orct8_code_of(dec, orc_exponent(x[i]));
+        orc8_put3(out + L.codes, i, k < 0 ? 0u : (unsigned)k);
+    }
+    /* stage 2: escapes chunk by chunk, ascending position */
+    uint64_t nch = orc_nchunks(n, C);
+    uint64_t j = 0;
+    for (uint64_t c = 0; c < nch; c++) {
+        put_u32(out + L.offs + 4 * c, (uint32_t)j);
+        uint64_t lo = c * C, hi = lo + C < n ? lo + C : n;
+        for (uint64_t i = lo; i < hi; i++) {
+            uint8_t e = orc_exponent(x[i]);
+            if (orct8_code_of(dec, e) < 0) {
+                put_u16(out + L.pos + 2 * j, (uint16_t)(i - lo));
+                out[L.val + j] = e;
+                j++;
+            }
+        }
+    }
+    put_u32(out + L.offs + 4 * nch, (uint32_t)j);
+    out[0] = 0x55; out[1] = 0x5A; out[2] = 0x42; out[3] = 0x31;
+    put_u16(out + 4, 1);
+    put_u16(out + 6, 4);                         /* format: Top-8 3-bit with positions */
+    put_u32(out + 8, C);
+    put_u32(out + 12, 0);
+    put_u64(out + 16, n);
+    put_u64(out + 24, m);
+    put_u64(out + 32, L.total);
+    memcpy(out + 40, dec, 16);
+    return L.total;
+}
+
+int orct8_decode(const uint8_t *in, uint64_t in_bytes, uint64_t n, uint32_t C, const uint8_t *dec, uint16_t *y)
+{
+    if (in_bytes < ORC_HEADER || n == 0 || C == 0) return -1;
+    if (get_u64(in + 16) != n || get_u32(in + 8) != C || get_u16(in + 6) != 4) return -1;
+    if (memcmp(in + 40, dec, 16) != 0) return -1;
+    uint64_t m = get_u64(in + 24);
+    orc_layout L = orct8_layout_of(n, C, m);
+    if (in_bytes < L.total) return -1;
+    /* dense lookup: escapes first decode to dec[0] */
+    for (uint64_t i = 0; i < n; i++) y[i] = orc_merge(in[L.sm + i], dec[orc8_get3(in + L.codes, i)]);
+    /* sparse patch */
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        for (uint32_t j = j0; j < j1; j++) {
+            uint64_t i = c * C + get_u16(in + L.pos + 2 * j);
+            if (i >= n || j >= m) return -1;
+            y[i] = orc_merge(in[L.sm + i], in[L.val + j]);
+        }
+    }
+    return 0;
+}
+
+int orct8_validate(const uint8_t *in, uint64_t in_bytes, const uint8_t *dec)
+{
+    if (in_bytes < ORC_HEADER) return -3;
+    if (!(in[0] == 0x55 && in[1] == 0x5A && in[2] == 0x42 && in[3] == 0x31)) return -3;
+    if (get_u16(in + 4) != 1 || get_u16(in + 6) != 4 || get_u32(in + 12) != 0) return -3;
+    uint32_t C = get_u32(in + 8);
+    uint64_t n = get_u64(in + 16), m = get_u64(in + 24), total = get_u64(in + 32);
+    if (C == 0 || C > 65536u || n == 0 || n >= ((uint64_t)1 << 32) || m > n) return -3;
+    for (int i = 56; i < 256; i++) if (in[i] != 0) return -3;
+    orc_layout L = orct8_layout_of(n, C, m);
+    if (total != L.total || in_bytes < L.total) return -3;
+    if (memcmp(in + 40, dec, 16) != 0) return -4;
+    for (int k = 0; k < 16; k++)
+        for (int q = k + 1; q < 16; q++)
+            if (dec[k] == dec[q]) return -3;
+    for (uint64_t p = L.sm + n; p < L.codes; p++) if (in[p]) return -3;
+    for (uint64_t b = 3 * n; b < 8 * ((3 * n + 7) / 8); b++)
+        if ((in[L.codes + b / 8] >> (b % 8)) & 1u) return -3;
+    for (uint64_t p = L.codes + (3 * n + 7) / 8; p < L.offs; p++) if (in[p]) return -3;
+    uint64_t nch = orc_nchunks(n, C);
+    for (uint64_t p = L.offs + 4 * (nch + 1); p < L.pos; p++) if (in[p]) return -3;
+    for (uint64_t p = L.pos + 2 * m; p < L.val; p++) if (in[p]) return -3;
+    if (get_u32(in + L.offs) != 0 || get_u32(in + L.offs + 4 * nch) != m) return -3;
+    for (uint64_t c = 0; c < nch; c++) {
+        uint32_t j0 = get_u32(in + L.offs + 4 * c), j1 = get_u32(in + L.offs + 4 * (c + 1));
+        uint64_t len = (c + 1) * C <= n ? C : n - c * C;
+        if (j1 < j0 || j1 - j0 > len) return -3;
+        for (uint32_t j = j0; j < j1; j++) {
+            uint32_t p = get_u16(in + L.pos + 2 * j);
+            if (p >= len || (j > j0 && p <= get_u16(in + L.pos + 2 * (j - 1)))) return -3;
+            if (orct8_code_of(dec, in[L.val + j]) >= 0) return -3;
+            if (orc8_get3(in + L.codes, c * C + p) != 0) return -3;
+        }
     }
     return 0;
 }

@@ -62,11 +62,15 @@ MUTANTS = {
     "z7_msb_first_planes": ("return (unsigned)(i % 8); }", "return 7u - (unsigned)(i % 8); }"),
     "z7_keeps_position_section": ("/* no position section */\n    L.val = L.pos;\n    L.total = L.val + m;\n    return L;\n}\n\nstatic unsigned orcz_get_code",
                                   "/* no position section */\n    L.val = L.pos + orc_align(2 * m);\n    L.total = L.val + m;\n    return L;\n}\n\nstatic unsigned orcz_get_code"),
+    "t8_seven_codes": ("    for (int k = 0; k < 8; k++)\n        if (dec[k] == e) return k;\n    return -1;\n}\n\nstatic orc_layout orct8_layout_of",
+                       "    for (int k = 0; k < 7; k++)\n        if (dec[k] == e) return k;\n    return -1;\n}\n\nstatic orc_layout orct8_layout_of"),
+    "t8_nibble_sized_codes": ("    L.offs = L.codes + orc_align((3 * n + 7) / 8);\n    L.pos = L.offs + orc_align(4 * (nch + 1));\n    L.val = L.pos + orc_align(2 * m);",
+                              "    L.offs = L.codes + orc_align((n + 1) / 2);\n    L.pos = L.offs + orc_align(4 * (nch + 1));\n    L.val = L.pos + orc_align(2 * m);"),
 }
 
 PIN_TESTS = ["tests/test_oracle_split.py", "tests/test_oracle_codec.py", "tests/test_oracle_reduce.py",
              "tests/test_oracle_reduce_k.py", "tests/test_oracle_fp8.py", "tests/test_oracle_s15.py",
-             "tests/test_oracle_z7.py"]
+             "tests/test_oracle_z7.py", "tests/test_oracle_t8.py"]
 
 
 def _run(name, a, b, tmp):
