@@ -433,20 +433,23 @@ def main():
                              "escape_rate": round(m_on / n, 6), "ratio_total": round(2 * n / tot_on, 4)}
         uzip.encode(x, cb, C, out=out, ws=ws)      # leave the offline stream in place
 
-    # --- ablation: Top-16 with positions against Top-15 + sentinel and Top-7
-    # 3-bit + zero-point, on the headline tensor, under the offline codebook
-    # and one calibrated on the tensor itself ---
+    # --- ablation: Top-16 with positions against Top-15 + sentinel, Top-7
+    # 3-bit + zero-point and Top-8 3-bit with positions, on the headline
+    # tensor, under the offline codebook and one calibrated on the tensor
+    # itself ---
     ablation = None
     if not args.no_ablation:
         ablation = {}
         cb_self = uzip.codebook_from_hist(uzip.histogram(x).cpu().numpy().astype(np.uint64))
         outs = torch.empty(uzip.s15_max_bytes(n, C), dtype=torch.uint8, device=dev)
         outz = torch.empty(uzip.z7_max_bytes(n, C), dtype=torch.uint8, device=dev)
+        outt = torch.empty(uzip.t8_max_bytes(n, C), dtype=torch.uint8, device=dev)
         for label, cbx in (("offline_codebook", cb), ("self_calibrated_codebook", cb_self)):
             row = {}
             for fmt, enc_f, dec_f, buf in (("top16_positions", uzip.encode, uzip.decode, out),
                                            ("top15_sentinel", uzip.s15_encode, uzip.s15_decode, outs),
-                                           ("top7_zero_point", uzip.z7_encode, uzip.z7_decode, outz)):
+                                           ("top7_zero_point", uzip.z7_encode, uzip.z7_decode, outz),
+                                           ("top8_3bit_positions", uzip.t8_encode, uzip.t8_decode, outt)):
                 enc_f(x, cbx, C, out=buf, ws=ws)
                 tt, mm = uzip.stream_bytes(buf)
                 dec_f(buf, cbx, n, C, out=y, in_bytes=tt)
@@ -473,11 +476,11 @@ def main():
                 row[fmt] = {"escape_rate": round(mm / n, 6), "ratio_total": round(2 * n / tt, 4),
                             "encode_ms": round(tee, 4), "decode_ms": round(tdd, 4),
                             "decode_GBps": round(2 * n / (tdd * 1e-3) / 1e9, 1)}
-            for fmt in ("top15_sentinel", "top7_zero_point"):
+            for fmt in ("top15_sentinel", "top7_zero_point", "top8_3bit_positions"):
                 row[fmt]["decode_slowdown"] = round(row[fmt]["decode_ms"] / row["top16_positions"]["decode_ms"], 3)
                 row[fmt]["encode_slowdown"] = round(row[fmt]["encode_ms"] / row["top16_positions"]["encode_ms"], 3)
             ablation[label] = row
-        del outs, outz
+        del outs, outz, outt
         uzip.encode(x, cb, C, out=out, ws=ws)      # leave the headline stream in place
 
     # --- FP8 E5M2 variant on the same KV-cache recipe cast to E5M2 (2^28 bytes) ---

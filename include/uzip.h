@@ -122,7 +122,7 @@ int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
 
 /* Full structural check of a stream held in host memory (any format: BF16,
  * FP8 E5M2 with header flags 1, Top-15 + sentinel with flags 2, Top-7 +
- * zero-point with flags 3): header fields, section sizes, zero padding,
+ * zero-point with flags 3, Top-8 3-bit with flags 4): header fields, section sizes, zero padding,
  * offsets monotone and ending at M, positions ascending and inside their
  * chunk, every escape value outside the codebook with code 0 in the dense
  * stream (for the position-free formats: as many stored values per chunk as
@@ -233,6 +233,29 @@ int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t ch
                     const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
 int uzip_s15_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
                        const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
+
+/* ------------------------------ Top-8 3-bit with positions (ablation) -- */
+/* "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM
+ * Serving", section 4.3 / Table 3 (Top-k exponent coding): the Top-16
+ * stream with 3-bit codes for dec[0..7] instead of 4-bit codes for
+ * dec[0..15]; every other exponent is an escape (dummy code 0, u16 in-chunk
+ * position, u8 raw exponent, as in uzip_encode). The page notes that its
+ * 3-bit codes are not byte-aligned; here they are packed back to back: value
+ * i's code at bits 3i..3i+2 of the section, least significant bit first.
+ * Stream: header (flags = 4) | sm | codes (ceil(3n/8) bytes) | offsets |
+ * pos | val, each section 256-byte aligned; payload n + ceil(3n/8) + 3M.
+ * The codebook is a Top-16 one (dec[8..15] are not used). Any chunk valid
+ * for uzip_encode; otherwise as uzip_encode / uzip_decode. */
+uint64_t uzip_t8_max_bytes(uint64_t n, uint32_t chunk);
+int uzip_t8_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s);
+int uzip_t8_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                      const uzip_opts_t *opts, hipStream_t s);
+int uzip_t8_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                   const uzip_codebook_t *cb, uint16_t *d_y, hipStream_t s);
+int uzip_t8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk,
+                      const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
 
 /* ------------------------------ Top-7 3-bit + zero-point (ablation) ---- */
 /* "ZipCCL: Efficient Lossless Data Compression of Communication

@@ -60,8 +60,9 @@ __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~
 // Stream formats (header flags): Top-16 codes with escape positions on BF16
 // words or on FP8 E5M2 bytes; Top-15 + sentinel on BF16 words (no position
 // section); Top-7 3-bit codes + zero-points on BF16 words (three bit planes,
-// no position section).
-enum : uint8_t { kFmtBF16 = 0, kFmtFP8 = 1, kFmtS15 = 2, kFmtZ7 = 3 };
+// no position section); Top-8 3-bit codes packed 3 bits per value, with the
+// Top-16 escape arrays.
+enum : uint8_t { kFmtBF16 = 0, kFmtFP8 = 1, kFmtS15 = 2, kFmtZ7 = 3, kFmtT8 = 4 };
 
 struct Layout {
     uint64_t n, nch;
@@ -72,7 +73,7 @@ struct Layout {
     uint32_t nplanes;                        // 1, or 3 bit planes for Z7
 };
 
-__host__ __device__ inline bool has_pos(uint8_t fmt) { return fmt == kFmtBF16 || fmt == kFmtFP8; }
+__host__ __device__ inline bool has_pos(uint8_t fmt) { return fmt == kFmtBF16 || fmt == kFmtFP8 || fmt == kFmtT8; }
 __host__ __device__ inline uint64_t off_val_of(const Layout &L, uint64_t m)
 {
     return L.off_pos + (has_pos(L.fmt) ? align256(2 * m) : 0);
@@ -94,7 +95,7 @@ Layout make_layout(uint64_t n, uint32_t C, uint8_t fmt = kFmtBF16)
     L.nch = (n + C - 1) / C;
     L.off_codes = kHeader + align256(sm_bytes_of(n, fp8));
     L.nplanes = fmt == kFmtZ7 ? 3 : 1;
-    L.code_bytes = fmt == kFmtZ7 ? (n + 7) / 8 : (n + 1) / 2;
+    L.code_bytes = fmt == kFmtZ7 ? (n + 7) / 8 : fmt == kFmtT8 ? (3 * n + 7) / 8 : (n + 1) / 2;
     L.plane = align256(L.code_bytes);
     L.off_offs = L.off_codes + L.nplanes * L.plane;
     L.off_pos = L.off_offs + align256(4 * (L.nch + 1));
@@ -258,6 +259,20 @@ __device__ __forceinline__ uint32_t spread4(uint32_t b) { return (b * 0x00204081
 // 0xFF in byte j where bit j of the nibble b is set, else 0 (byte permute
 // selectors 12 and 13 give 0x00 and 0xFF).
 __device__ __forceinline__ uint32_t bytemask4(uint32_t b) { return perm(0u, 0u, 0x0C0C0C0Cu + spread4(b)); }
+
+// 4 three-bit values held one per byte -> a0 | a1 << 3 | a2 << 6 | a3 << 9.
+__device__ __forceinline__ uint32_t pack12(uint32_t a)
+{
+    const uint32_t t = (a | (a >> 5)) & 0x003F003Fu;
+    return (t | (t >> 10)) & 0xFFFu;
+}
+
+// Inverse of pack12.
+__device__ __forceinline__ uint32_t unpack12(uint32_t c)
+{
+    const uint32_t t = (c & 0x3Fu) | ((c & 0xFC0u) << 10);
+    return (t & 0x00070007u) | ((t & 0x00380038u) << 5);
+}
 
 // Sign-mantissa bytes of 4 words held in two dwords (word 2i in the low half).
 __device__ __forceinline__ uint32_t signmant4(uint32_t v0, uint32_t v1)
@@ -575,10 +590,23 @@ __device__ __forceinline__ uint32_t quad_planes(uint32_t v, uint32_t q)
 // tile's escapes in element order in LDS (eb). Returns the tile's escape
 // count m (the same in every thread). cstart[k] is the number of the tile's
 // escapes before group k when group k starts a chunk, else ~0u. Ends without
-// a barrier after the LDS writes of eb. kPlanes: the codes are 3-bit (lut
-// bits 0..2) and go to three bit planes (p.plane bytes apart) instead of
-// nibbles; every thread of the workgroup must take part (quad exchanges).
-template <bool kPlanes = false>
+// a barrier after the LDS writes of eb. kCodes: kCodeNib, 4-bit codes two per
+// byte; kCodePlanes, 3-bit codes (lut bits 0..2) in three bit planes
+// (p.plane bytes apart); kCodePack3, 3-bit codes packed 3 bits per value.
+// With 3-bit codes every thread of the workgroup must take part (quad
+// exchanges).
+enum { kCodeNib = 0, kCodePlanes = 1, kCodePack3 = 2 };
+
+// The packed 3-bit codes of a quad of lanes (24 bits each, 8 values, lane
+// 0's lowest): lane q < 3 returns dword q of the quad's 12 bytes (its own
+// bits from bit 8q on, then the next lane's).
+__device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
+{
+    const uint32_t nxt = __builtin_amdgcn_update_dpp(0u, v, 0xF9, 0xF, 0xF, false);   // quad_perm [1,2,3,3]
+    return (v >> (8 * q)) | (nxt << (24 - 8 * q));
+}
+
+template <int kCodes = kCodeNib>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
                                                       EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
@@ -609,7 +637,9 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         Lw[k][1] = L1;
         sm[k][0] = signmant4(xw[k][0], xw[k][1]);
         sm[k][1] = signmant4(xw[k][2], xw[k][3]);
-        if constexpr (kPlanes) cw[k] = quad_planes(plane_bytes8(L0, L1), (uint32_t)(lane & 3));
+        if constexpr (kCodes == kCodePlanes) cw[k] = quad_planes(plane_bytes8(L0, L1), (uint32_t)(lane & 3));
+        else if constexpr (kCodes == kCodePack3)
+            cw[k] = quad_pack3(pack12(L0 & 0x07070707u) | (pack12(L1 & 0x07070707u) << 12), (uint32_t)(lane & 3));
         else cw[k] = pack_codes8(L0, L1);
     }
 #pragma unroll
@@ -620,9 +650,17 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
             smv.x = sm[k][0];
             smv.y = sm[k][1];
             st_stream(smv, reinterpret_cast<u32x2 *>(smt + lo));
-            if constexpr (!kPlanes) st_stream(cw[k], reinterpret_cast<uint32_t *>(cdt + lo / 2));
+            if constexpr (kCodes == kCodeNib) st_stream(cw[k], reinterpret_cast<uint32_t *>(cdt + lo / 2));
         }
-        if constexpr (kPlanes) {
+        if constexpr (kCodes == kCodePack3) {
+            // lane q < 3 of a quad stores dword q of the quad's 12 code
+            // bytes (32 words from lq); a quad whose first group is past the
+            // end stores nothing; bits past n are 0
+            const uint32_t q = (uint32_t)(lane & 3), lq = lo - 8 * q;
+            if (q < 3 && lq < rem)
+                st_stream(cw[k], reinterpret_cast<uint32_t *>(out + p.off_codes + (3 * (t0 + lq)) / 8 + 4 * q));
+        }
+        if constexpr (kCodes == kCodePlanes) {
             // lane q < 3 of a quad stores the quad's dword of plane q (its
             // bytes are the 4 lanes' 8-word groups); a quad whose first group
             // is past the end stores nothing
@@ -712,7 +750,7 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
     for (uint32_t q = tid; q < (m + 15) / 16; q += kEncThreads) sv[q] = lv[q];
 }
 
-template <bool kPlanes>
+template <int kCodes>
 __device__ __forceinline__ void encode_tile(const uint16_t *__restrict__ x, uint8_t *__restrict__ out,
                                             const EncWs &ws, const EncParams &p)
 {
@@ -741,14 +779,14 @@ __device__ __forceinline__ void encode_tile(const uint16_t *__restrict__ x, uint
     // the code table goes to LDS after the data loads are in flight
     if (p.dlut) load_wave_lut(sh, p.dlut); else load_wave_lut(sh, p.lut);
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kPlanes>(xw, t0, rem, out, p, sh, eb, cstart);
+    const uint32_t m = encode_dense_rank<kCodes>(xw, t0, rem, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
 }
 
 __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__restrict__ x,
                                                              uint8_t *__restrict__ out, EncWs ws, EncParams p)
 {
-    encode_tile<false>(x, out, ws, p);
+    encode_tile<kCodeNib>(x, out, ws, p);
 }
 
 // Top-7 3-bit + zero-point streams: the same pass with the codes written as
@@ -756,7 +794,14 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_tile(const uint16_t *__r
 __global__ __launch_bounds__(kEncThreads) void kz_encode_tile(const uint16_t *__restrict__ x,
                                                               uint8_t *__restrict__ out, EncWs ws, EncParams p)
 {
-    encode_tile<true>(x, out, ws, p);
+    encode_tile<kCodePlanes>(x, out, ws, p);
+}
+
+// Top-8 3-bit streams: the same pass with the codes packed 3 bits per value.
+__global__ __launch_bounds__(kEncThreads) void kt8_encode_tile(const uint16_t *__restrict__ x,
+                                                               uint8_t *__restrict__ out, EncWs ws, EncParams p)
+{
+    encode_tile<kCodePack3>(x, out, ws, p);
 }
 
 // One workgroup per group of 2^gshift tiles: gsum[g] = escapes in the group,
@@ -1682,20 +1727,6 @@ __device__ __forceinline__ uint32_t signmant8x4(uint32_t w)
     return bfi(0x03030303u, w, w >> 5) & 0x07070707u;
 }
 
-// 4 three-bit values held one per byte -> a0 | a1 << 3 | a2 << 6 | a3 << 9.
-__device__ __forceinline__ uint32_t pack12(uint32_t a)
-{
-    const uint32_t t = (a | (a >> 5)) & 0x003F003Fu;
-    return (t | (t >> 10)) & 0xFFFu;
-}
-
-// Inverse of pack12.
-__device__ __forceinline__ uint32_t unpack12(uint32_t c)
-{
-    const uint32_t t = (c & 0x3Fu) | ((c & 0xFC0u) << 10);
-    return (t & 0x00070007u) | ((t & 0x00380038u) << 5);
-}
-
 // Rebuild 4 E5M2 bytes from their 3 kept bits (a) and exponents (e), one per byte.
 __device__ __forceinline__ uint32_t merge8x4(uint32_t a, uint32_t e)
 {
@@ -2171,6 +2202,115 @@ __global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_
     }
 }
 
+// ================================================ Top-8 3-bit, positions ====
+// "SplitZip" section 4.3 / Table 3: codes 0..7 name dec[0..7], packed 3
+// bits per value; escapes as in the Top-16 stream. A 128-thread tile of
+// 4,096 words; each lane takes 2 groups of 16 words (group k at tile word
+// 2048 k + 16 lane): 16 sign-mantissa bytes and the group's 6 code bytes,
+// from two aligned dwords and a byte shift. unpack12 spreads 4 codes over 4
+// bytes, which select from the 8-entry table [dec0..dec7] in one byte
+// permute. Escapes patch the exponent bytes through the LDS exponent tile
+// (as in k_decode_tile), and each wave's output goes through LDS so that
+// every store instruction covers 1 KiB.
+constexpr int kT8Threads = 128;
+constexpr int kT8Groups = 2;
+constexpr int kT8Tile = kT8Threads * kT8Groups * 16;
+static_assert(kT8Tile == kDecTile, "the patch takes the decode tile's shape");
+
+__global__ __launch_bounds__(kT8Threads) void kt8_decode_tile(StreamIn s, uint16_t *__restrict__ y, DecParams p)
+{
+    __shared__ ExpTile<kT8Tile> sh;
+    __shared__ u32x4 xp[kT8Threads / 64][128];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint64_t t0 = (uint64_t)blockIdx.x * kT8Tile;
+    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kT8Tile) ? p.n - t0 : (uint64_t)kT8Tile);
+    const PatchHead ph = patch_begin<kT8Tile, kT8Threads>(s, t0, p);
+    const uint8_t *smt = s.base + kHeader + t0;
+    const uint8_t *cdt = s.base + p.off_codes + t0 / 8 * 3;      // 4-byte aligned (t0 is a multiple of 32)
+    u32x4 sm[kT8Groups];
+    uint32_t c0[kT8Groups], c1[kT8Groups], csh[kT8Groups];
+#pragma unroll
+    for (int k = 0; k < kT8Groups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kT8Threads * 16) + tid * 16);
+        sm[k] = u32x4{0u, 0u, 0u, 0u};
+        c0[k] = c1[k] = 0u;
+        const uint32_t b = lo / 8 * 3;                      // the group's first code byte: 6 per lane
+        csh[k] = b & 3u;                                    // 0 or 2
+        if (lo < rem) {
+            // the sections are padded to 256 bytes and followed by more of
+            // the stream, so the 16- and 8-byte loads stay inside it
+            sm[k] = ld_stream(reinterpret_cast<const u32x4 *>(smt + lo));
+            const uint32_t *cw = reinterpret_cast<const uint32_t *>(cdt + (b & ~3u));
+            c0[k] = ld_stream(cw);
+            c1[k] = ld_stream(cw + 1);
+        }
+    }
+    const PatchFetch<kDecFetch> pf = patch_fetch<kT8Tile, kT8Threads, kDecFetch>(s, t0, p, ph);
+    const uint32_t T0 = p.dec[0], T1 = p.dec[1];                  // dec[0..3], dec[4..7]
+    uint32_t ex[kT8Groups][4];
+#pragma unroll
+    for (int k = 0; k < kT8Groups; k++) {
+        // the 48 code bits of the group's 16 words: lo32 | hi16 << 32
+        const uint32_t lo32 = __builtin_amdgcn_alignbyte(c1[k], c0[k], csh[k]);
+        const uint32_t hi16 = (c1[k] >> (8 * csh[k])) & 0xFFFFu;
+        ex[k][0] = perm(T1, T0, unpack12(lo32 & 0xFFFu));
+        ex[k][1] = perm(T1, T0, unpack12((lo32 >> 12) & 0xFFFu));
+        ex[k][2] = perm(T1, T0, unpack12(((lo32 >> 24) | (hi16 << 8)) & 0xFFFu));
+        ex[k][3] = perm(T1, T0, unpack12((hi16 >> 4) & 0xFFFu));
+    }
+    if (pf.live) {
+#pragma unroll
+        for (int k = 0; k < kT8Groups; k++) {
+            const uint32_t lo = (uint32_t)(k * (kT8Threads * 16) + tid * 16);
+            if (lo < rem) *reinterpret_cast<u32x4 *>(&sh.ex[lo]) = u32x4{ex[k][0], ex[k][1], ex[k][2], ex[k][3]};
+        }
+        patch_put_offs(t0, p, ph, pf, sh);
+        __syncthreads();
+        patch_scatter<kT8Tile, kT8Threads, kDecFetch>(s, t0, p, ph, pf, sh);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kT8Groups; k++) {
+            const uint32_t lo = (uint32_t)(k * (kT8Threads * 16) + tid * 16);
+            if (lo < rem) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(&sh.ex[lo]);
+                ex[k][0] = v.x; ex[k][1] = v.y; ex[k][2] = v.z; ex[k][3] = v.w;
+            }
+        }
+    }
+    uint16_t *yt = y + t0;
+#pragma unroll
+    for (int k = 0; k < kT8Groups; k++) {
+        const uint32_t smq[4] = {sm[k].x, sm[k].y, sm[k].z, sm[k].w};
+        uint32_t out[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            out[2 * q] = merge2(perm(ex[k][q], smq[q], 0x05010400u));
+            out[2 * q + 1] = merge2(perm(ex[k][q], smq[q], 0x07030602u));
+        }
+        const uint32_t lo = (uint32_t)(k * (kT8Threads * 16) + tid * 16);
+        const uint32_t wlo = (uint32_t)(k * (kT8Threads * 16) + wave * 1024);
+        if (wlo + 1024 <= rem) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            xp[wave][2 * lane] = u32x4{out[0], out[1], out[2], out[3]};
+            xp[wave][2 * lane + 1] = u32x4{out[4], out[5], out[6], out[7]};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            u32x4 *dst = reinterpret_cast<u32x4 *>(yt + wlo);
+            st_stream(xp[wave][lane], dst + lane);
+            st_stream(xp[wave][64 + lane], dst + 64 + lane);
+        } else if (lo + 16 <= rem) {
+            st_stream(u32x4{out[0], out[1], out[2], out[3]}, reinterpret_cast<u32x4 *>(yt + lo));
+            st_stream(u32x4{out[4], out[5], out[6], out[7]}, reinterpret_cast<u32x4 *>(yt + lo + 8));
+        } else if (lo < rem) {
+            for (uint32_t j = 0; j < 16 && lo + j < rem; j++)
+                yt[lo + j] = (uint16_t)(out[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 // ================================================================ host ====
 thread_local char g_hip_err[160];
 
@@ -2435,9 +2575,9 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     uint32_t C;
     uint8_t dec[16];
     if (uzip_parse_header(s, &n, &C, &m, &total, dec) != UZIP_OK) return UZIP_ECORRUPT;
-    const uint16_t fmt = rd16(s + 6);       // 0 BF16, 1 FP8 E5M2, 2 Top-15 + sentinel, 3 Top-7 + zero-point
-    if (fmt > 3 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
-    const bool fp8 = fmt == kFmtFP8, s15 = fmt == kFmtS15, z7 = fmt == kFmtZ7;
+    const uint16_t fmt = rd16(s + 6);       // 0 BF16, 1 FP8 E5M2, 2 Top-15 + sentinel, 3 Top-7 + zero-point, 4 Top-8
+    if (fmt > 4 || rd32(s + 12) != 0) return UZIP_ECORRUPT;
+    const bool fp8 = fmt == kFmtFP8, s15 = fmt == kFmtS15, z7 = fmt == kFmtZ7, t8 = fmt == kFmtT8;
     for (uint64_t i = 56; i < kHeader; i++)
         if (s[i]) return UZIP_ECORRUPT;
     if (!valid_nc(n, C) || m > n) return UZIP_ECORRUPT;
@@ -2451,7 +2591,7 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     for (int k = 0; k < 16; k++) {
         if (seen[dec[k]] || (fp8 && dec[k] > 31)) return UZIP_ECORRUPT;
         seen[dec[k]] = true;
-        in_book[dec[k]] = z7 ? k < 7 : (!s15 || k < 15);   // Top-15 uses dec[0..14], Top-7 dec[0..6]
+        in_book[dec[k]] = z7 ? k < 7 : t8 ? k < 8 : (!s15 || k < 15);   // Top-15: dec[0..14], Top-7: dec[0..6], Top-8: dec[0..7]
     }
     auto zero = [&](uint64_t a, uint64_t b) {
         for (uint64_t i = a; i < b; i++)
@@ -2461,7 +2601,8 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
     const uint64_t smb = sm_bytes_of(n, fp8);
     if (!zero(kHeader + smb, L.off_codes)) return UZIP_ECORRUPT;
     if (fp8 && (3 * n) % 8 && (s[kHeader + smb - 1] >> ((3 * n) % 8))) return UZIP_ECORRUPT;   // unused bits
-    if (!z7 && (n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
+    if (!z7 && !t8 && (n & 1) && (s[L.off_codes + n / 2] >> 4)) return UZIP_ECORRUPT;
+    if (t8 && (3 * n) % 8 && (s[L.off_codes + (3 * n) / 8] >> ((3 * n) % 8))) return UZIP_ECORRUPT;   // bits past 3n
     for (uint32_t b = 0; b < L.nplanes; b++) {
         const uint64_t pl = L.off_codes + b * L.plane;
         if (z7 && (n & 7) && (s[pl + n / 8] >> (n & 7))) return UZIP_ECORRUPT;     // plane bits past n
@@ -2515,6 +2656,13 @@ int uzip_validate_host(const void *h_stream, uint64_t bytes, const uzip_codebook
             prev = p;
             if (in_book[s[off_val + j]] || (fp8 && s[off_val + j] > 31)) return UZIP_ECORRUPT;
             const uint64_t i = c * C + p;
+            if (t8) {
+                uint32_t code = 0;
+                for (uint32_t k = 0; k < 3; k++)
+                    code |= ((s[L.off_codes + (3 * i + k) / 8] >> ((3 * i + k) % 8)) & 1u) << k;
+                if (code != 0) return UZIP_ECORRUPT;
+                continue;
+            }
             const uint8_t b = s[L.off_codes + i / 2];
             if (((i & 1) ? (b >> 4) : (b & 0xF)) != 0) return UZIP_ECORRUPT;
         }
@@ -2685,6 +2833,65 @@ int uzip_s15_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t ch
                     uint16_t *d_y, hipStream_t s)
 {
     return uzip_s15_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
+}
+
+uint64_t uzip_t8_max_bytes(uint64_t n, uint32_t chunk)
+{
+    if (!valid_nc(n, chunk)) return 0;
+    return total_of(make_layout(n, chunk, kFmtT8), n);
+}
+
+int uzip_t8_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
+                      const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_x || !d_out || !d_ws || !aligned16(d_x) || !aligned16(d_out) || !aligned16(d_ws)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    if (out_cap < uzip_t8_max_bytes(n, chunk) || ws_bytes < uzip_workspace_bytes(n, chunk)) return UZIP_ENOSPC;
+    const Layout L = make_layout(n, chunk, kFmtT8);
+    EncParams ep = make_enc_params(L, cb);
+    for (int e = 0; e < 256; e++) ep.lut[e] = 0x80;       // escape: dummy code 0
+    for (int k = 0; k < 8; k++) ep.lut[cb->dec[k]] = (uint8_t)k;
+    const EncWs ws = make_ws(d_ws, n, chunk);
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    kt8_encode_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(d_x, static_cast<uint8_t *>(d_out), ws, ep);
+    UZIP_LAUNCH_CHECK("kt8_encode_tile");
+    if ((rc = ev.record(1))) return rc;
+    return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
+}
+
+int uzip_t8_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
+{
+    return uzip_t8_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_t8_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                      uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s)
+{
+    if (!d_in || !d_y || !aligned16(d_in) || !aligned16(d_y)) return UZIP_EINVAL;
+    if (!valid_nc(n, chunk)) return UZIP_EINVAL;
+    int rc = check_codebook(cb);
+    if (rc) return rc;
+    const Layout L = make_layout(n, chunk, kFmtT8);
+    if (in_bytes < total_of(L, 0)) return UZIP_EINVAL;
+    const DecParams dp = make_dec_params(L, cb);
+    const StreamIn si{static_cast<const uint8_t *>(d_in), in_bytes};
+    const Events ev{opts, s};
+    if ((rc = ev.record(0))) return rc;
+    const uint64_t tiles = (n + kT8Tile - 1) / kT8Tile;
+    kt8_decode_tile<<<(unsigned)tiles, kT8Threads, 0, s>>>(si, d_y, dp);
+    UZIP_LAUNCH_CHECK("kt8_decode_tile");
+    return ev.record(1);
+}
+
+int uzip_t8_decode(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                   uint16_t *d_y, hipStream_t s)
+{
+    return uzip_t8_decode_ex(d_in, in_bytes, n, chunk, cb, d_y, nullptr, s);
 }
 
 uint64_t uzip_z7_max_bytes(uint64_t n, uint32_t chunk)

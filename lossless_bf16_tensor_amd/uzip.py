@@ -30,6 +30,7 @@ EXPORTS = (
     "uzip_fp8_calibrate", "uzip_fp8_encode", "uzip_fp8_encode_ex", "uzip_fp8_decode", "uzip_fp8_decode_ex",
     "uzip_s15_max_bytes", "uzip_s15_encode", "uzip_s15_encode_ex", "uzip_s15_decode", "uzip_s15_decode_ex",
     "uzip_z7_max_bytes", "uzip_z7_encode", "uzip_z7_encode_ex", "uzip_z7_decode", "uzip_z7_decode_ex",
+    "uzip_t8_max_bytes", "uzip_t8_encode", "uzip_t8_encode_ex", "uzip_t8_decode", "uzip_t8_decode_ex",
 )
 
 MAX_K = 16                      # UZIP_MAX_K
@@ -102,6 +103,11 @@ def lib():
         "uzip_s15_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
         "uzip_s15_decode": (i32, [vp, u64, u64, u32, cbp, vp, vp]),
         "uzip_s15_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
+        "uzip_t8_max_bytes": (u64, [u64, u32]),
+        "uzip_t8_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
+        "uzip_t8_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_t8_decode": (i32, [vp, u64, u64, u32, cbp, vp, vp]),
+        "uzip_t8_decode_ex": (i32, [vp, u64, u64, u32, cbp, vp, op, vp]),
         "uzip_z7_max_bytes": (u64, [u64, u32]),
         "uzip_z7_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
         "uzip_z7_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
@@ -460,4 +466,35 @@ def z7_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: t
     nb = buf.numel() if in_bytes is None else in_bytes
     _check(lib().uzip_z7_decode_ex(_ptr(buf), nb, n, chunk, ctypes.byref(cb), _ptr(w),
                                    ctypes.byref(o) if o else None, _stream(stream)), "z7_decode")
+    return out
+
+
+# --------------------------------------- Top-8 3-bit with positions -----
+def t8_max_bytes(n: int, chunk: int) -> int:
+    return int(lib().uzip_t8_max_bytes(n, chunk))
+
+
+def t8_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None, events=None, stream=None) -> torch.Tensor:
+    w = _words(x)
+    n = w.numel()
+    if out is None:
+        out = torch.empty(t8_max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+    o = _opts(events)
+    _check(lib().uzip_t8_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
+                                   ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "t8_encode")
+    return out
+
+
+def t8_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
+              in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+    w = _words(out)
+    o = _opts(events)
+    nb = buf.numel() if in_bytes is None else in_bytes
+    _check(lib().uzip_t8_decode_ex(_ptr(buf), nb, n, chunk, ctypes.byref(cb), _ptr(w),
+                                   ctypes.byref(o) if o else None, _stream(stream)), "t8_decode")
     return out

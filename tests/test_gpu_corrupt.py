@@ -28,6 +28,9 @@ def sections(n, C, fmt):
     elif fmt == "z7":
         codes = 256 + A(n)
         offs = codes + 3 * A((n + 7) // 8)
+    elif fmt == "t8":
+        codes = 256 + A(n)
+        offs = codes + A((3 * n + 7) // 8)
     else:
         codes = 256 + A(n)
         offs = codes + A((n + 1) // 2)
@@ -65,8 +68,10 @@ def run_case(fmt, n, C, seed):
         s = oracle.fp8_encode(x, C, ocb.dec)
     else:
         x = np.resize(w.x, n).astype(np.uint16)
-        s = {"bf16": oracle.encode, "s15": oracle.s15_encode, "z7": oracle.z7_encode}[fmt](x, C, ocb.dec)
-    dec = {"bf16": uzip.decode, "s15": uzip.s15_decode, "z7": uzip.z7_decode, "fp8": uzip.fp8_decode}[fmt]
+        s = {"bf16": oracle.encode, "s15": oracle.s15_encode, "z7": oracle.z7_encode,
+             "t8": oracle.t8_encode}[fmt](x, C, ocb.dec)
+    dec = {"bf16": uzip.decode, "s15": uzip.s15_decode, "z7": uzip.z7_decode, "fp8": uzip.fp8_decode,
+           "t8": uzip.t8_decode}[fmt]
     for label, bad in corruptions(s, n, C, fmt, rng).items():
         buf = on_device(bad)
         if fmt == "fp8":
@@ -88,7 +93,8 @@ def run_case(fmt, n, C, seed):
 
 
 @pytest.mark.parametrize("fmt,n,C", [("bf16", 100003, 1024), ("bf16", 70001, 65536), ("bf16", 50000, 64),
-                                     ("s15", 100003, 1024), ("z7", 100003, 1024), ("fp8", 100003, 1024)])
+                                     ("s15", 100003, 1024), ("z7", 100003, 1024), ("fp8", 100003, 1024),
+                                     ("t8", 100003, 1024), ("t8", 70001, 65536)])
 def test_corrupt_stream_decodes_inside_its_buffers(fmt, n, C):
     run_case(fmt, n, C, seed=n + C)
 

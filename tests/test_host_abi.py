@@ -202,6 +202,35 @@ def test_validate_host_z7_streams():
     assert uzip.validate_host(bad.tobytes(), cb) == -3
 
 
+@pytest.mark.parametrize("n,C", [(1, 64), (1001, 256), (65536, 1024), (70001, 65536)])
+def test_t8_max_bytes_matches_oracle(n, C):
+    assert uzip.t8_max_bytes(n, C) == oracle.t8_max_bytes(n, C)
+
+
+def test_validate_host_t8_streams():
+    w = workloads.config(1)
+    x = w.x[:30001].copy()
+    ocb = oracle.calibrate(w.calib)
+    cb = uzip.codebook_from_hist(ocb.hist)
+    s = oracle.t8_encode(x, 256, ocb.dec)
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    A = lambda v: (v + 255) // 256 * 256
+    n = x.size
+    codes = 256 + A(n)
+    offs = codes + A((3 * n + 7) // 8)
+    pos = offs + A(4 * ((n + 255) // 256 + 1))
+    i = int(np.frombuffer(s[pos:pos + 2].tobytes(), np.uint16)[0])             # chunk 0's first escape
+    bad = s.copy(); bad[codes + (3 * i + 1) // 8] |= 1 << ((3 * i + 1) % 8)    # its code becomes 2
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[codes + (3 * n) // 8] |= 0x80                         # a code bit past 3n
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    m = int(np.frombuffer(s[24:32].tobytes(), np.uint64)[0])
+    bad = s.copy(); bad[s.size - m] = ocb.dec[7]                              # a stored exponent among the eight
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+    bad = s.copy(); bad[6] = 5
+    assert uzip.validate_host(bad.tobytes(), cb) == -3
+
+
 def test_strerror_texts():
     L = uzip.lib()
     for code in (0, -1, -2, -3, -4, -5, 7):
@@ -260,6 +289,12 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_s15_encode(p, 1000, 8192, cbr, p, big, p, ws, None) == -1       # chunk above 4096
     assert L.uzip_s15_encode(p, 1000, 1024, cbr, p, s15b - 1, p, ws, None) == -2
     assert L.uzip_s15_decode(p, 10, 1000, 1024, cbr, p, None) == -1
+    t8b = uzip.t8_max_bytes(1000, 1024)
+    assert L.uzip_t8_encode(p, 1000, 1000, cbr, p, big, p, ws, None) == -1        # chunk not a power of two
+    assert L.uzip_t8_encode(p, 1000, 1024, cbr, p, t8b - 1, p, ws, None) == -2
+    assert L.uzip_t8_encode(mis, 1000, 1024, cbr, p, t8b, p, ws, None) == -1
+    assert L.uzip_t8_decode(p, 10, 1000, 1024, cbr, p, None) == -1                # in_bytes too small
+    assert L.uzip_t8_decode(p, t8b, 1000, 1024, cbr, mis, None) == -1
     z7b = uzip.z7_max_bytes(1000, 1024)
     assert L.uzip_z7_encode(p, 1000, 8192, cbr, p, big, p, ws, None) == -1        # chunk above 4096
     assert L.uzip_z7_encode(mis, 1000, 1024, cbr, p, z7b, p, ws, None) == -1
