@@ -956,7 +956,7 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     if (tile >= p.ntiles) return;
     const uint64_t t0 = tile * kEncTile;
     const uint32_t C = p.Cmask + 1;
-    // ---- round 1: loads independent of the count and of P
+    // ---- first loads: everything independent of the count and of P
     const uint8_t *src_p = reinterpret_cast<const uint8_t *>(ws.stage_pos + tile * kEncTile);
     const uint8_t *src_v = ws.stage_val + tile * kEncTile;
     const u32x4 *sp4 = reinterpret_cast<const u32x4 *>(src_p);
@@ -1620,12 +1620,13 @@ __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint3
 }
 
 // One tile of the k-input reduce. Each thread keeps binary32 sums of its
-// 4 groups of 8 words. The inputs are taken in order: input i is decoded,
-// patched through the LDS map, and added to the sums, which start at -0.0
+// 4 groups of 8 words. The inputs are taken two at a time: both are loaded
+// and decoded, their escapes are patched through the two LDS exponent tiles
+// between one pair of barriers (half the barriers of one input at a time),
+// and they are added to the sums in input order. The sums start at -0.0
 // (-0.0 + x is x for every binary32 x but a NaN, which stays a NaN: the
-// first add sets them exactly),
-// while the chunk offsets and dense bytes of input i + 1 are already in
-// flight. The sums are rounded once to BF16 and encoded like k_reduce_tile.
+// first add sets them exactly). They are rounded once to BF16 and encoded
+// like k_reduce_tile.
 __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uint8_t *__restrict__ out,
                                                                EncWs ws, EncParams ep, DecParams dp)
 {
@@ -1641,47 +1642,74 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     for (int k = 0; k < kEncGroups; k++)
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
-    PatchHead h = patch_begin<kEncTile, kEncThreads>(ss.in[0], t0, dp);
-    DenseIn cur;
-    load_dense(ss.in[0], t0, rem, dp, cur);
-    load_wave_lut(esh, ep.lut);
-    for (uint32_t i = 0; i < ss.k; i++) {
-        const StreamIn si = ss.in[i];
-        const PatchFetch<kRedFetch> f = patch_fetch<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h);
-        PatchHead hn = h;
-        DenseIn nxt = cur;
-        if (i + 1 < ss.k) {
-            hn = patch_begin<kEncTile, kEncThreads>(ss.in[i + 1], t0, dp);
-            load_dense(ss.in[i + 1], t0, rem, dp, nxt);
+    for (uint32_t i = 0; i < ss.k; i += 2) {
+        const bool two = i + 1 < ss.k;                  // the same in every thread
+        const StreamIn s0 = ss.in[i];
+        const StreamIn s1 = ss.in[two ? i + 1 : i];
+        const PatchHead h0 = patch_begin<kEncTile, kEncThreads>(s0, t0, dp);
+        PatchHead h1 = h0;
+        DenseIn d0, d1;
+        load_dense(s0, t0, rem, dp, d0);
+        if (two) {
+            h1 = patch_begin<kEncTile, kEncThreads>(s1, t0, dp);
+            load_dense(s1, t0, rem, dp, d1);
         }
-        uint32_t ex[kEncGroups][2];
+        if (i == 0) load_wave_lut(esh, ep.lut);     // after the first data loads are in flight
+        const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kEncThreads, kRedFetch>(s0, t0, dp, h0);
+        PatchFetch<kRedFetch> f1 = f0;
+        f1.live = false;
+        if (two) f1 = patch_fetch<kEncTile, kEncThreads, kRedFetch>(s1, t0, dp, h1);
+        uint32_t e0[kEncGroups][2], e1[kEncGroups][2];
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) decode8_e(cur.cd[k], dec, ex[k]);
-        if (f.live) {
+        for (int k = 0; k < kEncGroups; k++) {
+            decode8_e(d0.cd[k], dec, e0[k]);
+            if (two) decode8_e(d1.cd[k], dec, e1[k]);
+        }
+        if (f0.live || f1.live) {
             // each thread rewrites only its own bytes here, which no thread
-            // reads after the previous input's second barrier but itself
+            // reads after the previous pair's second barrier but itself
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++) ex_put8(lds.ex.a, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
-            patch_put_offs(t0, dp, h, f, lds.ex.a);
+            for (int k = 0; k < kEncGroups; k++) {
+                const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+                if (f0.live) ex_put8(lds.ex.a, lo, e0[k]);
+                if (f1.live) ex_put8(lds.ex.b, lo, e1[k]);
+            }
+            if (f0.live) patch_put_offs(t0, dp, h0, f0, lds.ex.a);
+            if (f1.live) patch_put_offs(t0, dp, h1, f1, lds.ex.b);
             __syncthreads();
-            patch_scatter<kEncTile, kEncThreads, kRedFetch>(si, t0, dp, h, f, lds.ex.a);
+            if (f0.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(s0, t0, dp, h0, f0, lds.ex.a);
+            if (f1.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(s1, t0, dp, h1, f1, lds.ex.b);
             __syncthreads();
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++) ex_get8(lds.ex.a, (uint32_t)(k * (kEncThreads * 8) + tid * 8), ex[k]);
+            for (int k = 0; k < kEncGroups; k++) {
+                const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+                if (f0.live) ex_get8(lds.ex.a, lo, e0[k]);
+                if (f1.live) ex_get8(lds.ex.b, lo, e1[k]);
+            }
         }
+        // inputs i, then i + 1: the sums keep the input order
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++) {
             uint32_t y[4];
-            merge8(cur.sm[k].x, cur.sm[k].y, ex[k], y);
+            merge8(d0.sm[k].x, d0.sm[k].y, e0[k], y);
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const float v0 = __uint_as_float(y[q] << 16), v1 = __uint_as_float(y[q] & 0xFFFF0000u);
-                acc[k][2 * q] += v0;
-                acc[k][2 * q + 1] += v1;
+                acc[k][2 * q] += __uint_as_float(y[q] << 16);
+                acc[k][2 * q + 1] += __uint_as_float(y[q] & 0xFFFF0000u);
             }
         }
-        h = hn;
-        cur = nxt;
+        if (two) {
+#pragma unroll
+            for (int k = 0; k < kEncGroups; k++) {
+                uint32_t y[4];
+                merge8(d1.sm[k].x, d1.sm[k].y, e1[k], y);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    acc[k][2 * q] += __uint_as_float(y[q] << 16);
+                    acc[k][2 * q + 1] += __uint_as_float(y[q] & 0xFFFF0000u);
+                }
+            }
+        }
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
@@ -1945,7 +1973,7 @@ __global__ __launch_bounds__(kS15Threads) void k_s15_decode_tile(StreamIn s, uin
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t t0 = (uint64_t)blockIdx.x * kS15Tile;
     const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kS15Tile) ? p.n - t0 : (uint64_t)kS15Tile);
-    // round 1: M, the tile's chunk offsets (C <= tile: the tile starts a chunk)
+    // first loads: M, the tile's chunk offsets (C <= tile: the tile starts a chunk)
     const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
     const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs) + (t0 >> p.logC);
     const uint32_t nc = (uint32_t)(((t0 + rem - 1) >> p.logC) - (t0 >> p.logC) + 1);
@@ -2072,7 +2100,7 @@ __global__ __launch_bounds__(kZ7Threads) void kz_decode_tile(StreamIn s, uint16_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t t0 = (uint64_t)blockIdx.x * kZ7Tile;
     const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)kZ7Tile) ? p.n - t0 : (uint64_t)kZ7Tile);
-    // round 1: M, the tile's chunk offsets, the dense bytes
+    // first loads: M, the tile's chunk offsets, the dense bytes
     const uint64_t M = *reinterpret_cast<const uint64_t *>(s.base + 24);
     const uint32_t *offs = reinterpret_cast<const uint32_t *>(s.base + p.off_offs) + (t0 >> p.logC);
     const uint32_t nc = (uint32_t)(((t0 + rem - 1) >> p.logC) - (t0 >> p.logC) + 1);
