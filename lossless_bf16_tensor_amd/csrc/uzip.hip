@@ -380,6 +380,16 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
     return bf16x2_rne(a0 + b0, a1 + b1);
 }
 
+// bf16x2_rne without the NaN fix, which is final unless s0 or s1 is a NaN:
+// nan is set then (one unordered compare covers both). Callers redo the
+// values of a wave whose ballot of nan is not empty with bf16x2_rne.
+__device__ __forceinline__ uint32_t bf16x2_rne_fast(float s0, float s1, bool &nan)
+{
+    const f32x2 v = {s0, s1};
+    nan = __builtin_isunordered(s0, s1);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 
 // =========================================================== histogram ====
 // Exponent histogram of a sample of x: the first S values of every block of
@@ -1508,8 +1518,11 @@ union ReduceLds {
     EscBuf esc;
 };
 
-__global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, StreamIn sb, uint8_t *__restrict__ out,
-                                                             EncWs ws, EncParams ep, DecParams dp)
+// One tile of the pairwise reduce: both inputs decoded and patched, summed
+// in binary32, rounded to BF16 and encoded. Built for 5 waves per SIMD (at
+// most 96 registers, which the compiler meets without spilling).
+__global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, StreamIn sb, uint8_t *__restrict__ out,
+                                                                EncWs ws, EncParams ep, DecParams dp)
 {
     __shared__ EncShared esh;
     __shared__ ReduceLds lds;
@@ -1578,8 +1591,21 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_tile(StreamIn sa, Stream
         uint32_t ya[4], yb[4];
         merge8(sma[k].x, sma[k].y, ea[k], ya);
         merge8(smb[k].x, smb[k].y, eb[k], yb);
+        bool nan = false;
 #pragma unroll
-        for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[q], yb[q]);
+        for (int q = 0; q < 4; q++) {
+            const float s0 = __uint_as_float(ya[q] << 16) + __uint_as_float(yb[q] << 16);
+            const float s1 = __uint_as_float(ya[q] & 0xFFFF0000u) + __uint_as_float(yb[q] & 0xFFFF0000u);
+            bool n;
+            r[k][q] = bf16x2_rne_fast(s0, s1, n);
+            nan = nan || n;
+        }
+        if (__ballot(nan) != 0ull) {         // a NaN sum in the wave: the full rule for the group
+            merge8(sma[k].x, sma[k].y, ea[k], ya);
+            merge8(smb[k].x, smb[k].y, eb[k], yb);
+#pragma unroll
+            for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[q], yb[q]);
+        }
     }
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
@@ -1715,9 +1741,20 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        bool nan = false;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            bool n;
+            r[k][q] = bf16x2_rne_fast(acc[k][2 * q], acc[k][2 * q + 1], n);
+            nan = nan || n;
+        }
+        if (__ballot(nan) != 0ull) {         // a NaN sum in the wave: the full rule for the group
+#pragma unroll
+            for (int q = 0; q < 4; q++) r[k][q] = bf16x2_rne(acc[k][2 * q], acc[k][2 * q + 1]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; q++)
-            r[k][q] = (lo < rem) ? bf16x2_rne(acc[k][2 * q], acc[k][2 * q + 1]) : 0u;
+            if (lo >= rem) r[k][q] = 0u;
     }
     uint32_t cstart[kEncGroups];
     const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
