@@ -22,6 +22,7 @@ ratio, the escape rate, the per-kernel HIP-event durations and the roofline of
 the dominant kernel are extra fields.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -95,13 +96,20 @@ def cpu_baseline(x_np, calib_np, C, budget_s=12.0, sample=1 << 24):
         t_dec += t2 - t1
         reps += 1
     gb = 2 * xs.size * reps / 1e9
+    n = xs.size
+    m = int(np.frombuffer(s[24:32].tobytes(), dtype="<u8")[0])         # header: M, then total bytes
+    total = int(np.frombuffer(s[32:40].tobytes(), dtype="<u8")[0])
     return {
         "value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s",
         "cores": 1, "kind": "oracle",
-        "sample": f"first {xs.size} values of the same workload, {reps} round trips "
+        "sample": f"first {n} values of the same workload, {reps} round trips "
                   f"(encode {gb / t_enc:.4f} GB/s, decode {gb / t_dec:.4f} GB/s)",
         "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4),
-        "cpu": _cpu_model(),
+        "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__,
+        "sample_sha256": hashlib.sha256(xs.tobytes()).hexdigest()[:16],
+        "oracle_escape_rate": round(m / n, 6),
+        "oracle_ratio_payload": round(2 * n / (n + (n + 1) // 2 + 3 * m), 4),
+        "oracle_ratio_total": round(2 * n / total, 4),
     }
 
 
