@@ -1773,19 +1773,6 @@ static_assert(kEncThreads * k8Vals == kEncTile, "the FP8 encode tile is the BF16
 constexpr int k8DecThreads = 128;
 constexpr int k8DecTile = k8DecThreads * k8Vals;
 
-// Code-table entries of 4 exponents (one per byte, each < 32) from the 32
-// entries of T (8 dwords, in registers): one byte permute per 8-entry slice,
-// then two permutes choose the slice by bits 3 and 4 of the exponent.
-__device__ __forceinline__ uint32_t lut32(const uint32_t T[8], uint32_t e)
-{
-    const uint32_t sel = e & 0x07070707u;
-    const uint32_t c0 = perm(T[1], T[0], sel), c1 = perm(T[3], T[2], sel);
-    const uint32_t c2 = perm(T[5], T[4], sel), c3 = perm(T[7], T[6], sel);
-    const uint32_t p3 = ((e >> 1) & 0x04040404u) | 0x03020100u;
-    const uint32_t p4 = ((e >> 2) & 0x04040404u) | 0x03020100u;
-    return perm(perm(c3, c2, p3), perm(c1, c0, p3), p4);
-}
-
 // Three bits (sign, mantissa) of each byte of w, one per byte.
 __device__ __forceinline__ uint32_t signmant8x4(uint32_t w)
 {
@@ -1803,6 +1790,7 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
 {
     __shared__ uint32_t wtot[kEncThreads / 64];
     __shared__ EscBuf eb;
+    __shared__ uint32_t s_lut[8];          // the 32 code-table bytes
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
@@ -1826,14 +1814,16 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
             w[q] = v;
         }
     }
-    uint32_t T[8];
-#pragma unroll
-    for (int q = 0; q < 8; q++) T[q] = reinterpret_cast<const uint32_t *>(p.lut)[q];
+    // the table goes to LDS while the input loads are in flight
+    if (tid < 8) s_lut[tid] = reinterpret_cast<const uint32_t *>(p.lut)[tid];
+    __syncthreads();
+    const uint8_t *tb = reinterpret_cast<const uint8_t *>(s_lut);
     uint32_t L[8], E[8], A[8];
 #pragma unroll
     for (int q = 0; q < 8; q++) {
         E[q] = (w[q] >> 2) & 0x1F1F1F1Fu;
-        L[q] = lut32(T, E[q]);
+        L[q] = (uint32_t)tb[(w[q] >> 2) & 0x1Fu] | ((uint32_t)tb[(w[q] >> 10) & 0x1Fu] << 8) |
+               ((uint32_t)tb[(w[q] >> 18) & 0x1Fu] << 16) | ((uint32_t)tb[(w[q] >> 26) & 0x1Fu] << 24);
         A[q] = signmant8x4(w[q]);
     }
     if (lo + k8Vals > rem) {                     // tail: values past n are not escapes and take code 0
