@@ -534,6 +534,14 @@ struct alignas(16) EscBuf {
     uint8_t val[kEncTile];
 };
 
+// Copies the code table to the workgroup's first LDS copy (threads 0..63, 4
+// bytes each); a workgroup barrier must follow before any wave reads it.
+__device__ __forceinline__ void load_shared_lut(EncShared &sh, const uint8_t *lut)
+{
+    if (threadIdx.x < 64)
+        reinterpret_cast<uint32_t *>(sh.lut[0])[threadIdx.x] = reinterpret_cast<const uint32_t *>(lut)[threadIdx.x];
+}
+
 // Copies the code table to this wave's LDS copy (64 lanes x 4 bytes).
 __device__ __forceinline__ void load_wave_lut(EncShared &sh, const uint8_t *lut)
 {
@@ -616,7 +624,7 @@ __device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
     return (v >> (8 * q)) | (nxt << (24 - 8 * q));
 }
 
-template <int kCodes = kCodeNib>
+template <int kCodes = kCodeNib, bool kSharedLut = false>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
                                                       EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
@@ -633,8 +641,9 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         uint32_t L0 = 0, L1 = 0;
         if (lo < rem) {
-            L0 = lut4(sh.lut[wave], xw[k][0], xw[k][1]);
-            L1 = lut4(sh.lut[wave], xw[k][2], xw[k][3]);
+            const uint8_t *tbl = kSharedLut ? sh.lut[0] : sh.lut[wave];
+            L0 = lut4(tbl, xw[k][0], xw[k][1]);
+            L1 = lut4(tbl, xw[k][2], xw[k][3]);
             if (lo + 8 > rem) {       // tail group: words past n are not escapes
                 const uint32_t valid = rem - lo;   // 1..7
                 const uint64_t keep = (1ull << (8 * valid)) - 1ull;
@@ -1562,8 +1571,9 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
             ea[k][0] = ea[k][1] = eb[k][0] = eb[k][1] = 0u;
         }
     }
-    // the code table goes to LDS after the data loads are in flight
-    load_wave_lut(esh, ep.lut);
+    // the code table goes to LDS after the data loads are in flight (one copy
+    // for the workgroup: the barriers below publish it)
+    load_shared_lut(esh, ep.lut);
     // both inputs' escapes patched in one pass over two exponent tiles
     if (fa.live || fb.live) {
 #pragma unroll
@@ -1584,6 +1594,8 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
             if (fa.live) ex_get8(lds.ex.a, lo, ea[k]);
             if (fb.live) ex_get8(lds.ex.b, lo, eb[k]);
         }
+    } else {
+        __syncthreads();                       // publishes the code table
     }
     uint32_t r[kEncGroups][4];
 #pragma unroll
@@ -1610,7 +1622,7 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib, true>(r, t0, rem, out, ep, esh, lds.esc, cstart);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
@@ -1668,6 +1680,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     for (int k = 0; k < kEncGroups; k++)
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
+    bool synced = false;                                // a barrier has published the code table
     for (uint32_t i = 0; i < ss.k; i += 2) {
         const bool two = i + 1 < ss.k;                  // the same in every thread
         const StreamIn s0 = ss.in[i];
@@ -1680,7 +1693,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
             h1 = patch_begin<kEncTile, kEncThreads>(s1, t0, dp);
             load_dense(s1, t0, rem, dp, d1);
         }
-        if (i == 0) load_wave_lut(esh, ep.lut);     // after the first data loads are in flight
+        if (i == 0) load_shared_lut(esh, ep.lut);   // after the first data loads are in flight
         const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kEncThreads, kRedFetch>(s0, t0, dp, h0);
         PatchFetch<kRedFetch> f1 = f0;
         f1.live = false;
@@ -1712,6 +1725,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
                 if (f0.live) ex_get8(lds.ex.a, lo, e0[k]);
                 if (f1.live) ex_get8(lds.ex.b, lo, e1[k]);
             }
+            synced = true;
         }
         // inputs i, then i + 1: the sums keep the input order
 #pragma unroll
@@ -1756,8 +1770,9 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         for (int q = 0; q < 4; q++)
             if (lo >= rem) r[k][q] = 0u;
     }
+    if (!synced) __syncthreads();
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib, true>(r, t0, rem, out, ep, esh, lds.esc, cstart);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
