@@ -1026,7 +1026,9 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     }
     const uint32_t m = __builtin_amdgcn_readfirstlane(m_l);
     const uint32_t P = __builtin_amdgcn_readfirstlane(before + tp_l);
-    const uint64_t M = __builtin_amdgcn_readfirstlane(all);
+    // readfirstlane returns a signed int: through uint32_t, so that an M of
+    // 2^31 or more is not sign-extended
+    const uint64_t M = (uint32_t)__builtin_amdgcn_readfirstlane(all);
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // ---- the copies
