@@ -86,3 +86,72 @@ def test_maximum_size_round_trip_and_sampled_chunks():
     torch.cuda.empty_cache()
     assert ok
     say("round trip bit-exact")
+
+
+def test_maximum_size_fp8():
+    """The same at n = 2^32 - 1 E5M2 bytes. The codebook is calibrated on
+    bytes whose exponent is below 16 (bit 6 of the byte clear), so it holds
+    exponents 0..15; the data are uniform bytes with bit 6 also set in about
+    a fifth of them, so about 60 % of the exponents (16..31) are escapes and
+    M is well above 2^31."""
+    say(f"E5M2 n={N} C={C}: generating random bytes on the device")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4321)
+    x = torch.randint(0, 256, (N,), dtype=torch.uint8, device=DEV, generator=g)
+    step = 1 << 28
+    for i in range(0, N, step):
+        r = torch.randint(0, 256, (min(step, N - i),), dtype=torch.uint8, device=DEV, generator=g)
+        x[i:i + step] |= (r < 51).to(torch.uint8) << 6
+    cal = x[: 1 << 20].cpu().numpy() & 0xBF
+    ocb = oracle.fp8_calibrate(cal)
+    assert sorted(ocb.dec.tolist()) == list(range(16))
+    cb = uzip.codebook_from_hist(ocb.hist)
+    member = torch.zeros(32, dtype=torch.bool, device=DEV)
+    member[torch.from_numpy(ocb.dec.astype(np.int64)).to(DEV)] = True
+
+    say("encode")
+    out = uzip.fp8_encode(x, cb, C)
+    total, m = uzip.stream_bytes(out)
+    say(f"M={m} total={total}")
+    want_m = 0
+    for i in range(0, N, step):
+        e = (x[i:i + step].to(torch.int32) >> 2) & 0x1F
+        want_m += int((~member[e.long()]).sum().item())
+    assert m == want_m
+    assert (1 << 31) < m < (1 << 32)
+    nch = (N + C - 1) // C
+    sm_bytes = (3 * N + 7) // 8
+    off_codes = 256 + A(sm_bytes)
+    off_offs = off_codes + A((N + 1) // 2)
+    off_pos = off_offs + A(4 * (nch + 1))
+    off_val = off_pos + A(2 * m)
+    assert total == off_val + m
+
+    say("sampled chunks against the oracle")
+    for c in (0, (1 << 31) // C - 1, (1 << 31) // C, nch - 1):
+        lo = c * C
+        ln = min(C, N - lo)
+        mini = oracle.fp8_encode(x[lo:lo + ln].cpu().numpy(), C, ocb.dec)
+        mm = int(mini[24:32].view(np.uint64)[0])
+        msm = (3 * ln + 7) // 8
+        mcodes = 256 + A(msm)
+        mpos = mcodes + A((ln + 1) // 2) + A(8)          # one chunk: two offsets
+        mval = mpos + A(2 * mm)
+        sm = out[256 + 3 * lo // 8:256 + 3 * lo // 8 + msm].cpu().numpy()
+        codes = out[off_codes + lo // 2:off_codes + lo // 2 + (ln + 1) // 2].cpu().numpy()
+        o = out[off_offs + 4 * c:off_offs + 4 * (c + 2)].cpu().numpy().view(np.uint32).astype(np.int64)
+        pos = out[off_pos + 2 * o[0]:off_pos + 2 * o[1]].cpu().numpy().view(np.uint16)
+        val = out[off_val + o[0]:off_val + o[1]].cpu().numpy()
+        assert np.array_equal(sm, mini[256:256 + msm]), f"chunk {c}: sign-mantissa bits"
+        assert np.array_equal(codes, mini[mcodes:mcodes + (ln + 1) // 2]), f"chunk {c}: codes"
+        assert np.array_equal(pos, mini[mpos:mpos + 2 * mm].view(np.uint16)), f"chunk {c}: positions"
+        assert np.array_equal(val, mini[mval:mval + mm]), f"chunk {c}: exponents"
+
+    say("decode")
+    y = uzip.fp8_decode(out, cb, N, C, in_bytes=total)
+    del out
+    ok = torch.equal(y, x)
+    del x, y
+    torch.cuda.empty_cache()
+    assert ok
+    say("round trip bit-exact")
