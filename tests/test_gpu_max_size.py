@@ -155,3 +155,72 @@ def test_maximum_size_fp8():
     torch.cuda.empty_cache()
     assert ok
     say("round trip bit-exact")
+
+
+def test_maximum_size_reduce():
+    """The fused reduce at n = 2^32 - 1: two inputs of uniformly random words
+    (so the sum's escapes also number more than 2^31). Checked: the output's
+    M against a count over its decoded words, sampled chunks of the output
+    stream against the oracle's reduce of the same chunks of the inputs, and
+    2^20 sampled sums against the oracle's add."""
+    say(f"reduce n={N} C={C}: generating two inputs on the device")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    a = torch.randint(-32768, 32768, (N,), dtype=torch.int16, device=DEV, generator=g)
+    b = torch.randint(-32768, 32768, (N,), dtype=torch.int16, device=DEV, generator=g)
+    ocb = oracle.calibrate(a[: 1 << 20].cpu().numpy().view(np.uint16), b[: 1 << 20].cpu().numpy().view(np.uint16))
+    cb = uzip.codebook_from_hist(ocb.hist)
+    member = torch.zeros(256, dtype=torch.bool, device=DEV)
+    member[torch.from_numpy(ocb.dec.astype(np.int64)).to(DEV)] = True
+
+    say("encode both, reduce")
+    sa = uzip.encode(a, cb, C)
+    ta = uzip.stream_bytes(sa)[0]
+    sb = uzip.encode(b, cb, C)
+    tb = uzip.stream_bytes(sb)[0]
+    out = uzip.reduce_add(sa[:ta], sb[:tb], cb, N, C)
+    del sa, sb
+    total, m = uzip.stream_bytes(out)
+    say(f"M={m} total={total}")
+    nch = (N + C - 1) // C
+    off_codes = 256 + A(N)
+    off_offs = off_codes + A((N + 1) // 2)
+    off_pos = off_offs + A(4 * (nch + 1))
+    off_val = off_pos + A(2 * m)
+    assert total == off_val + m
+    assert (1 << 31) < m < (1 << 32)
+
+    say("sampled chunks against the oracle's reduce")
+    for c in (0, (1 << 31) // C - 1, (1 << 31) // C, nch - 1):
+        lo = c * C
+        ln = min(C, N - lo)
+        wa = a[lo:lo + ln].cpu().numpy().view(np.uint16)
+        wb = b[lo:lo + ln].cpu().numpy().view(np.uint16)
+        mini = oracle.reduce_add(oracle.encode(wa, C, ocb.dec), oracle.encode(wb, C, ocb.dec), ln, C, ocb.dec)
+        sec = oracle.sections(mini)
+        sm = out[256 + lo:256 + lo + ln].cpu().numpy()
+        codes = out[off_codes + lo // 2:off_codes + lo // 2 + (ln + 1) // 2].cpu().numpy()
+        o = out[off_offs + 4 * c:off_offs + 4 * (c + 2)].cpu().numpy().view(np.uint32).astype(np.int64)
+        pos = out[off_pos + 2 * o[0]:off_pos + 2 * o[1]].cpu().numpy().view(np.uint16)
+        val = out[off_val + o[0]:off_val + o[1]].cpu().numpy()
+        assert np.array_equal(sm, sec["sm"]), f"chunk {c}: sign-mantissa bytes"
+        assert np.array_equal(codes, sec["codes"]), f"chunk {c}: codes"
+        assert np.array_equal(pos, sec["pos"]), f"chunk {c}: positions"
+        assert np.array_equal(val, sec["val"]), f"chunk {c}: exponents"
+
+    say("decode, M over the decoded sums, sampled sums against the oracle")
+    y = uzip.decode(out, cb, N, C, in_bytes=total)
+    del out
+    want_m = 0
+    step = 1 << 28
+    for i in range(0, N, step):
+        e = (y[i:i + step].to(torch.int32) >> 7) & 0xFF
+        want_m += int((~member[e.long()]).sum().item())
+    assert m == want_m
+    idx = torch.randint(0, N, (1 << 20,), device=DEV, generator=g)
+    got = y[idx].cpu().numpy().view(np.uint16)
+    want = oracle.add_words(a[idx].cpu().numpy().view(np.uint16), b[idx].cpu().numpy().view(np.uint16))
+    del a, b, y
+    torch.cuda.empty_cache()
+    assert np.array_equal(got, want)
+    say("reduce checked")
