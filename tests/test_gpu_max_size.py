@@ -224,3 +224,40 @@ def test_maximum_size_reduce():
     torch.cuda.empty_cache()
     assert np.array_equal(got, want)
     say("reduce checked")
+
+
+@pytest.mark.parametrize("fmt,kept", [("s15", 15), ("z7", 7), ("t8", 8)])
+def test_maximum_size_ablation_formats(fmt, kept):
+    """The ablation formats at n = 2^32 - 1 uniformly random words: the
+    values outside the first `kept` codebook exponents (escapes or
+    zero-points) number more than 2^31. Checked: M against a count on the
+    device and the bit-exact round trip."""
+    say(f"{fmt} n={N} C={C}: generating uniform random words on the device")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    x = torch.randint(-32768, 32768, (N,), dtype=torch.int16, device=DEV, generator=g)
+    ocb = oracle.calibrate(x[: 1 << 20].cpu().numpy().view(np.uint16))
+    cb = uzip.codebook_from_hist(ocb.hist)
+    member = torch.zeros(256, dtype=torch.bool, device=DEV)
+    member[torch.from_numpy(ocb.dec[:kept].astype(np.int64)).to(DEV)] = True
+    enc = getattr(uzip, f"{fmt}_encode")
+    dec = getattr(uzip, f"{fmt}_decode")
+    say("encode")
+    out = enc(x, cb, C)
+    total, m = uzip.stream_bytes(out)
+    say(f"M={m} total={total}")
+    want_m = 0
+    step = 1 << 28
+    for i in range(0, N, step):
+        e = (x[i:i + step].to(torch.int32) >> 7) & 0xFF
+        want_m += int((~member[e.long()]).sum().item())
+    assert m == want_m
+    assert (1 << 31) < m < (1 << 32)
+    say("decode")
+    y = dec(out, cb, N, C, in_bytes=total)
+    del out
+    ok = torch.equal(y, x)
+    del x, y
+    torch.cuda.empty_cache()
+    assert ok
+    say("round trip bit-exact")
