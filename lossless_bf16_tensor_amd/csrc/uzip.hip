@@ -343,6 +343,26 @@ __device__ __forceinline__ void merge8(uint32_t sm0, uint32_t sm1, const uint32_
     y[3] = merge2(perm(e[1], sm1, 0x07030602u));
 }
 
+// The binary32 values of 8 words from their sign-mantissa bytes (sm0: words
+// 0..3, sm1: words 4..7, one per byte) and exponents (e[2]), without forming
+// the words: value j is the word shifted up 16 bits, i.e. the bytes
+// [0, 0, lo_j, hi_j] with hi_j = sign | e >> 1 and lo_j = (e & 1) << 7 |
+// mantissa. Each shift of the exponent bytes moves bits into a neighbouring
+// byte only at positions the sign-mantissa byte fills in the following bfi,
+// and one byte permute (selector 12 gives 0x00) places each value.
+__device__ __forceinline__ void floats8(uint32_t sm0, uint32_t sm1, const uint32_t e[2], float f[8])
+{
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t a = h ? sm1 : sm0;
+        const uint32_t hi = bfi(0x80808080u, a, e[h] >> 1);
+        const uint32_t lo = bfi(0x7F7F7F7Fu, a, e[h] << 7);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            f[4 * h + j] = __uint_as_float(perm(hi, lo, ((4u + j) << 24) | ((uint32_t)j << 16) | 0x0C0Cu));
+    }
+}
+
 // Decode 8 words: sm (8 sign-mantissa bytes in 2 dwords), codes (8 nibbles).
 __device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t codes,
                                         const uint32_t dec[4], uint32_t y[4])
@@ -369,15 +389,6 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float s0, float s1)
     if (s0 != s0) r = (r & 0xFFFF0000u) | 0x7FC0u;
     if (s1 != s1) r = (r & 0x0000FFFFu) | 0x7FC00000u;
     return r;
-}
-
-// Sum of the two BF16 words in each half of a and b: binary32 add, then
-// round to BF16.
-__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b)
-{
-    const float a0 = __uint_as_float(a << 16), a1 = __uint_as_float(a & 0xFFFF0000u);
-    const float b0 = __uint_as_float(b << 16), b1 = __uint_as_float(b & 0xFFFF0000u);
-    return bf16x2_rne(a0 + b0, a1 + b1);
 }
 
 // bf16x2_rne without the NaN fix, which is final unless s0 or s1 is a NaN:
@@ -1602,23 +1613,21 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
     uint32_t r[kEncGroups][4];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        uint32_t ya[4], yb[4];
-        merge8(sma[k].x, sma[k].y, ea[k], ya);
-        merge8(smb[k].x, smb[k].y, eb[k], yb);
+        float fa[8], fb[8];
+        floats8(sma[k].x, sma[k].y, ea[k], fa);
+        floats8(smb[k].x, smb[k].y, eb[k], fb);
         bool nan = false;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const float s0 = __uint_as_float(ya[q] << 16) + __uint_as_float(yb[q] << 16);
-            const float s1 = __uint_as_float(ya[q] & 0xFFFF0000u) + __uint_as_float(yb[q] & 0xFFFF0000u);
             bool n;
-            r[k][q] = bf16x2_rne_fast(s0, s1, n);
+            r[k][q] = bf16x2_rne_fast(fa[2 * q] + fb[2 * q], fa[2 * q + 1] + fb[2 * q + 1], n);
             nan = nan || n;
         }
         if (__ballot(nan) != 0ull) {         // a NaN sum in the wave: the full rule for the group
-            merge8(sma[k].x, sma[k].y, ea[k], ya);
-            merge8(smb[k].x, smb[k].y, eb[k], yb);
+            floats8(sma[k].x, sma[k].y, ea[k], fa);
+            floats8(smb[k].x, smb[k].y, eb[k], fb);
 #pragma unroll
-            for (int q = 0; q < 4; q++) r[k][q] = add_bf16x2(ya[q], yb[q]);
+            for (int q = 0; q < 4; q++) r[k][q] = bf16x2_rne(fa[2 * q] + fb[2 * q], fa[2 * q + 1] + fb[2 * q + 1]);
         }
     }
     // encode_dense_rank writes the escape list only after its first barrier,
@@ -1732,24 +1741,18 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         // inputs i, then i + 1: the sums keep the input order
 #pragma unroll
         for (int k = 0; k < kEncGroups; k++) {
-            uint32_t y[4];
-            merge8(d0.sm[k].x, d0.sm[k].y, e0[k], y);
+            float f[8];
+            floats8(d0.sm[k].x, d0.sm[k].y, e0[k], f);
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                acc[k][2 * q] += __uint_as_float(y[q] << 16);
-                acc[k][2 * q + 1] += __uint_as_float(y[q] & 0xFFFF0000u);
-            }
+            for (int j = 0; j < 8; j++) acc[k][j] += f[j];
         }
         if (two) {
 #pragma unroll
             for (int k = 0; k < kEncGroups; k++) {
-                uint32_t y[4];
-                merge8(d1.sm[k].x, d1.sm[k].y, e1[k], y);
+                float f[8];
+                floats8(d1.sm[k].x, d1.sm[k].y, e1[k], f);
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    acc[k][2 * q] += __uint_as_float(y[q] << 16);
-                    acc[k][2 * q + 1] += __uint_as_float(y[q] & 0xFFFF0000u);
-                }
+                for (int j = 0; j < 8; j++) acc[k][j] += f[j];
             }
         }
     }
