@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) void k_top16(const unsigned long long *__restr
 // ============================================================== encode ====
 // LDS of the encode back end.
 struct EncShared {
-    uint8_t lut[kEncThreads / 64][256];     // one copy per wave: no barrier to publish it
+    uint8_t lut[256];                       // the code table (one copy: a barrier publishes it)
     uint32_t wtot[kEncGroups][kEncThreads / 64];
 };
 // A tile's escapes in element order (compacted), written out with 16-byte
@@ -545,22 +545,23 @@ struct alignas(16) EscBuf {
     uint8_t val[kEncTile];
 };
 
-// Copies the code table to the workgroup's first LDS copy (threads 0..63, 4
-// bytes each); a workgroup barrier must follow before any wave reads it.
+// Copies the code table to LDS (threads 0..63, 4 bytes each); a workgroup
+// barrier must follow before any wave reads it.
 __device__ __forceinline__ void load_shared_lut(EncShared &sh, const uint8_t *lut)
 {
     if (threadIdx.x < 64)
-        reinterpret_cast<uint32_t *>(sh.lut[0])[threadIdx.x] = reinterpret_cast<const uint32_t *>(lut)[threadIdx.x];
+        reinterpret_cast<uint32_t *>(sh.lut)[threadIdx.x] = reinterpret_cast<const uint32_t *>(lut)[threadIdx.x];
 }
 
-// Copies the code table to this wave's LDS copy (64 lanes x 4 bytes).
-__device__ __forceinline__ void load_wave_lut(EncShared &sh, const uint8_t *lut)
+// Inclusive prefix sum of v within each row of 16 lanes (a lane whose
+// source lies before its row's start adds 0).
+__device__ __forceinline__ uint32_t row_inclusive_sum(uint32_t v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    reinterpret_cast<uint32_t *>(sh.lut[wave])[lane] = reinterpret_cast<const uint32_t *>(lut)[lane];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    return v;
 }
 
 // Inclusive prefix sum of v over the 64 lanes of a wave: row shifts by 1, 2,
@@ -568,10 +569,7 @@ __device__ __forceinline__ void load_wave_lut(EncShared &sh, const uint8_t *lut)
 // next row and lane 31 to the upper two rows (DPP row broadcasts).
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v)
 {
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v = row_inclusive_sum(v);
     v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
     v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
     return v;
@@ -635,7 +633,7 @@ __device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
     return (v >> (8 * q)) | (nxt << (24 - 8 * q));
 }
 
-template <int kCodes = kCodeNib, bool kSharedLut = false>
+template <int kCodes = kCodeNib>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
                                                       EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
@@ -652,9 +650,8 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         uint32_t L0 = 0, L1 = 0;
         if (lo < rem) {
-            const uint8_t *tbl = kSharedLut ? sh.lut[0] : sh.lut[wave];
-            L0 = lut4(tbl, xw[k][0], xw[k][1]);
-            L1 = lut4(tbl, xw[k][2], xw[k][3]);
+            L0 = lut4(sh.lut, xw[k][0], xw[k][1]);
+            L1 = lut4(sh.lut, xw[k][2], xw[k][3]);
             if (lo + 8 > rem) {       // tail group: words past n are not escapes
                 const uint32_t valid = rem - lo;   // 1..7
                 const uint64_t keep = (1ull << (8 * valid)) - 1ull;
@@ -714,16 +711,19 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         if (lane == 0) sh.wtot[k][wave] = wt;
     }
     __syncthreads();
-    // element order inside the tile is (group k, wave, lane, word)
-    uint32_t run = 0, base[kEncGroups];
+    // element order inside the tile is (group k, wave, lane, word): each row
+    // of 16 lanes takes the exclusive prefix of the group-major totals, and
+    // the wave reads its own entries out of it (wave-uniform values)
+    constexpr int kTot = kEncGroups * (kEncThreads / 64);
+    static_assert(kTot <= 16, "the wave totals fit one row of 16 lanes");
+    const uint32_t tv = (lane & 15) < kTot ? (&sh.wtot[0][0])[lane & 15] : 0u;
+    const uint32_t tinc = row_inclusive_sum(tv), texc = tinc - tv;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t base[kEncGroups];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-#pragma unroll
-        for (int w = 0; w < kEncThreads / 64; w++) {
-            if (w == wave) base[k] = run;
-            run += sh.wtot[k][w];
-        }
-    }
+    for (int k = 0; k < kEncGroups; k++)
+        base[k] = __builtin_amdgcn_readlane(texc, k * (kEncThreads / 64) + wv);
+    const uint32_t run = __builtin_amdgcn_readlane(tinc, kTot - 1);
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
@@ -806,8 +806,11 @@ __device__ __forceinline__ void encode_tile(const uint16_t *__restrict__ x, uint
             for (int q = 0; q < 4; q++) xw[k][q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
         }
     }
-    // the code table goes to LDS after the data loads are in flight
-    if (p.dlut) load_wave_lut(sh, p.dlut); else load_wave_lut(sh, p.lut);
+    // the code table goes to LDS after the data loads are in flight: one
+    // copy for the workgroup, at a constant address that the byte reads'
+    // offset absorbs
+    load_shared_lut(sh, p.dlut ? p.dlut : p.lut);
+    __syncthreads();
     uint32_t cstart[kEncGroups];
     const uint32_t m = encode_dense_rank<kCodes>(xw, t0, rem, out, p, sh, eb, cstart);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
@@ -1633,7 +1636,7 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib, true>(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
@@ -1777,7 +1780,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     }
     if (!synced) __syncthreads();
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib, true>(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
