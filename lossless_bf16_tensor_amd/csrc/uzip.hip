@@ -610,6 +610,17 @@ __device__ __forceinline__ uint32_t quad_planes(uint32_t v, uint32_t q)
     return perm(a1, a0, sel) | (perm(a3, a2, sel) << 16);
 }
 
+// Escape flags (bit 7 of each table byte) of 8 words whose table bytes are
+// L0 (words 0..3) and L1 (words 4..7), word j's at bit 4j + 3: the even
+// words' bytes and the odd words' bytes are each gathered into one dword,
+// and the even words' flags move down 4 bits, so that one loop over the set
+// bits of a whole group meets them in word order.
+__device__ __forceinline__ uint32_t escape_flags8(uint32_t L0, uint32_t L1)
+{
+    const uint32_t fe = perm(L1, L0, 0x06040200u), fo = perm(L1, L0, 0x07050301u);
+    return ((fe >> 4) & 0x08080808u) | (fo & 0x80808080u);
+}
+
 // Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
 // holds kEncGroups groups of 8 words (group k covers tile words
 // k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
@@ -730,19 +741,17 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         uint32_t rank = base[k] + pre[k];
         const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
         cstart[k] = (lo < rem && g0m == 0) ? rank : ~0u;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            uint32_t mask = Lw[k][h] & 0x80808080u;
-            if (mask == 0) continue;
-            // exponents of words 4h..4h+3, one per byte
-            const uint32_t ex = perm(xw[k][2 * h + 1] >> 7, xw[k][2 * h] >> 7, 0x06040200u);
-            while (mask) {
-                const uint32_t bit = __builtin_ctz(mask);          // 7, 15, 23 or 31
-                eb.pos[rank] = (uint16_t)(g0m + 4 * h + (bit >> 3));
-                eb.val[rank] = (uint8_t)(ex >> (bit - 7));
-                rank++;
-                mask &= mask - 1;
-            }
+        uint32_t mask = escape_flags8(Lw[k][0], Lw[k][1]);
+        if (mask == 0) continue;
+        // exponents of words 0..7, one per byte of ex1:ex0
+        const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
+        const uint32_t ex1 = perm(xw[k][3] >> 7, xw[k][2] >> 7, 0x06040200u);
+        while (mask) {
+            const uint32_t j = __builtin_ctz(mask) >> 2;           // the word, 0..7
+            eb.pos[rank] = (uint16_t)(g0m + j);
+            eb.val[rank] = (uint8_t)perm(ex1, ex0, j);
+            rank++;
+            mask &= mask - 1;
         }
     }
     return run;
@@ -1907,12 +1916,12 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     uint32_t cstart[1];
     cstart[0] = (lo < rem && g0m == 0) ? rank : ~0u;
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-        uint32_t mask = L[q] & 0x80808080u;
+    for (int q = 0; q < 8; q += 2) {               // 8 values per loop, in value order
+        uint32_t mask = escape_flags8(L[q], L[q + 1]);
         while (mask) {
-            const uint32_t bit = __builtin_ctz(mask);          // 7, 15, 23 or 31
-            eb.pos[rank] = (uint16_t)(g0m + 4 * q + (bit >> 3));
-            eb.val[rank] = (uint8_t)(E[q] >> (bit - 7));
+            const uint32_t j = __builtin_ctz(mask) >> 2;       // value 4q + j
+            eb.pos[rank] = (uint16_t)(g0m + 4 * q + j);
+            eb.val[rank] = (uint8_t)perm(E[q + 1], E[q], j);
             rank++;
             mask &= mask - 1;
         }
