@@ -293,15 +293,23 @@ __device__ __forceinline__ uint32_t lut4(const uint8_t *s_lut, uint32_t v0, uint
     return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
-// Pack the code nibbles of 8 table entries (bytes of L0, L1): word 2j in the
-// low nibble of byte j.
-__device__ __forceinline__ uint32_t pack_codes8(uint32_t L0, uint32_t L1)
+// The table bytes of 8 words, L0 (words 0..3) and L1 (words 4..7), gathered
+// by parity into two dwords (words 0, 2, 4, 6 and words 1, 3, 5, 7, one per
+// byte). From them, the packed code nibbles (word 2j in the low nibble of
+// byte j, word 2j + 1 in the high one) and the escape flags (bit 7 of each
+// table byte), word j's at bit 4j + 3 (the even words' flags moved down 4
+// bits), so that one loop over the set bits of a whole group meets them in
+// word order.
+struct Codes8 {
+    uint32_t codes, flags;
+};
+__device__ __forceinline__ Codes8 codes_flags8(uint32_t L0, uint32_t L1)
 {
-    uint32_t t0 = L0 & 0x0F0F0F0Fu;
-    uint32_t t1 = L1 & 0x0F0F0F0Fu;
-    t0 |= t0 >> 4;
-    t1 |= t1 >> 4;
-    return perm(t1, t0, 0x06040200u);
+    const uint32_t fe = perm(L1, L0, 0x06040200u), fo = perm(L1, L0, 0x07050301u);
+    Codes8 c;
+    c.codes = (fe & 0x0F0F0F0Fu) | ((fo & 0x0F0F0F0Fu) << 4);
+    c.flags = ((fe >> 4) & 0x08080808u) | (fo & 0x80808080u);
+    return c;
 }
 
 // Exponents of 4 words from 4 code nibbles held one per byte (values 0..15),
@@ -610,17 +618,6 @@ __device__ __forceinline__ uint32_t quad_planes(uint32_t v, uint32_t q)
     return perm(a1, a0, sel) | (perm(a3, a2, sel) << 16);
 }
 
-// Escape flags (bit 7 of each table byte) of 8 words whose table bytes are
-// L0 (words 0..3) and L1 (words 4..7), word j's at bit 4j + 3: the even
-// words' bytes and the odd words' bytes are each gathered into one dword,
-// and the even words' flags move down 4 bits, so that one loop over the set
-// bits of a whole group meets them in word order.
-__device__ __forceinline__ uint32_t escape_flags8(uint32_t L0, uint32_t L1)
-{
-    const uint32_t fe = perm(L1, L0, 0x06040200u), fo = perm(L1, L0, 0x07050301u);
-    return ((fe >> 4) & 0x08080808u) | (fo & 0x80808080u);
-}
-
 // Encode front half shared by k_encode_tile and k_reduce_tile. Each thread
 // holds kEncGroups groups of 8 words (group k covers tile words
 // k*kEncThreads*8 + tid*8 .. +8) in xw[k][0..3] (word 2q in the low half of
@@ -654,7 +651,7 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     uint8_t *smt = out + kHeader + t0;
     uint8_t *cdt = out + p.off_codes + t0 / 2;
     const uint32_t t0m = (uint32_t)(t0 & p.Cmask);      // offset of the tile in its chunk
-    uint32_t Lw[kEncGroups][2], sm[kEncGroups][2], cw[kEncGroups];
+    uint32_t fl[kEncGroups], sm[kEncGroups][2], cw[kEncGroups];
     // table lookups and dense values for every group, then all the stores
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
@@ -671,14 +668,14 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
                 L1 = (uint32_t)(both >> 32);
             }
         }
-        Lw[k][0] = L0;
-        Lw[k][1] = L1;
+        const Codes8 c8 = codes_flags8(L0, L1);
+        fl[k] = c8.flags;
         sm[k][0] = signmant4(xw[k][0], xw[k][1]);
         sm[k][1] = signmant4(xw[k][2], xw[k][3]);
         if constexpr (kCodes == kCodePlanes) cw[k] = quad_planes(plane_bytes8(L0, L1), (uint32_t)(lane & 3));
         else if constexpr (kCodes == kCodePack3)
             cw[k] = quad_pack3(pack12(L0 & 0x07070707u) | (pack12(L1 & 0x07070707u) << 12), (uint32_t)(lane & 3));
-        else cw[k] = pack_codes8(L0, L1);
+        else cw[k] = c8.codes;
     }
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
@@ -711,7 +708,7 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     uint32_t pre[kEncGroups];
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t cnt = __builtin_popcount(Lw[k][0] & 0x80808080u) + __builtin_popcount(Lw[k][1] & 0x80808080u);
+        const uint32_t cnt = __builtin_popcount(fl[k]);
         uint32_t wt = 0, pr = 0;
         if (__ballot(cnt != 0) != 0ull) {
             const uint32_t inc = wave_inclusive_sum(cnt);
@@ -741,7 +738,7 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         uint32_t rank = base[k] + pre[k];
         const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
         cstart[k] = (lo < rem && g0m == 0) ? rank : ~0u;
-        uint32_t mask = escape_flags8(Lw[k][0], Lw[k][1]);
+        uint32_t mask = fl[k];
         if (mask == 0) continue;
         // exponents of words 0..7, one per byte of ex1:ex0
         const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
@@ -1042,16 +1039,14 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
         all += v;
         if (q < g) before += v;
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        before += __shfl_xor(before, d, 64);
-        all += __shfl_xor(all, d, 64);
-    }
+    // the wave totals: lane 63 of DPP inclusive scans (no LDS round trips)
+    const uint32_t before_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
+    const uint32_t all_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
     const uint32_t m = __builtin_amdgcn_readfirstlane(m_l);
-    const uint32_t P = __builtin_amdgcn_readfirstlane(before + tp_l);
-    // readfirstlane returns a signed int: through uint32_t, so that an M of
-    // 2^31 or more is not sign-extended
-    const uint64_t M = (uint32_t)__builtin_amdgcn_readfirstlane(all);
+    const uint32_t P = __builtin_amdgcn_readfirstlane(before_w + tp_l);
+    // readlane returns a signed int: through uint32_t, so that an M of 2^31
+    // or more is not sign-extended
+    const uint64_t M = all_w;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // ---- the copies
@@ -1865,12 +1860,15 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
             for (int b = 0; b < 4; b++)
                 if (lo + 4 * q + b >= rem) L[q] &= ~(0xFFu << (8 * b));
     }
+    Codes8 c8[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) c8[q] = codes_flags8(L[2 * q], L[2 * q + 1]);
     if (lo < rem) {
         u32x4 cw;
-        cw.x = pack_codes8(L[0], L[1]);
-        cw.y = pack_codes8(L[2], L[3]);
-        cw.z = pack_codes8(L[4], L[5]);
-        cw.w = pack_codes8(L[6], L[7]);
+        cw.x = c8[0].codes;
+        cw.y = c8[1].codes;
+        cw.z = c8[2].codes;
+        cw.w = c8[3].codes;
         st_stream(cw, reinterpret_cast<u32x4 *>(out + p.off_codes + t0 / 2 + lo / 2));
         uint32_t c[8];
 #pragma unroll
@@ -1896,7 +1894,7 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     // order), the list in LDS
     uint32_t cnt = 0;
 #pragma unroll
-    for (int q = 0; q < 8; q++) cnt += __builtin_popcount(L[q] & 0x80808080u);
+    for (int q = 0; q < 4; q++) cnt += __builtin_popcount(c8[q].flags);
     uint32_t pre = 0, wt = 0;
     if (__ballot(cnt != 0) != 0ull) {
         const uint32_t inc = wave_inclusive_sum(cnt);
@@ -1917,7 +1915,7 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     cstart[0] = (lo < rem && g0m == 0) ? rank : ~0u;
 #pragma unroll
     for (int q = 0; q < 8; q += 2) {               // 8 values per loop, in value order
-        uint32_t mask = escape_flags8(L[q], L[q + 1]);
+        uint32_t mask = c8[q / 2].flags;
         while (mask) {
             const uint32_t j = __builtin_ctz(mask) >> 2;       // value 4q + j
             eb.pos[rank] = (uint16_t)(g0m + 4 * q + j);
