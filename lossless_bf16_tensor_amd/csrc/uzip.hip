@@ -858,12 +858,7 @@ __global__ __launch_bounds__(kThreads) void k_group_sums(EncWs ws, EncParams p)
     const uint64_t hi = (lo + per < ghi) ? lo + per : (lo < ghi ? ghi : lo);
     uint32_t sum = 0;
     for (uint64_t t = lo; t < hi; t++) sum += ws.counts[t];
-    uint32_t inc = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t u = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += u;
-    }
+    const uint32_t inc = wave_inclusive_sum(sum);
     if (lane == 63) s_wave[wave] = inc;
     __syncthreads();
     uint32_t run = inc - sum, total = 0;
