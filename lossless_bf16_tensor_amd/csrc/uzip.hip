@@ -1138,26 +1138,18 @@ struct StreamIn {
     uint64_t bytes;       // readable bytes at base
 };
 
-// Patch map of a tile of TILE values (the FP8 decode's form of the patch):
-// escape bitmap + each escape's exponent, and the tile's chunk offsets.
-template <int TILE>
-struct PatchShared {
-    uint32_t mask[TILE / 32];
-    uint8_t val[TILE];
-    uint32_t offs[TILE / 64 + 1];
-};
-
-// A tile's patch map, for the tile's words [t0, t0 + TILE) and NT threads,
-// is built in three steps, so that its dependent loads take two rounds and
+// A tile's patch, for the tile's words [t0, t0 + TILE) and NT threads, is
+// prepared in two steps, so that its dependent loads take two rounds and
 // overlap the tile's dense loads:
 //   patch_begin, before the dense loads: the stream's M and the tile's chunk
 //     offsets (one per thread);
 //   patch_fetch, after the dense loads are issued: the tile's escape range
 //     and its first FB * NT escapes, held in registers;
-//   patch_build: the LDS map (more escapes are loaded there, 4 * NT per
-//     round, only for tiles with over FB * NT of them); ends with a barrier.
-// Every thread of the workgroup calls all three. Values read from the stream
-// are clamped so that a corrupt stream cannot drive an access out of bounds.
+// then patch_scatter applies it to an LDS copy of the tile's exponents (more
+// escapes are loaded there, 4 * NT per round, only for tiles with over
+// FB * NT of them). Every thread of the workgroup calls all of them. Values
+// read from the stream are clamped so that a corrupt stream cannot drive an
+// access out of bounds.
 struct PatchHead {
     uint64_t M;
     uint32_t lo, hi;      // offsets at the tile's first chunk and past its last one
@@ -1256,73 +1248,7 @@ __device__ __forceinline__ PatchFetch<FB> patch_fetch(const StreamIn &s, uint64_
     return f;
 }
 
-// Marks escape j (position ps, exponent v) in the map of a tile of rem words
-// at t0.
-template <int TILE>
-__device__ __forceinline__ void patch_mark(PatchShared<TILE> &sh, uint64_t t0, uint32_t rem, const DecParams &p,
-                                           uint32_t nc, uint32_t j, uint32_t ps, uint32_t v)
-{
-    uint32_t li;
-    if (p.C <= (uint32_t)TILE) {
-        // last chunk q with offs[q] <= j
-        uint32_t a = 0, b = nc;             // offs[a] <= j < offs[b]
-        while (b - a > 1) {
-            const uint32_t mid = (a + b) >> 1;
-            if (sh.offs[mid] <= j) a = mid; else b = mid;
-        }
-        li = (a << p.logC) + ps;
-    } else {
-        li = ps - (uint32_t)(t0 & (uint64_t)(p.C - 1));   // wraps for a position before the tile
-    }
-    if (ps < p.C && li < rem) {
-        sh.val[li] = (uint8_t)v;
-        atomicOr(&sh.mask[li >> 5], 1u << (li & 31));
-    }
-}
-
-// Returns false (without a barrier) when the tile has no escapes.
-template <int TILE, int NT, int FB>
-__device__ bool patch_build(const StreamIn &s, uint64_t t0, const DecParams &p, const PatchHead &h,
-                            const PatchFetch<FB> &f, PatchShared<TILE> &sh)
-{
-    const int tid = threadIdx.x;
-    if (!f.live) return false;
-    const uint32_t rem = (uint32_t)((p.n - t0 < (uint64_t)TILE) ? p.n - t0 : (uint64_t)TILE);
-    const uint32_t nc = (p.C <= (uint32_t)TILE) ? (uint32_t)tile_chunks<TILE>(t0, p) : 0u;
-    const uint32_t E1 = f.E0 + f.cnt;
-    for (int i = tid; i < TILE / 32; i += NT) sh.mask[i] = 0;
-    if ((uint32_t)tid <= nc && p.C <= (uint32_t)TILE) sh.offs[tid] = h.mine > E1 ? E1 : h.mine;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < FB; u++) {
-        const uint32_t d = (uint32_t)(u * NT + tid);
-        if (d < f.cnt) patch_mark<TILE>(sh, t0, rem, p, nc, f.E0 + d, f.ps[u], f.vv[u]);
-    }
-    if (f.cnt > (uint32_t)(FB * NT)) {
-        const uint64_t M = h.M;
-        const uint16_t *pos = reinterpret_cast<const uint16_t *>(s.base + p.off_pos) + f.E0;
-        const uint8_t *val = s.base + p.off_pos + align256(2 * M) + f.E0;
-        for (uint64_t db = FB * NT; db < f.cnt; db += 4 * NT) {
-            uint32_t ps[4], vv[4];
-            // issue the loads of 4 escapes per thread before using any of them
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint64_t d = db + (uint64_t)(u * NT + tid);
-                ps[u] = (d < f.cnt) ? pos[d] : 0xFFFFFFFFu;
-                vv[u] = (d < f.cnt) ? val[d] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint64_t d = db + (uint64_t)(u * NT + tid);
-                if (d < f.cnt) patch_mark<TILE>(sh, t0, rem, p, nc, f.E0 + (uint32_t)d, ps[u], vv[u]);
-            }
-        }
-    }
-    __syncthreads();
-    return true;
-}
-
-// The exponent form of the patch, for BF16 tiles: each thread writes the
+// The exponent form of the patch (BF16 and FP8 tiles): each thread writes the
 // exponents it decoded (one byte per word) into an LDS copy of the tile,
 // every escape then overwrites its word's byte in place, and each thread
 // reads its bytes back before the merge. In order:
@@ -1922,29 +1848,10 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     stage_escapes<1, k8Vals>(m, cstart, t0, tile, ws, p, eb);
 }
 
-// Merge the LDS patch of a thread's 32 values (li0 a multiple of 32): each
-// dword of 4 values takes the exponent bytes whose patch bits are set.
-template <int TILE>
-__device__ __forceinline__ void apply_patch32(const PatchShared<TILE> &sh, uint32_t li0, uint32_t y[8])
-{
-    const uint32_t bits = sh.mask[li0 >> 5];
-    if (bits == 0) return;
-    const u32x4 va = *reinterpret_cast<const u32x4 *>(&sh.val[li0]);
-    const u32x4 vb = *reinterpret_cast<const u32x4 *>(&sh.val[li0 + 16]);
-    const uint32_t v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-        const uint32_t b = (bits >> (4 * q)) & 0xFu;
-        const uint32_t spread = (b * 0x00204081u) & 0x01010101u;      // bit j -> byte j
-        const uint32_t m = perm(0u, 0u, 0x0C0C0C0Cu + spread) & 0x7C7C7C7Cu;   // 0x00 / 0xFF per byte
-        y[q] = bfi(m, v[q] << 2, y[q]);
-    }
-}
-
 template <bool kPatch>
 __global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8_t *__restrict__ y, DecParams p)
 {
-    __shared__ PatchShared<k8DecTile> sh;
+    __shared__ ExpTile<k8DecTile> sh;
     __shared__ u32x4 xp[k8DecThreads / 64][128];     // one wave's 2 KiB of output, for contiguous stores
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t t0 = (uint64_t)blockIdx.x * k8DecTile;
@@ -1969,17 +1876,31 @@ __global__ __launch_bounds__(k8DecThreads) void k8_decode_tile(StreamIn s, uint8
                            (sm[1] >> 4) & 0xFFFu, (sm[1] >> 16) & 0xFFFu, (sm[1] >> 28) | ((sm[2] & 0xFFu) << 4),
                            (sm[2] >> 8) & 0xFFFu, sm[2] >> 20};
     const uint32_t cw[4] = {cd.x, cd.y, cd.z, cd.w};
-    uint32_t out[8];
+    uint32_t e[8];
 #pragma unroll
     for (int h = 0; h < 4; h++) {
         const uint32_t lo4 = cw[h] & 0x0F0F0F0Fu;             // codes of values 8h + 0, 2, 4, 6
         const uint32_t hi4 = (cw[h] >> 4) & 0x0F0F0F0Fu;      // 8h + 1, 3, 5, 7
-        out[2 * h] = merge8x4(unpack12(c[2 * h]), dec4(dec, perm(hi4, lo4, 0x05010400u)));
-        out[2 * h + 1] = merge8x4(unpack12(c[2 * h + 1]), dec4(dec, perm(hi4, lo4, 0x07030602u)));
+        e[2 * h] = dec4(dec, perm(hi4, lo4, 0x05010400u));
+        e[2 * h + 1] = dec4(dec, perm(hi4, lo4, 0x07030602u));
     }
-    if (kPatch) {
-        if (patch_build<k8DecTile, k8DecThreads, kDecFetch>(s, t0, p, ph, pf, sh)) apply_patch32(sh, lo, out);
+    if (kPatch && pf.live) {
+        // this thread's 32 exponent bytes to the LDS tile, where each escape
+        // overwrites its own, and back
+        u32x4 *ex4 = reinterpret_cast<u32x4 *>(&sh.ex[lo]);
+        ex4[0] = u32x4{e[0], e[1], e[2], e[3]};
+        ex4[1] = u32x4{e[4], e[5], e[6], e[7]};
+        patch_put_offs(t0, p, ph, pf, sh);
+        __syncthreads();
+        patch_scatter<k8DecTile, k8DecThreads, kDecFetch>(s, t0, p, ph, pf, sh);
+        __syncthreads();
+        const u32x4 r0 = ex4[0], r1 = ex4[1];
+        e[0] = r0.x; e[1] = r0.y; e[2] = r0.z; e[3] = r0.w;
+        e[4] = r1.x; e[5] = r1.y; e[6] = r1.z; e[7] = r1.w;
     }
+    uint32_t out[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) out[q] = merge8x4(unpack12(c[q]), e[q]);
     uint8_t *yt = y + t0;
     const uint32_t wlo = (uint32_t)wave * 64u * k8Vals;          // the wave's first value in the tile
     if (wlo + 64u * k8Vals <= rem) {
