@@ -548,10 +548,17 @@ struct EncShared {
 };
 // A tile's escapes in element order (compacted), written out with 16-byte
 // stores; room for every word of the tile.
-struct alignas(16) EscBuf {
-    uint16_t pos[kEncTile];
-    uint8_t val[kEncTile];
+template <int CAP>
+struct alignas(16) EscBufT {
+    uint16_t pos[CAP];
+    uint8_t val[CAP];
 };
+using EscBuf = EscBufT<kEncTile>;
+// The reduces' LDS escape list holds 3/4 of a tile, which lets 8 of their
+// workgroups share a CU instead of 6; a tile with more escapes lists them in
+// its staging slot directly.
+constexpr int kRedEscCap = 6144;
+static_assert(kRedEscCap % 16 == 0 && kRedEscCap <= kEncTile, "whole 16-byte copies");
 
 // Copies the code table to LDS (threads 0..63, 4 bytes each); a workgroup
 // barrier must follow before any wave reads it.
@@ -641,10 +648,11 @@ __device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
     return (v >> (8 * q)) | (nxt << (24 - 8 * q));
 }
 
-template <int kCodes = kCodeNib>
+template <int kCodes = kCodeNib, int CAP = kEncTile>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
-                                                      EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups])
+                                                      EncShared &sh, EscBufT<CAP> &eb, uint32_t cstart[kEncGroups],
+                                                      uint16_t *gpos = nullptr, uint8_t *gval = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the tile's bases (scalar); lanes index them with 32-bit offsets
@@ -735,22 +743,32 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
 #pragma unroll
     for (int k = 0; k < kEncGroups; k++) {
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
-        uint32_t rank = base[k] + pre[k];
-        const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
-        cstart[k] = (lo < rem && g0m == 0) ? rank : ~0u;
-        uint32_t mask = fl[k];
-        if (mask == 0) continue;
-        // exponents of words 0..7, one per byte of ex1:ex0
-        const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
-        const uint32_t ex1 = perm(xw[k][3] >> 7, xw[k][2] >> 7, 0x06040200u);
-        while (mask) {
-            const uint32_t j = __builtin_ctz(mask) >> 2;           // the word, 0..7
-            eb.pos[rank] = (uint16_t)(g0m + j);
-            eb.val[rank] = (uint8_t)perm(ex1, ex0, j);
-            rank++;
-            mask &= mask - 1;
-        }
+        cstart[k] = (lo < rem && ((t0m + lo) & p.Cmask) == 0) ? base[k] + pre[k] : ~0u;
     }
+    // the list, to LDS, or (a buffer smaller than the tile that the tile's
+    // escapes overflow: run is the same in every thread) to gpos/gval
+    auto list = [&](auto *dpos, auto *dval) {
+#pragma unroll
+        for (int k = 0; k < kEncGroups; k++) {
+            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            uint32_t rank = base[k] + pre[k];
+            const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
+            uint32_t mask = fl[k];
+            if (mask == 0) continue;
+            // exponents of words 0..7, one per byte of ex1:ex0
+            const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
+            const uint32_t ex1 = perm(xw[k][3] >> 7, xw[k][2] >> 7, 0x06040200u);
+            while (mask) {
+                const uint32_t j = __builtin_ctz(mask) >> 2;       // the word, 0..7
+                dpos[rank] = (uint16_t)(g0m + j);
+                dval[rank] = (uint8_t)perm(ex1, ex0, j);
+                rank++;
+                mask &= mask - 1;
+            }
+        }
+    };
+    if (CAP >= kEncTile || run <= (uint32_t)CAP) list(eb.pos, eb.val);
+    else list(gpos, gval);
     return run;
 }
 
@@ -762,9 +780,10 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
 // Infinity Cache.
 // G groups of GW values per thread (group k of thread tid starts at tile
 // value k*kEncThreads*GW + tid*GW).
-template <int G = kEncGroups, int GW = 8>
+template <int G = kEncGroups, int GW = 8, int CAP = kEncTile>
 __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[G], uint64_t t0,
-                                              uint64_t tile, const EncWs &ws, const EncParams &p, const EscBuf &eb)
+                                              uint64_t tile, const EncWs &ws, const EncParams &p,
+                                              const EscBufT<CAP> &eb)
 {
     const int tid = threadIdx.x;
     if (tid == 0) ws.counts[tile] = m;
@@ -776,7 +795,7 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
             if (cstart[k] != ~0u) cpt[lo >> p.logC] = cstart[k];
         }
     }
-    if (m == 0) return;
+    if (m == 0 || m > (uint32_t)CAP) return;           // none, or listed in the slot already
     __syncthreads();
     u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_pos + tile * kEncTile);
     const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
@@ -1465,7 +1484,7 @@ struct ExpTile2 {
 };
 union ReduceLds {
     ExpTile2 ex;
-    EscBuf esc;
+    EscBufT<kRedEscCap> esc;
 };
 
 // One tile of the pairwise reduce: both inputs decoded and patched, summed
@@ -1561,7 +1580,9 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib, kRedEscCap>(r, t0, rem, out, ep, esh, lds.esc, cstart,
+                                                               ws.stage_pos + tile * kEncTile,
+                                                               ws.stage_val + tile * kEncTile);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
@@ -1705,7 +1726,9 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     }
     if (!synced) __syncthreads();
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart);
+    const uint32_t m = encode_dense_rank<kCodeNib, kRedEscCap>(r, t0, rem, out, ep, esh, lds.esc, cstart,
+                                                               ws.stage_pos + tile * kEncTile,
+                                                               ws.stage_val + tile * kEncTile);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
