@@ -79,32 +79,52 @@ def entropy_bits(hist):
 
 
 def cpu_baseline(x_np, calib_np, C, budget_s=12.0, sample=1 << 24):
-    """The CPU oracle (single thread, plain C) on a bounded sample."""
+    """The CPU oracle (plain C, untuned) on a bounded sample of the workload:
+    once on one thread, then with the sample's chunks shared out over every
+    core this process may use (oracle/parallel.py: the unchanged oracle per
+    piece, a serial offsets prefix). The two streams must be identical."""
+    import concurrent.futures as cf
+
     import oracle
+    from oracle import parallel
     xs = np.ascontiguousarray(x_np[:sample])
-    cb = oracle.calibrate(calib_np)
-    reps, t_enc, t_dec = 0, 0.0, 0.0
-    t_start = time.perf_counter()
-    while reps < 5 and (reps == 0 or time.perf_counter() - t_start < budget_s):
-        t0 = time.perf_counter()
-        s = oracle.encode(xs, C, cb.dec)
-        t1 = time.perf_counter()
-        y = oracle.decode(s, xs.size, C, cb.dec)
-        t2 = time.perf_counter()
-        assert np.array_equal(y, xs)
-        t_enc += t1 - t0
-        t_dec += t2 - t1
-        reps += 1
-    gb = 2 * xs.size * reps / 1e9
     n = xs.size
-    m = int(np.frombuffer(s[24:32].tobytes(), dtype="<u8")[0])         # header: M, then total bytes
-    total = int(np.frombuffer(s[32:40].tobytes(), dtype="<u8")[0])
+    cb = oracle.calibrate(calib_np)
+
+    def timed(enc, dec):
+        reps, t_enc, t_dec = 0, 0.0, 0.0
+        t_start = time.perf_counter()
+        while reps < 5 and (reps == 0 or time.perf_counter() - t_start < budget_s):
+            t0 = time.perf_counter()
+            s = enc()
+            t1 = time.perf_counter()
+            y = dec(s)
+            t2 = time.perf_counter()
+            assert np.array_equal(y, xs)
+            t_enc += t1 - t0
+            t_dec += t2 - t1
+            reps += 1
+        gb = 2 * n * reps / 1e9
+        return s, reps, gb / t_enc, gb / t_dec, gb / (t_enc + t_dec)
+
+    s1, r1, e1, d1, v1 = timed(lambda: oracle.encode(xs, C, cb.dec), lambda s: oracle.decode(s, n, C, cb.dec))
+    threads = parallel.default_threads()
+    with cf.ThreadPoolExecutor(threads) as pool:
+        sp, rp, ep, dp, vp = timed(lambda: parallel.encode_parallel(xs, C, cb.dec, threads, pool),
+                                   lambda s: parallel.decode_parallel(s, n, C, cb.dec, threads, pool))
+    assert np.array_equal(sp, s1), "chunk-parallel oracle stream differs from the one-thread stream"
+    m = int(np.frombuffer(s1[24:32].tobytes(), dtype="<u8")[0])         # header: M, then total bytes
+    total = int(np.frombuffer(s1[32:40].tobytes(), dtype="<u8")[0])
     return {
-        "value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s",
-        "cores": 1, "kind": "oracle",
-        "sample": f"first {n} values of the same workload, {reps} round trips "
-                  f"(encode {gb / t_enc:.4f} GB/s, decode {gb / t_dec:.4f} GB/s)",
-        "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4),
+        "value": round(vp, 4), "unit": "GB/s",
+        "cores": threads, "kind": "oracle",
+        "sample": f"first {n} values of the same workload, {rp} round trips on {threads} threads "
+                  f"(chunks shared out, the unchanged oracle per piece; encode {ep:.4f} GB/s, decode {dp:.4f} GB/s); "
+                  f"one thread: {r1} round trips, encode {e1:.4f} GB/s, decode {d1:.4f} GB/s",
+        "encode_GBps": round(ep, 4), "decode_GBps": round(dp, 4),
+        "one_thread": {"value": round(v1, 4), "encode_GBps": round(e1, 4), "decode_GBps": round(d1, 4),
+                       "cores": 1},
+        "streams_identical": True,
         "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__,
         "sample_sha256": hashlib.sha256(xs.tobytes()).hexdigest()[:16],
         "oracle_escape_rate": round(m / n, 6),

@@ -100,12 +100,19 @@ typedef struct uzip_opts {
 /* ---------------------------------------------------------- host only -- */
 
 /* Largest stream for n values at chunk C: the format above with M = n.
- * Returns 0 when n or C is invalid. */
+ * The page's size formula B = N + N/2 + 3M ("SplitZip: Ultra Fast Lossless
+ * KV Compression for Disaggregated LLM Serving", section 3.2) is the payload;
+ * this adds the header, the chunk offsets and the padding, at the worst case
+ * M = n (4.5 bytes per value: the pages define no raw fallback for inputs
+ * that expand). M is known only after the encode, so every encode's out_cap
+ * must reach this. Returns 0 when n or C is invalid. */
 uint64_t uzip_max_bytes(uint64_t n, uint32_t chunk);
 
-/* Device workspace that uzip_encode / uzip_reduce_add / uzip_reduce_k need for (n, C): per-tile
- * escape counts and prefixes, and a staging area for each tile's escapes
- * (at most 3 bytes per value). Returns 0 when n or C is invalid. */
+/* Device workspace that uzip_encode / uzip_reduce_add / uzip_reduce_k need
+ * for (n, C). A format helper with no passage of its own: it is scratch for
+ * the escape arrays of section 3.2 (per-tile escape counts and prefixes, and
+ * a staging area for each tile's escape list) that lets the library allocate
+ * nothing itself. Returns 0 when n or C is invalid. */
 uint64_t uzip_workspace_bytes(uint64_t n, uint32_t chunk);
 
 /* Builds the codebook from a 256-bin exponent histogram (page section 3.3).
@@ -120,7 +127,11 @@ int uzip_codebook_from_hist(const uint64_t hist[256], uzip_codebook_t *cb);
  * Returns UZIP_OK, or UZIP_EINVAL (NULL, or entries not distinct). */
 int uzip_codebook_from_dec(const uint8_t dec[16], uzip_codebook_t *cb);
 
-/* Full structural check of a stream held in host memory (any format: BF16,
+/* A format helper with no passage of its own: the pages check a bit-exact
+ * round trip before they time anything ("SplitZip: Ultra Fast Lossless KV
+ * Compression for Disaggregated LLM Serving", section 4.1), and a receiver of
+ * an untrusted stream needs the same guarantee without the original tensor.
+ * Full structural check of a stream held in host memory (any format: BF16,
  * FP8 E5M2 with header flags 1, Top-15 + sentinel with flags 2, Top-7 +
  * zero-point with flags 3, Top-8 3-bit with flags 4): header fields, section sizes, zero padding,
  * offsets monotone and ending at M, positions ascending and inside their
@@ -283,7 +294,12 @@ int uzip_z7_decode_ex(const void *d_in, uint64_t in_bytes, uint64_t n, uint32_t 
                       const uzip_codebook_t *cb, uint16_t *d_y, const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Reads a device stream's header. Returns its size and M.
- * Either output pointer may be NULL. */
+ * Either output pointer may be NULL. A format helper: compression changes the
+ * size of the data a sender ships, so the transfer has to learn it from the
+ * stream ("UCCL-Zip: Lossless Compression Supercharged GPU Communication",
+ * section 4, the metadata of compressed sends); the size is also what the
+ * ratio 2N / total_bytes is reported on. Returns UZIP_OK, UZIP_EINVAL (NULL
+ * stream), UZIP_ECORRUPT (bad magic or version) or UZIP_EHIP. */
 int uzip_stream_bytes(const void *d_stream, uint64_t *total_bytes, uint64_t *m, hipStream_t s);
 
 /* async. Encode with a codebook calibrated on the input itself, entirely on
@@ -372,7 +388,8 @@ int uzip_reduce_k_ex(const void *const *d_in, const uint64_t *in_bytes, uint32_t
                      const uzip_opts_t *opts, hipStream_t s);
 
 /* blocking. Copies a device stream of `bytes` bytes to the host and runs
- * uzip_validate_host on it. */
+ * uzip_validate_host on it (the same format helper, for a stream in device
+ * memory). */
 int uzip_validate(const void *d_stream, uint64_t bytes, const uzip_codebook_t *cb, hipStream_t s);
 
 #ifdef __cplusplus

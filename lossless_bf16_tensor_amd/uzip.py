@@ -139,6 +139,17 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(n, dtype, device, stream=None, zero=False):
+    """A new device tensor that belongs to `stream` (None: the current
+    stream). The caching allocator hands a freed block only to later work on
+    the stream the block belongs to, so a temporary that a call's kernels use
+    on `stream` cannot be reused by other streams' work while they run."""
+    if stream is None:
+        return torch.zeros(n, dtype=dtype, device=device) if zero else torch.empty(n, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.zeros(n, dtype=dtype, device=device) if zero else torch.empty(n, dtype=dtype, device=device)
+
+
 def _ptr(t: torch.Tensor):
     if not t.is_cuda:
         raise ValueError("expected a device tensor")
@@ -219,7 +230,7 @@ def histogram(x: torch.Tensor, hist: torch.Tensor | None = None, block: int = 0,
     are counted."""
     w = _words(x)
     if hist is None:
-        hist = torch.zeros(256, dtype=torch.int64, device=w.device)
+        hist = _empty(256, torch.int64, w.device, stream, zero=True)
     if block:
         _check(lib().uzip_histogram_sampled(_ptr(w), w.numel(), block, sample, _ptr(hist), _stream(stream)),
                "histogram_sampled")
@@ -230,7 +241,7 @@ def histogram(x: torch.Tensor, hist: torch.Tensor | None = None, block: int = 0,
 
 def calibrate(x: torch.Tensor, stream=None) -> Codebook:
     w = _words(x)
-    ws = torch.empty(256, dtype=torch.int64, device=w.device)
+    ws = _empty(256, torch.int64, w.device, stream)
     cb = Codebook()
     _check(lib().uzip_calibrate(_ptr(w), w.numel(), _ptr(ws), ctypes.byref(cb), _stream(stream)),
            "calibrate")
@@ -247,9 +258,9 @@ def encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor |
     if cap == 0:
         raise UzipError(-1, f"bad n={n} or chunk={chunk}")
     if out is None:
-        out = torch.empty(cap, dtype=torch.uint8, device=w.device)
+        out = _empty(cap, torch.uint8, w.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, w.device, stream)
     o = _opts(events)
     _check(lib().uzip_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(),
                                 _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
@@ -267,9 +278,9 @@ def encode_online(x: torch.Tensor, chunk: int = 1024, block: int = 0, sample: in
     w = _words(x)
     n = w.numel()
     if out is None:
-        out = torch.empty(max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        out = _empty(max_bytes(n, chunk), torch.uint8, w.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, w.device, stream)
     if cb_out is not None and cb_out.numel() < ctypes.sizeof(Codebook):
         raise ValueError("cb_out is smaller than a codebook")
     o = _opts(events)
@@ -299,7 +310,7 @@ def decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torc
            stream=None) -> torch.Tensor:
     """Decode n words; returns an int16 tensor of BF16 bit patterns."""
     if out is None:
-        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+        out = _empty(n, torch.int16, buf.device, stream)
     w = _words(out)
     o = _opts(events, UZIP_F_SEPARATE_PATCH if separate_patch else 0)
     nb = buf.numel() if in_bytes is None else in_bytes
@@ -314,9 +325,9 @@ def reduce_add(a: torch.Tensor, b: torch.Tensor, cb: Codebook, n: int, chunk: in
     """Fused decode(a) + decode(b) -> binary32 add -> BF16 (RNE) -> encode."""
     cap = max_bytes(n, chunk)
     if out is None:
-        out = torch.empty(cap, dtype=torch.uint8, device=a.device)
+        out = _empty(cap, torch.uint8, a.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=a.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, a.device, stream)
     o = _opts(events)
     _check(lib().uzip_reduce_add_ex(_ptr(a), a.numel(), _ptr(b), b.numel(), n, chunk, ctypes.byref(cb),
                                     _ptr(out), out.numel(), _ptr(ws), ws.numel(),
@@ -331,9 +342,9 @@ def reduce_k(streams, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor
     encode."""
     k = len(streams)
     if out is None:
-        out = torch.empty(max_bytes(n, chunk), dtype=torch.uint8, device=streams[0].device)
+        out = _empty(max_bytes(n, chunk), torch.uint8, streams[0].device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=streams[0].device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, streams[0].device, stream)
     ptrs = (ctypes.c_void_p * max(k, 1))(*[_ptr(t) for t in streams])
     sizes = (ctypes.c_uint64 * max(k, 1))(*[t.numel() for t in streams])
     o = _opts(events)
@@ -367,14 +378,14 @@ def fp8_max_bytes(n: int, chunk: int) -> int:
 def fp8_histogram(x: torch.Tensor, hist: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     b = _bytes(x)
     if hist is None:
-        hist = torch.zeros(256, dtype=torch.int64, device=b.device)
+        hist = _empty(256, torch.int64, b.device, stream, zero=True)
     _check(lib().uzip_fp8_histogram(_ptr(b), b.numel(), _ptr(hist), _stream(stream)), "fp8_histogram")
     return hist
 
 
 def fp8_calibrate(x: torch.Tensor, stream=None) -> Codebook:
     b = _bytes(x)
-    ws = torch.empty(256, dtype=torch.int64, device=b.device)
+    ws = _empty(256, torch.int64, b.device, stream)
     cb = Codebook()
     _check(lib().uzip_fp8_calibrate(_ptr(b), b.numel(), _ptr(ws), ctypes.byref(cb), _stream(stream)),
            "fp8_calibrate")
@@ -386,9 +397,9 @@ def fp8_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tens
     b = _bytes(x)
     n = b.numel()
     if out is None:
-        out = torch.empty(fp8_max_bytes(n, chunk), dtype=torch.uint8, device=b.device)
+        out = _empty(fp8_max_bytes(n, chunk), torch.uint8, b.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=b.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, b.device, stream)
     o = _opts(events)
     _check(lib().uzip_fp8_encode_ex(_ptr(b), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
                                     ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "fp8_encode")
@@ -399,7 +410,7 @@ def fp8_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: 
                in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
     """Decode n E5M2 values; returns a uint8 tensor."""
     if out is None:
-        out = torch.empty(n, dtype=torch.uint8, device=buf.device)
+        out = _empty(n, torch.uint8, buf.device, stream)
     o = _opts(events)
     nb = buf.numel() if in_bytes is None else in_bytes
     _check(lib().uzip_fp8_decode_ex(_ptr(buf), nb, n, chunk, ctypes.byref(cb), _ptr(out),
@@ -417,9 +428,9 @@ def s15_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tens
     w = _words(x)
     n = w.numel()
     if out is None:
-        out = torch.empty(s15_max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        out = _empty(s15_max_bytes(n, chunk), torch.uint8, w.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, w.device, stream)
     o = _opts(events)
     _check(lib().uzip_s15_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
                                     ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "s15_encode")
@@ -429,7 +440,7 @@ def s15_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tens
 def s15_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
                in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
     if out is None:
-        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+        out = _empty(n, torch.int16, buf.device, stream)
     w = _words(out)
     o = _opts(events)
     nb = buf.numel() if in_bytes is None else in_bytes
@@ -448,9 +459,9 @@ def z7_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tenso
     w = _words(x)
     n = w.numel()
     if out is None:
-        out = torch.empty(z7_max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        out = _empty(z7_max_bytes(n, chunk), torch.uint8, w.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, w.device, stream)
     o = _opts(events)
     _check(lib().uzip_z7_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
                                    ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "z7_encode")
@@ -460,7 +471,7 @@ def z7_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tenso
 def z7_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
               in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
     if out is None:
-        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+        out = _empty(n, torch.int16, buf.device, stream)
     w = _words(out)
     o = _opts(events)
     nb = buf.numel() if in_bytes is None else in_bytes
@@ -479,9 +490,9 @@ def t8_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tenso
     w = _words(x)
     n = w.numel()
     if out is None:
-        out = torch.empty(t8_max_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        out = _empty(t8_max_bytes(n, chunk), torch.uint8, w.device, stream)
     if ws is None:
-        ws = torch.empty(workspace_bytes(n, chunk), dtype=torch.uint8, device=w.device)
+        ws = _empty(workspace_bytes(n, chunk), torch.uint8, w.device, stream)
     o = _opts(events)
     _check(lib().uzip_t8_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _ptr(ws),
                                    ws.numel(), ctypes.byref(o) if o else None, _stream(stream)), "t8_encode")
@@ -491,7 +502,7 @@ def t8_encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tenso
 def t8_decode(buf: torch.Tensor, cb: Codebook, n: int, chunk: int = 1024, out: torch.Tensor | None = None,
               in_bytes: int | None = None, events=None, stream=None) -> torch.Tensor:
     if out is None:
-        out = torch.empty(n, dtype=torch.int16, device=buf.device)
+        out = _empty(n, torch.int16, buf.device, stream)
     w = _words(out)
     o = _opts(events)
     nb = buf.numel() if in_bytes is None else in_bytes

@@ -57,3 +57,36 @@ def test_encode_decode_reduce_on_two_streams():
             assert np.array_equal(outs[i][:want[i].size].cpu().numpy(), want[i]), f"rep {rep} stream {i}: encode"
             assert np.array_equal(ys[i].cpu().numpy().view(np.uint16), xs[i]), f"rep {rep} stream {i}: decode"
             assert np.array_equal(reds[i][:want_r[i].size].cpu().numpy(), want_r[i]), f"rep {rep} stream {i}: reduce"
+
+
+def test_stream_argument_without_buffers():
+    """Calls given stream= and no out/ws: the binding's temporaries belong
+    to that stream, so allocations made meanwhile on the current stream (and
+    filled there) cannot take their memory while the call's kernels run."""
+    w = workloads.config(2, small=True)
+    C = 1024
+    xs = [w.x, np.roll(w.x, w.x.size // 5)]
+    n = xs[0].size
+    ocb = oracle.calibrate(w.calib)
+    cb = uzip.codebook_from_hist(ocb.hist)
+    want = [oracle.encode(x, C, ocb.dec) for x in xs]
+    want_r = oracle.reduce_add(want[0], want[1], n, C, ocb.dec)
+    xd = [to_dev(x) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cap = uzip.max_bytes(n, C)
+    wsb = uzip.workspace_bytes(n, C)
+    for rep in range(3):
+        outs = [uzip.encode(xd[i], cb, C, stream=streams[i]) for i in range(2)]
+        # same-sized allocations on the current stream, overwritten at once
+        junk = [torch.full((sz,), 0x5A, dtype=torch.uint8, device=DEV) for sz in (wsb, cap, wsb, cap)]
+        ys = [uzip.decode(outs[i], cb, n, C, stream=streams[i]) for i in range(2)]
+        streams[1].wait_stream(streams[0])
+        red = uzip.reduce_add(outs[0], outs[1], cb, n, C, stream=streams[1])
+        junk += [torch.full((sz,), 0xA5, dtype=torch.uint8, device=DEV) for sz in (wsb, cap)]
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert np.array_equal(outs[i][:want[i].size].cpu().numpy(), want[i]), f"rep {rep} stream {i}: encode"
+            assert np.array_equal(ys[i].cpu().numpy().view(np.uint16), xs[i]), f"rep {rep} stream {i}: decode"
+        assert np.array_equal(red[:want_r.size].cpu().numpy(), want_r), f"rep {rep}: reduce"
+        del junk, outs, ys, red
