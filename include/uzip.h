@@ -64,6 +64,7 @@ extern "C" {
 #define UZIP_ECORRUPT   -3   /* stream fails a structural check */
 #define UZIP_ECODEBOOK  -4   /* stream's dec[16] differs from the codebook */
 #define UZIP_EHIP       -5   /* a HIP runtime call or kernel launch failed */
+#define UZIP_ESCRATCH   -6   /* input too large for uzip_encode_noalloc's fixed scratch */
 
 /* Codebook: the three tables of the page's offline calibration (section 3.3)
  * and the histogram they came from. Plain data, owned by the caller. It is
@@ -183,6 +184,22 @@ int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_code
 int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
                    void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes,
                    const uzip_opts_t *opts, hipStream_t s);
+
+/* async. uzip_encode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The call allocates nothing: its workspace
+ * is a fixed array of UZIP_NOALLOC_SCRATCH_BYTES in the library's device
+ * memory, one per GPU, held from the library's first use on that GPU until
+ * the process ends. Inputs with uzip_workspace_bytes(n, chunk) larger than
+ * that are rejected with UZIP_ESCRATCH before anything is enqueued. Every call
+ * on one GPU uses that GPU's array, so calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be serialised by the caller.
+ * The array keeps the last call's contents; the encode reads no workspace
+ * byte it has not written in the same call. Output, arguments and the other
+ * errors are those of uzip_encode (the device is the current one). */
+#define UZIP_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int uzip_encode_noalloc(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                        void *d_out, uint64_t out_cap, hipStream_t s);
 
 /* ------------------------------------------------ FP8 E5M2 variant ---- */
 /* "SplitZip: Ultra Fast Lossless KV Compression for Disaggregated LLM

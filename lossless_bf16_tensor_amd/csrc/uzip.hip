@@ -48,6 +48,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "uzip.h"
 
 namespace {
@@ -2504,6 +2506,36 @@ void launch_hist(const void *d_x, uint64_t n, uint64_t block, uint64_t sample, u
     else k_hist<1><<<grid, kThreads, 0, s>>>(x, n, block, sample, h);
 }
 
+// Workspace of uzip_encode_noalloc: one fixed array per GPU, in the code
+// object's device memory, that every call on that GPU shares. In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the
+// device address that hipGetSymbolAddress returns for the current device
+// (each device holds its own copy at its own address), looked up once per
+// device and cached.
+constexpr uint64_t kScratchBytes = UZIP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return UZIP_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned16(p)) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return UZIP_OK;
+}
+
 // Host-side structural check (same rules as the header comment of
 // uzip_validate_host).
 uint16_t rd16(const uint8_t *p) { uint16_t v; memcpy(&v, p, 2); return v; }
@@ -2703,6 +2735,8 @@ const char *uzip_strerror(int code)
     case UZIP_ECORRUPT: return "stream is malformed";
     case UZIP_ECODEBOOK: return "stream was encoded with a different codebook";
     case UZIP_EHIP: return g_hip_err[0] ? g_hip_err : "HIP runtime error";
+    case UZIP_ESCRATCH: return "input too large for uzip_encode_noalloc: its workspace exceeds the fixed "
+                               "UZIP_NOALLOC_SCRATCH_BYTES scratch (use uzip_encode with a workspace)";
     default: return "unknown error";
     }
 }
@@ -3063,6 +3097,18 @@ int uzip_encode(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_code
                 void *d_out, uint64_t out_cap, void *d_ws, uint64_t ws_bytes, hipStream_t s)
 {
     return uzip_encode_ex(d_x, n, chunk, cb, d_out, out_cap, d_ws, ws_bytes, nullptr, s);
+}
+
+int uzip_encode_noalloc(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
+                        void *d_out, uint64_t out_cap, hipStream_t s)
+{
+    // the size check comes before any HIP call, so an input that is too
+    // large is rejected without touching the device
+    if (valid_nc(n, chunk) && uzip_workspace_bytes(n, chunk) > kScratchBytes) return UZIP_ESCRATCH;
+    void *ws = nullptr;
+    const int rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+    return uzip_encode_ex(d_x, n, chunk, cb, d_out, out_cap, ws, kScratchBytes, nullptr, s);
 }
 
 int uzip_stream_bytes(const void *d_stream, uint64_t *total_bytes, uint64_t *m, hipStream_t s)

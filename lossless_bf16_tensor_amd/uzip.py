@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libuzip.so")
 UZIP_VERSION = 1
 UZIP_F_SEPARATE_PATCH = 0x1
 ERRORS = {0: "UZIP_OK", -1: "UZIP_EINVAL", -2: "UZIP_ENOSPC", -3: "UZIP_ECORRUPT",
-          -4: "UZIP_ECODEBOOK", -5: "UZIP_EHIP"}
+          -4: "UZIP_ECODEBOOK", -5: "UZIP_EHIP", -6: "UZIP_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20        # UZIP_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/uzip.h declares
 EXPORTS = (
@@ -31,6 +32,7 @@ EXPORTS = (
     "uzip_s15_max_bytes", "uzip_s15_encode", "uzip_s15_encode_ex", "uzip_s15_decode", "uzip_s15_decode_ex",
     "uzip_z7_max_bytes", "uzip_z7_encode", "uzip_z7_encode_ex", "uzip_z7_decode", "uzip_z7_decode_ex",
     "uzip_t8_max_bytes", "uzip_t8_encode", "uzip_t8_encode_ex", "uzip_t8_decode", "uzip_t8_decode_ex",
+    "uzip_encode_noalloc",
 )
 
 MAX_K = 16                      # UZIP_MAX_K
@@ -86,6 +88,7 @@ def lib():
         "uzip_calibrate": (i32, [vp, u64, vp, cbp, vp]),
         "uzip_encode": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, vp]),
         "uzip_encode_ex": (i32, [vp, u64, u32, cbp, vp, u64, vp, u64, op, vp]),
+        "uzip_encode_noalloc": (i32, [vp, u64, u32, cbp, vp, u64, vp]),
         "uzip_encode_online": (i32, [vp, u64, u32, u64, u64, vp, vp, u64, vp, u64, vp]),
         "uzip_encode_online_ex": (i32, [vp, u64, u32, u64, u64, vp, vp, u64, vp, u64, op, vp]),
         "uzip_stream_bytes": (i32, [vp, vp, vp, vp]),
@@ -265,6 +268,20 @@ def encode(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor |
     _check(lib().uzip_encode_ex(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(),
                                 _ptr(ws), ws.numel(), ctypes.byref(o) if o else None, _stream(stream)),
            "encode")
+    return out
+
+
+def encode_noalloc(x: torch.Tensor, cb: Codebook, chunk: int = 1024, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """encode() through uzip_encode_noalloc: the library allocates nothing
+    and uses its fixed per-GPU scratch as the workspace (calls on one GPU
+    must not overlap). With out given, this allocates nothing either."""
+    w = _words(x)
+    n = w.numel()
+    if out is None:
+        out = _empty(max_bytes(n, chunk), torch.uint8, w.device, stream)
+    _check(lib().uzip_encode_noalloc(_ptr(w), n, chunk, ctypes.byref(cb), _ptr(out), out.numel(), _stream(stream)),
+           "encode_noalloc")
     return out
 
 

@@ -306,3 +306,14 @@ def test_device_calls_reject_bad_args_without_gpu():
     assert L.uzip_histogram(p, 0, p, None) == -1
     assert L.uzip_calibrate(p, 100, None, cbr, None) == -1
     assert L.uzip_validate(None, 100, cbr, None) == -1
+
+
+def test_noalloc_rejects_inputs_beyond_its_scratch_on_the_host():
+    # the size check comes before any HIP call: no device is needed here
+    L = uzip.lib()
+    cb = uzip.codebook_from_hist(np.arange(256, dtype=np.uint64))
+    for n, C in [((1 << 32) - 1, 1024), (1 << 26, 64)]:
+        assert uzip.workspace_bytes(n, C) > uzip.NOALLOC_SCRATCH_BYTES
+        rc = L.uzip_encode_noalloc(None, n, C, ctypes.byref(cb), None, 0, None)
+        assert rc == -6
+        assert b"UZIP_NOALLOC_SCRATCH_BYTES" in L.uzip_strerror(rc)
