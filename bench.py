@@ -54,6 +54,19 @@ def algorithmic_bytes(n, C, m):
     }
 
 
+def stream_bytes_alg(n, C, m):
+    """Algorithmic bytes of one compressed stream: the payload N + N/2 + 3M
+    plus the chunk offsets and the header."""
+    nch = (n + C - 1) // C
+    return n + (n + 1) // 2 + 3 * m + 4 * (nch + 1) + 256
+
+
+def stats_ms(vals):
+    v = np.asarray(vals, dtype=np.float64)
+    return {"mean": round(float(v.mean()), 4), "median": round(float(np.median(v)), 4),
+            "min": round(float(v.min()), 4)}
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (two rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, each scaled by a
@@ -258,6 +271,62 @@ def table(uzip, torch, reps=10, flush_mib=1024):
         torch.cuda.empty_cache()
 
 
+def reduce_config5(uzip, torch, dev, flush, C, reps=10):
+    """The fused reduce at its own configuration: two 2^29-value gradient
+    buffers (seeded recipe), one codebook from both histograms, both encoded,
+    then decode-add-RNE-reencode timed with events between its kernels."""
+    import workloads
+    log("reduce: generating two 2^29-value gradient buffers")
+    w = workloads.config(5)
+    xa = torch.from_numpy(w.x[0].view(np.int16)).to(dev)
+    xb = torch.from_numpy(w.x[1].view(np.int16)).to(dev)
+    n = xa.numel()
+    hist = uzip.histogram(xb, uzip.histogram(xa))
+    cb = uzip.codebook_from_hist(hist.cpu().numpy().astype(np.uint64))
+    ws = torch.empty(uzip.workspace_bytes(n, C), dtype=torch.uint8, device=dev)
+    sa = uzip.encode(xa, cb, C, ws=ws)
+    sb = uzip.encode(xb, cb, C, ws=ws)
+    ta, ma = uzip.stream_bytes(sa)
+    tb, mb = uzip.stream_bytes(sb)
+    del xa, xb
+    outr = torch.empty(uzip.max_bytes(n, C), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        uzip.reduce_add(sa[:ta], sb[:tb], cb, n, C, out=outr, ws=ws)
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for row in rev + oev:
+        for e in row:
+            e.record()
+    for k in range(reps):                       # events between the kernels
+        flush()
+        uzip.reduce_add(sa[:ta], sb[:tb], cb, n, C, out=outr, ws=ws, events=rev[k])
+    for k in range(reps):                       # events around the call only
+        flush()
+        oev[k][0].record()
+        uzip.reduce_add(sa[:ta], sb[:tb], cb, n, C, out=outr, ws=ws)
+        oev[k][1].record()
+    torch.cuda.synchronize()
+    op = [oev[k][0].elapsed_time(oev[k][1]) for k in range(reps)]
+    kt = float(np.mean([rev[k][0].elapsed_time(rev[k][1]) for k in range(reps)]))
+    kg = float(np.mean([rev[k][1].elapsed_time(rev[k][2]) for k in range(reps)]))
+    kp = float(np.mean([rev[k][2].elapsed_time(rev[k][3]) for k in range(reps)]))
+    tr, mr = uzip.stream_bytes(outr)
+    alg = stream_bytes_alg(n, C, ma) + stream_bytes_alg(n, C, mb) + stream_bytes_alg(n, C, mr)
+    t = float(np.mean(op))
+    # the tile kernel's own bytes: both inputs' streams read, the result's
+    # dense sections written (its escapes go through the staging slots)
+    kbytes = stream_bytes_alg(n, C, ma) + stream_bytes_alg(n, C, mb) + n + (n + 1) // 2
+    del sa, sb, outr, ws
+    return {"workload": f"{w.name}: two BF16 gradient buffers of {n} values, codebook from both histograms",
+            "n": n, "chunk": C, "ms": stats_ms(op),
+            "GBps_uncompressed_in": round(2 * 2 * n / (t * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": alg, "op_frac": round(alg / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "kernels_ms": {"k_reduce_tile": round(kt, 4), "k_group_sums": round(kg, 4), "k_place_escapes": round(kp, 4)},
+            "k_reduce_tile_frac": round(kbytes / (kt * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "escape_rate_inputs": [round(ma / n, 6), round(mb / n, 6)], "escape_rate_out": round(mr / n, 6),
+            "stream_bytes": [ta, tb, tr]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,19 +488,56 @@ def main():
         uzip.decode(out, cb, n, C, out=y, in_bytes=total)
         oevs[k][3].record()
     torch.cuda.synchronize()
-    t_enc = float(np.mean([oevs[k][0].elapsed_time(oevs[k][1]) for k in range(args.steps)]))
-    t_dec = float(np.mean([oevs[k][2].elapsed_time(oevs[k][3]) for k in range(args.steps)]))
+    enc_list = [oevs[k][0].elapsed_time(oevs[k][1]) for k in range(args.steps)]
+    dec_list = [oevs[k][2].elapsed_time(oevs[k][3]) for k in range(args.steps)]
+    t_enc = float(np.mean(enc_list))
+    t_dec = float(np.mean(dec_list))
     ab = algorithmic_bytes(n, C, m)
-    dom = max(("k_encode_tile", "k_decode_tile"), key=lambda k: kern[k])
+    # roofline per op: each op's whole-call fraction and its dominant
+    # (longest) kernel's own fraction; the line's roofline is the slower op's
+    op_frac = {"encode": ab["encode"] / (t_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "decode": ab["decode"] / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    op_kernels = {"encode": ("k_encode_tile", "k_group_sums", "k_place_escapes"), "decode": ("k_decode_tile",)}
+    roofline_ops = {}
+    for op_name, ks in op_kernels.items():
+        dk = max(ks, key=lambda k: kern[k])
+        kb = ab.get(dk)
+        roofline_ops[op_name] = {
+            "op_ms": stats_ms(enc_list if op_name == "encode" else dec_list),
+            "op_algorithmic_bytes": ab[op_name], "op_frac": round(op_frac[op_name], 4),
+            "dominant_kernel": dk, "kernel_ms_mean": round(kern[dk], 4),
+            "kernel_algorithmic_bytes": kb,
+            "kernel_frac": round(kb / (kern[dk] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if kb else None,
+            "kernels_ms": {k: round(kern[k], 4) for k in ks}}
+    slow_op = min(op_frac, key=op_frac.get)
+    dom = roofline_ops[slow_op]["dominant_kernel"]
     achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
+
+    # --- a plain device copy of 1 GiB in the same run, for context: the
+    # rate a read-and-write stream reaches on this machine ---
+    cpy_a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    cpy_b = torch.empty_like(cpy_a)
+    cpy_b.copy_(cpy_a)
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for k in range(5):
+        flush()
+        cev[k][0].record()
+        cpy_b.copy_(cpy_a)
+        cev[k][1].record()
+    torch.cuda.synchronize()
+    t_cpy = [cev[k][0].elapsed_time(cev[k][1]) for k in range(5)]
+    copy_gbps = 2 * cpy_a.numel() * 2 / (float(np.median(t_cpy)) * 1e-3) / 1e9
+    del cpy_a, cpy_b
     enc_gbps = 2 * n / (t_enc * 1e-3) / 1e9
     dec_gbps = 2 * n / (t_dec * 1e-3) / 1e9
     rho_payload = 2 * n / (n + (n + 1) // 2 + 3 * m)
     rho_total = 2 * n / total
     value = 2 * n / (ms_step * 1e-3) / 1e9
 
-    # --- fused reduce on two tensors of the same workload (K and V halves swapped) ---
-    reduce = None
+    # --- fused reduce: the gradient-reduce configuration (two 2^29-value
+    # buffers), and a high-escape pair (the headline tensor and the same
+    # tensor with its K and V halves swapped) ---
+    reduce = reduce_hi = None
     if not args.no_reduce:
         b = torch.roll(x, shifts=n // 2)
         outb = torch.empty_like(out)
@@ -450,9 +556,17 @@ def main():
         torch.cuda.synchronize()
         t_red = float(np.mean([rev[k][0].elapsed_time(rev[k][3]) for k in range(10)]))
         t_red_k = float(np.mean([rev[k][0].elapsed_time(rev[k][1]) for k in range(10)]))
-        reduce = {"ms": round(t_red, 4), "k_reduce_tile_ms": round(t_red_k, 4),
-                  "GBps_uncompressed_in": round(2 * 2 * n / (t_red * 1e-3) / 1e9, 1),
-                  "inputs": "the workload and the same tensor with its K and V halves swapped"}
+        trr, mr = uzip.stream_bytes(outr)
+        _, mb = uzip.stream_bytes(outb)
+        rb = stream_bytes_alg(n, C, m) + stream_bytes_alg(n, C, mb) + stream_bytes_alg(n, C, mr)
+        reduce_hi = {"ms": round(t_red, 4), "k_reduce_tile_ms": round(t_red_k, 4),
+                     "GBps_uncompressed_in": round(2 * 2 * n / (t_red * 1e-3) / 1e9, 1),
+                     "algorithmic_bytes": rb, "op_frac": round(rb / (t_red * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "escape_rate_inputs": round(m / n, 6), "escape_rate_out": round(mr / n, 6),
+                     "inputs": "the headline tensor and the same tensor with its K and V halves swapped "
+                               "(a permutation: each input keeps its escape rate)"}
+        del b, outb, outr
+        reduce = reduce_config5(uzip, torch, dev, flush, C)
 
     # --- online calibration: codebook built on the device from the input
     # itself (whole input, or 256 KiB of every 2 MiB), then the encode ---
@@ -642,16 +756,19 @@ def main():
         "calibrate_ms": round(t_cal * 1e3, 3),
         "B_hide_GBps": round(min(enc_gbps, dec_gbps) / rho_total, 1),
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
-        "op_roofline_frac": {
-            "encode": round(ab["encode"] / (t_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "decode": round(ab["decode"] / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        },
+        "encode_ms_stats": stats_ms(enc_list), "decode_ms_stats": stats_ms(dec_list),
+        "op_roofline_frac": {k: round(v, 4) for k, v in op_frac.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom]},
+                     "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom],
+                     "op": slow_op, "op_frac": round(op_frac[slow_op], 4)},
+        "roofline_ops": roofline_ops,
+        "copy_kernel_GBps": {"value": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                             "what": "torch copy_ of 1 GiB to 1 GiB (2 GiB moved), median of 5 after a cache-evicting read"},
         "cache_flush_mib_before_each_call": args.flush_mib,
         "round_trip_bit_exact": round_trip, "oracle_stream_equal": parity,
         "reduce": reduce,
+        "reduce_high_escape": reduce_hi,
         "reduce_k": reduce_k,
         "online_calibration": online,
         "fp8_e5m2": fp8,
