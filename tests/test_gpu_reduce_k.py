@@ -124,3 +124,28 @@ def test_reduce_k_shards_full():
     cb = uzip.codebook_from_hist(hist.cpu().numpy().astype(np.uint64))
     assert list(cb.dec) == ocb.dec.tolist()
     check_reduce_k(rows, 1024, cb, ocb, "shards full k=8 x 2^26")
+
+
+@pytest.mark.parametrize("k", [3, 2])
+def test_tiles_with_more_escapes_than_the_lds_list(k):
+    """Sums that mostly miss the codebook: a tile with more output escapes
+    than the kernel's LDS escape list holds (6,144 of a tile's 8,192 words)
+    lists them straight into its staging slot. The stream must still equal
+    the oracle's byte for byte."""
+    n, C = 50_003, 1024
+    rng = np.random.default_rng(4242 + k)
+    rows = [rng.integers(0, 1 << 16, n, dtype=np.uint16) for _ in range(k)]
+    # a codebook of exponents the sums of uniform words almost never take:
+    # the 16 smallest (a sum lands there only if every input is that small,
+    # or by cancellation)
+    hist = np.zeros(256, dtype=np.uint64)
+    hist[0:16] = np.arange(16, 0, -1, dtype=np.uint64)
+    cb = uzip.codebook_from_hist(hist)
+    ocb = oracle.top16(hist)
+    R, tr = check_reduce_k(rows, C, cb, ocb, f"k={k} overflowing tiles")
+    # the stream (equal to the oracle's) has tiles over the LDS list's capacity
+    secs = oracle.sections(R[:tr].cpu().numpy())
+    offs = secs["offsets"].astype(np.int64)
+    tile_chunks = 8192 // C
+    per_tile = [offs[min(t + tile_chunks, secs["nchunks"])] - offs[t] for t in range(0, secs["nchunks"], tile_chunks)]
+    assert max(per_tile) > 6144, per_tile
