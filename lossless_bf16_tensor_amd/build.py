@@ -16,15 +16,30 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", SRC]
+# Host code only under AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is built as usual): for CPU tests of the host-side stream
+# parsing, validation and table building. The process that loads such a
+# build must preload clang's ASan runtime.
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-g",
+]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str | None = None) -> str:
+    lib = out or LIB
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-I", os.path.join(ROOT, "include"),
+           "-o", lib + ".tmp", SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose:
         print(r.stderr)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

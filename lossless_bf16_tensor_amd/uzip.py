@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libuzip.so")
+# UZIP_LIB points the binding at another build of the same library (the CPU
+# sanitizer test loads a host-instrumented build this way).
+LIB_PATH = os.environ.get("UZIP_LIB", os.path.join(_HERE, "libuzip.so"))
 
 UZIP_VERSION = 1
 UZIP_F_SEPARATE_PATCH = 0x1

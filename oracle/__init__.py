@@ -33,14 +33,19 @@ _LIB = os.environ.get("UZIP_ORACLE_LIB", _LIB)
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with gcc (IEEE binary32, no fast-math, no FMA)."""
+def build(sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the oracle with gcc (IEEE binary32, no fast-math, no FMA).
+    sanitize=True adds AddressSanitizer and UndefinedBehaviorSanitizer (a
+    process loading that build must preload gcc's libasan)."""
+    lib = out or _LIB
+    san = (["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+           if sanitize else [])
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-msse2", "-mfpmath=sse", "-Wall", "-Wextra",
-           "-o", _LIB + ".tmp", _SRC]
+           "-fno-fast-math", "-msse2", "-mfpmath=sse", "-Wall", "-Wextra", *san,
+           "-o", lib + ".tmp", _SRC]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 def _load():
