@@ -118,9 +118,6 @@ Layout make_layout(uint64_t n, uint32_t C, uint8_t fmt = kFmtBF16)
 #ifndef UZIP_DEC_GROUPS
 #define UZIP_DEC_GROUPS 2          // groups of 16 words per thread
 #endif
-#ifndef UZIP_PLACE_PRE
-#define UZIP_PLACE_PRE 0           // staging blocks each placement wave loads before its count is known
-#endif
 #ifndef UZIP_DEC_FETCH
 #define UZIP_DEC_FETCH 2           // escapes per thread a decode tile loads with its first patch round
 #endif
@@ -138,11 +135,19 @@ constexpr int kDecThreads = UZIP_DEC_THREADS;
 constexpr int kDecGroups = UZIP_DEC_GROUPS;
 constexpr int kDecTile = kDecThreads * kDecGroups * 16;
 constexpr int kThreads = 256;               // histogram, placement and patch kernels
-constexpr int kPlacePre = UZIP_PLACE_PRE;
 constexpr int kDecFetch = UZIP_DEC_FETCH;
 constexpr int kRedFetch = UZIP_RED_FETCH;
 
 static_assert((kEncTile & (kEncTile - 1)) == 0 && kEncTile <= 65536, "encode tile: power of two <= 65536");
+
+// A tile's escapes wait in its staging slot between the tile kernel and the
+// placement: the raw exponents (kEncTile bytes at most), and kAux bytes that
+// hold either the list of their in-chunk positions (a tile with at most
+// kPosListMax escapes) or, for a heavier tile, the tile's escape bitmap (bit
+// i set when tile value i is an escape), which is smaller than its list; the
+// placement rebuilds such a tile's positions from the bitmap.
+constexpr int kAux = kEncTile / 8;
+constexpr int kPosListMax = kAux / 2;
 static_assert((kDecTile & (kDecTile - 1)) == 0 && kDecTile >= 64, "decode tile: power of two");
 
 // Encode workspace (see uzip_workspace_bytes).
@@ -154,12 +159,12 @@ struct EncWs {
     uint32_t *gsum;        // [ngroups] escapes per group of 2^gshift tiles
     uint32_t *tpre;        // [ntiles] escapes of the tiles before it inside its group
     uint32_t *chunk_pre;   // [nch] escapes in the tile before each chunk start
-    uint16_t *stage_pos;   // [ntiles * kEncTile] in-chunk positions, per tile
+    uint8_t  *stage_aux;   // [ntiles * kAux] per tile: its position list, or its escape bitmap
     uint8_t  *stage_val;   // [ntiles * kEncTile] raw exponents, per tile
 };
 
 struct WsLayout {
-    uint64_t hist, lut, dec, counts, gsum, tpre, chunk_pre, stage_pos, stage_val, total;
+    uint64_t hist, lut, dec, counts, gsum, tpre, chunk_pre, stage_aux, stage_val, total;
 };
 
 // Tiles are summed in groups of 2^gshift, with gshift about half of log2(ntiles)
@@ -185,8 +190,8 @@ WsLayout ws_layout(uint64_t n, uint32_t C)
     w.gsum = w.counts + align256(4 * ntiles);
     w.tpre = w.gsum + align256(4 * ngroups);
     w.chunk_pre = w.tpre + align256(4 * ntiles);
-    w.stage_pos = w.chunk_pre + align256(4 * nch);
-    w.stage_val = w.stage_pos + align256(2 * ntiles * kEncTile);
+    w.stage_aux = w.chunk_pre + align256(4 * nch);
+    w.stage_val = w.stage_aux + align256(ntiles * kAux);
     w.total = w.stage_val + align256(ntiles * kEncTile) + 256;   // slack for 16-byte over-reads
     return w;
 }
@@ -314,6 +319,16 @@ __device__ __forceinline__ Codes8 codes_flags8(uint32_t L0, uint32_t L1)
     return c;
 }
 
+// The 8 escape flags of a group (codes_flags8's layout, word j at bit
+// 4j + 3) as one byte, word j at bit j.
+__device__ __forceinline__ uint32_t flags_byte(uint32_t fl)
+{
+    uint32_t x = (fl >> 3) & 0x11111111u;          // word j at bit 4j
+    x = (x | (x >> 3)) & 0x03030303u;              // words 2i, 2i + 1 at bits 8i, 8i + 1
+    x = (x | (x >> 6)) & 0x000F000Fu;              // words 4h..4h + 3 at bits 16h..16h + 3
+    return (x | (x >> 12)) & 0xFFu;
+}
+
 // Exponents of 4 words from 4 code nibbles held one per byte (values 0..15),
 // through the 16-entry table dec (4 dwords).
 __device__ __forceinline__ uint32_t dec4(const uint32_t dec[4], uint32_t nib)
@@ -371,15 +386,6 @@ __device__ __forceinline__ void floats8(uint32_t sm0, uint32_t sm1, const uint32
         for (int j = 0; j < 4; j++)
             f[4 * h + j] = __uint_as_float(perm(hi, lo, ((4u + j) << 24) | ((uint32_t)j << 16) | 0x0C0Cu));
     }
-}
-
-// Decode 8 words: sm (8 sign-mantissa bytes in 2 dwords), codes (8 nibbles).
-__device__ __forceinline__ void decode8(uint32_t sm0, uint32_t sm1, uint32_t codes,
-                                        const uint32_t dec[4], uint32_t y[4])
-{
-    uint32_t e[2];
-    decode8_e(codes, dec, e);
-    merge8(sm0, sm1, e, y);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -549,18 +555,12 @@ struct EncShared {
     uint32_t wtot[kEncGroups][kEncThreads / 64];
 };
 // A tile's escapes in element order (compacted), written out with 16-byte
-// stores; room for every word of the tile.
-template <int CAP>
-struct alignas(16) EscBufT {
-    uint16_t pos[CAP];
-    uint8_t val[CAP];
+// stores: the exponents of all of them, the positions of a tile with at most
+// kPosListMax (a heavier tile's positions go out as its bitmap).
+struct alignas(16) EscBuf {
+    uint16_t pos[kPosListMax];
+    uint8_t val[kEncTile];
 };
-using EscBuf = EscBufT<kEncTile>;
-// The reduces' LDS escape list holds 3/4 of a tile, which lets 8 of their
-// workgroups share a CU instead of 6; a tile with more escapes lists them in
-// its staging slot directly.
-constexpr int kRedEscCap = 6144;
-static_assert(kRedEscCap % 16 == 0 && kRedEscCap <= kEncTile, "whole 16-byte copies");
 
 // Copies the code table to LDS (threads 0..63, 4 bytes each); a workgroup
 // barrier must follow before any wave reads it.
@@ -650,11 +650,11 @@ __device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
     return (v >> (8 * q)) | (nxt << (24 - 8 * q));
 }
 
-template <int kCodes = kCodeNib, int CAP = kEncTile>
+template <int kCodes = kCodeNib>
 __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
-                                                      EncShared &sh, EscBufT<CAP> &eb, uint32_t cstart[kEncGroups],
-                                                      uint16_t *gpos = nullptr, uint8_t *gval = nullptr)
+                                                      EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups],
+                                                      uint8_t *__restrict__ aux)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the tile's bases (scalar); lanes index them with 32-bit offsets
@@ -747,45 +747,52 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
         cstart[k] = (lo < rem && ((t0m + lo) & p.Cmask) == 0) ? base[k] + pre[k] : ~0u;
     }
-    // the list, to LDS, or (a buffer smaller than the tile that the tile's
-    // escapes overflow: run is the same in every thread) to gpos/gval
-    auto list = [&](auto *dpos, auto *dval) {
+    // the list in LDS: every escape's exponent, and its position as well
+    // when the tile has at most kPosListMax escapes (run is the same in
+    // every thread); a heavier tile's positions go to its staging slot as
+    // the tile's escape bitmap, one byte per group of 8 words (byte lo / 8;
+    // groups past the end have no escapes, so their bytes are 0)
+    const bool want_pos = p.posw != 0;
+    const bool lst = want_pos && run <= (uint32_t)kPosListMax;
+    if (want_pos && !lst) {
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) {
-            const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
-            uint32_t rank = base[k] + pre[k];
-            const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
-            uint32_t mask = fl[k];
-            if (mask == 0) continue;
-            // exponents of words 0..7, one per byte of ex1:ex0
-            const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
-            const uint32_t ex1 = perm(xw[k][3] >> 7, xw[k][2] >> 7, 0x06040200u);
-            while (mask) {
-                const uint32_t j = __builtin_ctz(mask) >> 2;       // the word, 0..7
-                dpos[rank] = (uint16_t)(g0m + j);
-                dval[rank] = (uint8_t)perm(ex1, ex0, j);
-                rank++;
-                mask &= mask - 1;
-            }
+        for (int k = 0; k < kEncGroups; k++)
+            aux[(uint32_t)(k * (kEncThreads * 8) + tid * 8) >> 3] = (uint8_t)flags_byte(fl[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kEncGroups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+        uint32_t rank = base[k] + pre[k];
+        const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
+        uint32_t mask = fl[k];
+        if (mask == 0) continue;
+        // exponents of words 0..7, one per byte of ex1:ex0
+        const uint32_t ex0 = perm(xw[k][1] >> 7, xw[k][0] >> 7, 0x06040200u);
+        const uint32_t ex1 = perm(xw[k][3] >> 7, xw[k][2] >> 7, 0x06040200u);
+        while (mask) {
+            const uint32_t j = __builtin_ctz(mask) >> 2;       // the word, 0..7
+            if (lst) eb.pos[rank] = (uint16_t)(g0m + j);
+            eb.val[rank] = (uint8_t)perm(ex1, ex0, j);
+            rank++;
+            mask &= mask - 1;
         }
-    };
-    if (CAP >= kEncTile || run <= (uint32_t)CAP) list(eb.pos, eb.val);
-    else list(gpos, gval);
+    }
     return run;
 }
 
 // Staging back half: the tile's count, its in-tile prefix at each chunk
 // start, and its escape list copied to the tile's staging slot with 16-byte
-// stores (the last store of each array may carry stale bytes past m: the
-// slot is scratch and only its first m entries are read). The stores are
-// temporal: the placement kernel reads the slot back right away, from the
-// Infinity Cache.
+// stores: the exponents, and the positions of a tile with at most
+// kPosListMax escapes (the last store of each array may carry stale bytes
+// past m: the slot is scratch and only its first m entries are read). The
+// stores are temporal: the placement kernel reads the slot back right away,
+// from the Infinity Cache.
 // G groups of GW values per thread (group k of thread tid starts at tile
 // value k*kEncThreads*GW + tid*GW).
-template <int G = kEncGroups, int GW = 8, int CAP = kEncTile>
+template <int G = kEncGroups, int GW = 8>
 __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[G], uint64_t t0,
                                               uint64_t tile, const EncWs &ws, const EncParams &p,
-                                              const EscBufT<CAP> &eb)
+                                              const EscBuf &eb)
 {
     const int tid = threadIdx.x;
     if (tid == 0) ws.counts[tile] = m;
@@ -797,11 +804,13 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
             if (cstart[k] != ~0u) cpt[lo >> p.logC] = cstart[k];
         }
     }
-    if (m == 0 || m > (uint32_t)CAP) return;           // none, or listed in the slot already
+    if (m == 0) return;
     __syncthreads();
-    u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_pos + tile * kEncTile);
-    const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
-    for (uint32_t q = tid; q < (m + 7) / 8; q += kEncThreads) sp[q] = lp[q];
+    if (p.posw && m <= (uint32_t)kPosListMax) {
+        u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_aux + tile * kAux);
+        const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
+        for (uint32_t q = tid; q < (m + 7) / 8; q += kEncThreads) sp[q] = lp[q];
+    }
     u32x4 *sv = reinterpret_cast<u32x4 *>(ws.stage_val + tile * kEncTile);
     const u32x4 *lv = reinterpret_cast<const u32x4 *>(eb.val);
     for (uint32_t q = tid; q < (m + 15) / 16; q += kEncThreads) sv[q] = lv[q];
@@ -839,7 +848,7 @@ __device__ __forceinline__ void encode_tile(const uint16_t *__restrict__ x, uint
     load_shared_lut(sh, p.dlut ? p.dlut : p.lut);
     __syncthreads();
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodes>(xw, t0, rem, out, p, sh, eb, cstart);
+    const uint32_t m = encode_dense_rank<kCodes>(xw, t0, rem, out, p, sh, eb, cstart, ws.stage_aux + tile * kAux);
     stage_escapes(m, cstart, t0, tile, ws, p, eb);
 }
 
@@ -967,18 +976,6 @@ __device__ __forceinline__ uint64_t edge_offset(uint64_t head, uint64_t tail0, u
     return ok ? j : ~0ull;
 }
 
-// Byte j of the source from the prefetched blocks pf (block `lane` in each
-// lane), for j < 64 * 16; every lane must call it (cross-lane shuffles).
-__device__ __forceinline__ uint32_t byte_from_blocks(u32x4 pf, uint64_t j)
-{
-    const int sl = (int)((j >> 4) & 63);
-    const uint32_t comp = (uint32_t)(j >> 2) & 3u;
-    const uint32_t x = __shfl(pf.x, sl, 64), y = __shfl(pf.y, sl, 64);
-    const uint32_t z = __shfl(pf.z, sl, 64), w = __shfl(pf.w, sl, 64);
-    const uint32_t d = comp == 0 ? x : comp == 1 ? y : comp == 2 ? z : w;
-    return (d >> (8 * (j & 3))) & 0xFFu;
-}
-
 // Whole destination block k of a plan from source blocks lo = k, hi = k + 1.
 __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 lo, u32x4 hi)
 {
@@ -986,43 +983,73 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
 }
 
 // One wave per encode tile. Its escape prefix P = (group sums before the
-// tile's group) + (the tile's prefix inside its group). Every load that
-// needs neither the tile's escape count nor P goes out first, in one round:
-// the count, the sums, the tile's chunk prefixes and the first kPlacePre + 1
-// blocks of both staging arrays (speculative: most tiles need only a few).
-// Then positions and exponents go to pos[P..] and val[P..]: each whole
-// 16-byte destination block by one store (two aligned source blocks and a
-// byte funnel), the partial blocks at the ends by byte stores (lanes 0..31
-// for pos, 32..63 for val), their bytes taken from the prefetched blocks by
-// cross-lane shuffles or else loaded. Pos and val blocks past the prefetch
-// are copied together, 64 per round, with the loads of each round issued
-// before the stores of the round before it (a wait for a load also waits
-// for every store issued before it). Tile 0's wave also writes the header,
+// tile's group) + (the tile's prefix inside its group). Every load goes out
+// in one first round: the count, the sums, the tile's chunk prefixes, and
+// the first KiB of each part of its staging slot (its position list or
+// bitmap, and its exponents; 16 bytes per lane). Then:
+//  - positions, a tile with at most kPosListMax escapes: its list is all in
+//    the prefetched bytes. Each whole 16-byte destination block of pos[P..]
+//    is built from two lanes' bytes (a cross-lane read and a byte funnel)
+//    and stored; the partial blocks at the two ends, which the neighbouring
+//    tiles share, by byte stores;
+//  - positions, a heavier tile: from its escape bitmap, in four passes of
+//    2,048 values. Each lane takes 32 values, counts their escapes, and,
+//    after a wave scan of the counts, writes their in-chunk positions into
+//    the wave's LDS buffer in value order; the buffer's whole 16-byte blocks
+//    go out with one store each (the buffer starts on a 16-byte boundary of
+//    the destination: the tile's first block is preceded by the entries of
+//    the tile before it, which are not written), and the at most 7 entries
+//    of a partial last block move to the buffer's start for the next pass;
+//  - exponents: like a short position list for the blocks within the
+//    prefetched KiB, then 64 blocks per round from the slot, the loads of
+//    each round issued before the stores of the round before it (a wait for
+//    a load also waits for every store issued before it).
+// Lanes 0..31 store a short list's edge bytes, lanes 32..63 the exponents'.
+// It writes the tile's chunk offsets. Tile 0's wave also writes the header,
 // offsets[nch] = M and every padding byte.
-static_assert(kPlacePre >= 0 && kPlacePre <= 64, "placement prefetch: 0..64 blocks");
+constexpr int kPassVals = 2048;                    // values per bitmap pass: 32 per lane
+static_assert(kEncTile % kPassVals == 0 && kAux == 16 * 64, "the slot's first KiB is 16 bytes per lane");
 static_assert(kEncTile >= 16 * 65, "placement reads at most 65 blocks past a round start");
 static_assert(kEncTile / 64 <= 128, "placement loads at most two chunk prefixes per lane");
+
+// Byte j (j < 1024) of the bytes held 16 per lane in pf (lane l: bytes
+// 16l..16l + 15); every lane must call it (cross-lane reads).
+__device__ __forceinline__ uint32_t byte_from_lanes(u32x4 pf, uint32_t j)
+{
+    const int sl = (int)((j >> 4) & 63);
+    const uint32_t comp = (j >> 2) & 3u;
+    const uint32_t x = __shfl(pf.x, sl, 64), y = __shfl(pf.y, sl, 64);
+    const uint32_t z = __shfl(pf.z, sl, 64), w = __shfl(pf.w, sl, 64);
+    const uint32_t d = comp == 0 ? x : comp == 1 ? y : comp == 2 ? z : w;
+    return (d >> (8 * (j & 3))) & 0xFFu;
+}
+
+// The next lane's 16 bytes (lane 63 gets its own back).
+__device__ __forceinline__ u32x4 next_lane(u32x4 v)
+{
+    const int nl = ((int)(threadIdx.x & 63) + 1) & 63;
+    return u32x4{(uint32_t)__shfl(v.x, nl, 64), (uint32_t)__shfl(v.y, nl, 64), (uint32_t)__shfl(v.z, nl, 64),
+                 (uint32_t)__shfl(v.w, nl, 64)};
+}
+
 __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
                                                             HeaderParams hp)
 {
+    // one buffer of positions per wave: a pass, plus the carried partial block
+    __shared__ __attribute__((aligned(16))) uint16_t s_pos[kThreads / 64][kPassVals + 16];
     // wave-uniform values are moved to scalar registers (readfirstlane)
     const int lane = threadIdx.x & 63;
-    const uint64_t tile = (uint64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t tile = (uint64_t)blockIdx.x * (kThreads / 64) + wv;
     if (tile >= p.ntiles) return;
     const uint64_t t0 = tile * kEncTile;
     const uint32_t C = p.Cmask + 1;
-    // ---- first loads: everything independent of the count and of P
-    const uint8_t *src_p = reinterpret_cast<const uint8_t *>(ws.stage_pos + tile * kEncTile);
+    // ---- the one load round
+    const uint8_t *aux = ws.stage_aux + tile * kAux;
     const uint8_t *src_v = ws.stage_val + tile * kEncTile;
-    const u32x4 *sp4 = reinterpret_cast<const u32x4 *>(src_p);
     const u32x4 *sv4 = reinterpret_cast<const u32x4 *>(src_v);
-    u32x4 pp0 = {}, pp1 = {}, pv0 = {}, pv1 = {};
-    if (lane < kPlacePre) {
-        pp0 = sp4[lane];
-        pp1 = sp4[lane + 1];
-        pv0 = sv4[lane];
-        pv1 = sv4[lane + 1];
-    }
+    const u32x4 ap = reinterpret_cast<const u32x4 *>(aux)[lane];
+    const u32x4 vp = sv4[lane];
     const uint32_t m_l = ws.counts[tile];
     const uint32_t tp_l = ws.tpre[tile];
     const uint64_t g = tile >> p.gshift;
@@ -1065,52 +1092,102 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     const uint64_t M = all_w;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
-    // ---- the copies
-    const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, p.posw ? 2 * (uint64_t)m : 0);
-    const ShiftPlan qv = shift_plan(out + off_val + P, m);
-    const uint64_t nb = qp.nblk > qv.nblk ? qp.nblk : qv.nblk;
-    // loads of the first round past the prefetch
-    u32x4 alo = {}, ahi = {}, blo = {}, bhi = {};
-    {
-        const uint64_t k = (uint64_t)kPlacePre + lane;
-        if (k < qp.nblk) {
-            alo = sp4[k];
-            ahi = sp4[k + 1];
+    // ---- positions
+    const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, (p.posw && m <= kPosListMax) ? 2 * (uint64_t)m : 0);
+    if (qp.nblk) {                                  // a short list, from the prefetched bytes
+        const u32x4 nxt = next_lane(ap);
+        if ((uint64_t)lane < qp.nblk) st_stream(qp.r == 0 ? ap : extract16(ap, nxt, qp.r), qp.d4 + lane);
+    }
+    if (p.posw && m > (uint32_t)kPosListMax) {      // from the bitmap
+        uint16_t *buf = s_pos[wv];
+        const uint32_t t0m = (uint32_t)(t0 & p.Cmask);
+        const uint64_t d0 = p.off_pos + 2 * (uint64_t)P;
+        uint8_t *base = out + (d0 & ~15ull);        // destination of buffer entry 0
+        const uint32_t phantom = (uint32_t)((d0 & 15u) >> 1);   // entries of the tile before
+        uint32_t carry = phantom, done = 0;         // entries waiting at the buffer's start; blocks stored
+        for (int c = 0; c < kEncTile / kPassVals; c++) {
+            // this lane's 32 values: dword (lane & 3) of lane 16c + lane / 4
+            const int sl = 16 * c + (lane >> 2);
+            const uint32_t bx = __shfl(ap.x, sl, 64), by = __shfl(ap.y, sl, 64);
+            const uint32_t bz = __shfl(ap.z, sl, 64), bw = __shfl(ap.w, sl, 64);
+            const uint32_t q = (uint32_t)lane & 3u;
+            uint32_t bits = q == 0 ? bx : q == 1 ? by : q == 2 ? bz : bw;
+            const uint32_t cnt = __builtin_popcount(bits);
+            const uint32_t inc = wave_inclusive_sum(cnt);
+            const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane(inc, 63);
+            uint32_t slot = carry + inc - cnt;
+            const uint32_t v0 = t0m + (uint32_t)(c * kPassVals) + 32u * (uint32_t)lane;
+            while (bits) {
+                buf[slot++] = (uint16_t)((v0 + (uint32_t)__builtin_ctz(bits)) & p.Cmask);
+                bits &= bits - 1;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint32_t ntot = carry + tot, nb = ntot >> 3;
+            for (uint32_t k = (uint32_t)lane; k < nb; k += 64) {
+                const u32x4 blk = *reinterpret_cast<const u32x4 *>(buf + 8 * k);
+                uint8_t *dst = base + 16 * (uint64_t)(done + k);
+                if (done + k == 0 && phantom) {     // the first block: skip the tile before's bytes
+                    for (uint32_t b = 2 * phantom; b < 16; b++)
+                        dst[b] = (uint8_t)((b < 8 ? (b < 4 ? blk.x : blk.y) : (b < 12 ? blk.z : blk.w)) >> (8 * (b & 3)));
+                } else {
+                    st_stream(blk, reinterpret_cast<u32x4 *>(dst));
+                }
+            }
+            const uint32_t left = ntot & 7u;        // entries of a partial last block
+            uint32_t keep = 0;
+            if ((uint32_t)lane < left) keep = buf[8 * nb + lane];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if ((uint32_t)lane < left) buf[lane] = (uint16_t)keep;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            done += nb;
+            carry = left;
         }
+        // the partial last block: its entries' bytes (after the tile
+        // before's, if it is also the first block)
+        const uint32_t b0 = done == 0 ? 2 * phantom : 0, b1 = 2 * carry;
+        if ((uint32_t)lane >= b0 && (uint32_t)lane < b1)
+            base[16 * (uint64_t)done + lane] = (uint8_t)(buf[lane >> 1] >> (8 * (lane & 1)));
+    }
+    // ---- exponents
+    const ShiftPlan qv = shift_plan(out + off_val + P, m);
+    // blocks whose two source blocks are both prefetched (k + 1 < 64)
+    const uint64_t nreg = qv.nblk < 63 ? qv.nblk : 63;
+    {
+        const u32x4 nxt = next_lane(vp);
+        if ((uint64_t)lane < nreg) st_stream(qv.r == 0 ? vp : extract16(vp, nxt, qv.r), qv.d4 + lane);
+    }
+    // edge bytes: this lane's byte (lanes 0..31: a short position list's,
+    // 32..63: the exponents'), from the prefetched bytes or else loaded
+    const bool is_p = lane < 32;
+    const uint64_t ej = edge_offset(is_p ? qp.head : qv.head, is_p ? qp.tail0 : qv.tail0,
+                                    is_p ? qp.len : qv.len, lane & 31);
+    const uint32_t jj = (ej == ~0ull || ej >= (uint64_t)kAux) ? 0u : (uint32_t)ej;
+    const uint32_t bp = byte_from_lanes(ap, jj), bv = byte_from_lanes(vp, jj);
+    uint32_t eb = is_p ? bp : bv;
+    if (!is_p && ej != ~0ull && ej >= (uint64_t)kAux) eb = src_v[ej];
+    // the rest of the exponents, 64 blocks per round from the slot
+    u32x4 blo = {}, bhi = {};
+    {
+        const uint64_t k = nreg + lane;
         if (k < qv.nblk) {
             blo = sv4[k];
             bhi = sv4[k + 1];
         }
     }
-    // edge bytes: this lane's byte, from the prefetched blocks if it is
-    // there, else loaded now and stored after the block rounds
-    const bool is_p = lane < 32;
-    const uint64_t ej = edge_offset(is_p ? qp.head : qv.head, is_p ? qp.tail0 : qv.tail0,
-                                    is_p ? qp.len : qv.len, lane & 31);
-    const uint64_t jj = ej == ~0ull ? 0 : ej;
-    uint32_t eb = 0;
-    if (kPlacePre > 0) {
-        const uint32_t bp = byte_from_blocks(pp0, jj), bv = byte_from_blocks(pv0, jj);
-        eb = is_p ? bp : bv;
-    }
-    if (ej != ~0ull && (ej >> 4) >= (uint64_t)kPlacePre) eb = is_p ? src_p[ej] : src_v[ej];
-    if ((uint64_t)lane < qp.nblk && lane < kPlacePre) put_block(qp, lane, pp0, pp1);
-    if ((uint64_t)lane < qv.nblk && lane < kPlacePre) put_block(qv, lane, pv0, pv1);
-    for (uint64_t k0 = kPlacePre; k0 < nb; k0 += 64) {
+    for (uint64_t k0 = nreg; k0 < qv.nblk; k0 += 64) {
         const uint64_t k = k0 + lane, kn = k + 64;
-        u32x4 nalo = alo, nahi = ahi, nblo = blo, nbhi = bhi;
-        if (kn < qp.nblk) {
-            nalo = sp4[kn];
-            nahi = sp4[kn + 1];
-        }
+        u32x4 nblo = blo, nbhi = bhi;
         if (kn < qv.nblk) {
             nblo = sv4[kn];
             nbhi = sv4[kn + 1];
         }
-        if (k < qp.nblk) put_block(qp, k, alo, ahi);
         if (k < qv.nblk) put_block(qv, k, blo, bhi);
-        alo = nalo;
-        ahi = nahi;
         blo = nblo;
         bhi = nbhi;
     }
@@ -1486,7 +1563,7 @@ struct ExpTile2 {
 };
 union ReduceLds {
     ExpTile2 ex;
-    EscBufT<kRedEscCap> esc;
+    EscBuf esc;
 };
 
 // One tile of the pairwise reduce: both inputs decoded and patched, summed
@@ -1582,9 +1659,8 @@ __global__ __launch_bounds__(kEncThreads, 5) void k_reduce_tile(StreamIn sa, Str
     // encode_dense_rank writes the escape list only after its first barrier,
     // which every thread reaches after its last read of the patch map
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib, kRedEscCap>(r, t0, rem, out, ep, esh, lds.esc, cstart,
-                                                               ws.stage_pos + tile * kEncTile,
-                                                               ws.stage_val + tile * kEncTile);
+    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart,
+                                                   ws.stage_aux + tile * kAux);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
@@ -1728,9 +1804,8 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
     }
     if (!synced) __syncthreads();
     uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib, kRedEscCap>(r, t0, rem, out, ep, esh, lds.esc, cstart,
-                                                               ws.stage_pos + tile * kEncTile,
-                                                               ws.stage_val + tile * kEncTile);
+    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart,
+                                                   ws.stage_aux + tile * kAux);
     stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
@@ -1859,12 +1934,19 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     const uint32_t g0m = ((uint32_t)(t0 & p.Cmask) + lo) & p.Cmask;   // a multiple of 32, below C
     uint32_t cstart[1];
     cstart[0] = (lo < rem && g0m == 0) ? rank : ~0u;
+    // positions listed for a tile with at most kPosListMax escapes, else the
+    // tile's escape bitmap: this lane's 32 values are its bytes 4 tid..4 tid + 3
+    const bool lst = m <= (uint32_t)kPosListMax;
+    if (!lst)
+        reinterpret_cast<uint32_t *>(ws.stage_aux + tile * kAux)[tid] =
+            flags_byte(c8[0].flags) | (flags_byte(c8[1].flags) << 8) | (flags_byte(c8[2].flags) << 16) |
+            (flags_byte(c8[3].flags) << 24);
 #pragma unroll
     for (int q = 0; q < 8; q += 2) {               // 8 values per loop, in value order
         uint32_t mask = c8[q / 2].flags;
         while (mask) {
             const uint32_t j = __builtin_ctz(mask) >> 2;       // value 4q + j
-            eb.pos[rank] = (uint16_t)(g0m + 4 * q + j);
+            if (lst) eb.pos[rank] = (uint16_t)(g0m + 4 * q + j);
             eb.val[rank] = (uint8_t)perm(E[q + 1], E[q], j);
             rank++;
             mask &= mask - 1;
@@ -2455,7 +2537,7 @@ EncWs make_ws(void *d_ws, uint64_t n, uint32_t C)
     ws.gsum = reinterpret_cast<uint32_t *>(b + w.gsum);
     ws.tpre = reinterpret_cast<uint32_t *>(b + w.tpre);
     ws.chunk_pre = reinterpret_cast<uint32_t *>(b + w.chunk_pre);
-    ws.stage_pos = reinterpret_cast<uint16_t *>(b + w.stage_pos);
+    ws.stage_aux = b + w.stage_aux;
     ws.stage_val = b + w.stage_val;
     return ws;
 }

@@ -43,7 +43,10 @@ def test_library_links_no_oracle():
                                  ((1 << 32) - 1, 65536)])
 def test_max_bytes_matches_format(n, C):
     assert uzip.max_bytes(n, C) == oracle.max_bytes(n, C)
-    assert uzip.workspace_bytes(n, C) >= 3 * n
+    # the workspace holds each tile's exponents (a byte per value) and a
+    # position list or bitmap (an eighth of a byte per value), plus small
+    # per-tile and per-chunk tables: at most 1.2 bytes per value
+    assert 9 * n // 8 <= uzip.workspace_bytes(n, C) <= 1.2 * n + (1 << 16)
 
 
 @pytest.mark.parametrize("n,C", [(0, 1024), (1 << 32, 1024), (100, 0), (100, 32), (100, 1000),
