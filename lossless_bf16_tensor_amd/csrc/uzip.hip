@@ -1032,64 +1032,28 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v)
                  (uint32_t)__shfl(v.w, nl, 64)};
 }
 
-__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
-                                                            HeaderParams hp)
+#ifndef UZIP_PLACE_T
+#define UZIP_PLACE_T 1
+#endif
+constexpr int kPlaceT = UZIP_PLACE_T;              // consecutive tiles per placement wave
+static_assert(kPlaceT >= 1 && 64 % kPlaceT == 0, "a wave's tiles lie in one group of 2^gshift >= 64 tiles");
+
+// What the first load round fetches for one tile.
+struct PlaceIn {
+    u32x4 ap, vp;                                  // the slot's first KiB of each part, 16 bytes per lane
+    uint32_t cp[2];                                // in-tile prefixes of the chunks starting in the tile
+};
+
+__device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
+                                           uint64_t tile, uint32_t m, uint32_t P, uint64_t M, const PlaceIn &in,
+                                           uint16_t *buf)
 {
-    // one buffer of positions per wave: a pass, plus the carried partial block
-    __shared__ __attribute__((aligned(16))) uint16_t s_pos[kThreads / 64][kPassVals + 16];
-    // wave-uniform values are moved to scalar registers (readfirstlane)
     const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t tile = (uint64_t)blockIdx.x * (kThreads / 64) + wv;
-    if (tile >= p.ntiles) return;
     const uint64_t t0 = tile * kEncTile;
     const uint32_t C = p.Cmask + 1;
-    // ---- the one load round
-    const uint8_t *aux = ws.stage_aux + tile * kAux;
+    const u32x4 ap = in.ap, vp = in.vp;
     const uint8_t *src_v = ws.stage_val + tile * kEncTile;
     const u32x4 *sv4 = reinterpret_cast<const u32x4 *>(src_v);
-    const u32x4 ap = reinterpret_cast<const u32x4 *>(aux)[lane];
-    const u32x4 vp = sv4[lane];
-    const uint32_t m_l = ws.counts[tile];
-    const uint32_t tp_l = ws.tpre[tile];
-    const uint64_t g = tile >> p.gshift;
-    uint32_t gs[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint64_t q = (uint64_t)lane + 64 * i;
-        gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
-    }
-    uint64_t c0 = 0, cn = 0;
-    uint32_t cp[2] = {0u, 0u};
-    if (C < (uint32_t)kEncTile) {
-        c0 = t0 >> p.logC;
-        cn = (uint64_t)kEncTile >> p.logC;
-        if (c0 + cn > p.nch) cn = p.nch - c0;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-            if ((uint64_t)lane + 64 * i < cn) cp[i] = ws.chunk_pre[c0 + lane + 64 * i];
-    }
-    // ---- the prefix
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint64_t q = (uint64_t)lane + 64 * i;
-        all += gs[i];
-        if (q < g) before += gs[i];
-    }
-    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) {
-        const uint32_t v = ws.gsum[q];
-        all += v;
-        if (q < g) before += v;
-    }
-    // the wave totals: lane 63 of DPP inclusive scans (no LDS round trips)
-    const uint32_t before_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
-    const uint32_t all_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
-    const uint32_t m = __builtin_amdgcn_readfirstlane(m_l);
-    const uint32_t P = __builtin_amdgcn_readfirstlane(before_w + tp_l);
-    // readlane returns a signed int: through uint32_t, so that an M of 2^31
-    // or more is not sign-extended
-    const uint64_t M = all_w;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // ---- positions
@@ -1099,7 +1063,6 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
         if ((uint64_t)lane < qp.nblk) st_stream(qp.r == 0 ? ap : extract16(ap, nxt, qp.r), qp.d4 + lane);
     }
     if (p.posw && m > (uint32_t)kPosListMax) {      // from the bitmap
-        uint16_t *buf = s_pos[wv];
         const uint32_t t0m = (uint32_t)(t0 & p.Cmask);
         const uint64_t d0 = p.off_pos + 2 * (uint64_t)P;
         uint8_t *base = out + (d0 & ~15ull);        // destination of buffer entry 0
@@ -1197,13 +1160,85 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
     }
     // offsets of the chunks that start in the tile
     if (C < (uint32_t)kEncTile) {
+        const uint64_t c0 = t0 >> p.logC;
+        uint64_t cn = (uint64_t)kEncTile >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
 #pragma unroll
         for (int i = 0; i < 2; i++)
-            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + cp[i];
+            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + in.cp[i];
     } else if ((t0 & p.Cmask) == 0 && lane == 0) {
         offs[t0 >> p.logC] = P;
     }
-    if (tile != 0) return;
+}
+
+__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
+                                                            HeaderParams hp)
+{
+    // one buffer of positions per wave: a pass, plus the carried partial block
+    __shared__ __attribute__((aligned(16))) uint16_t s_pos[kThreads / 64][kPassVals + 16];
+    // wave-uniform values are moved to scalar registers (readfirstlane)
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t tile0 = ((uint64_t)blockIdx.x * (kThreads / 64) + wv) * kPlaceT;
+    if (tile0 >= p.ntiles) return;
+    const uint32_t nt = (uint32_t)((p.ntiles - tile0 < (uint64_t)kPlaceT) ? p.ntiles - tile0 : (uint64_t)kPlaceT);
+    const uint32_t C = p.Cmask + 1;
+    // ---- the one load round, for all the wave's tiles
+    PlaceIn in[kPlaceT];
+#pragma unroll
+    for (int i = 0; i < kPlaceT; i++) {
+        const uint64_t tile = tile0 + (i < (int)nt ? i : 0);
+        in[i].ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
+        in[i].vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
+        in[i].cp[0] = in[i].cp[1] = 0u;
+        if (C < (uint32_t)kEncTile) {
+            const uint64_t c0 = (tile * kEncTile) >> p.logC;
+            uint64_t cn = (uint64_t)kEncTile >> p.logC;
+            if (c0 + cn > p.nch) cn = p.nch - c0;
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                if ((uint64_t)lane + 64 * j < cn) in[i].cp[j] = ws.chunk_pre[c0 + lane + 64 * j];
+        }
+    }
+    // lane i < nt: tile i's count and in-group prefix
+    const uint32_t m_l = (lane < (int)nt) ? ws.counts[tile0 + lane] : 0u;
+    const uint32_t tp_l = (lane < (int)nt) ? ws.tpre[tile0 + lane] : 0u;
+    const uint64_t g = tile0 >> p.gshift;
+    uint32_t gs[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t q = (uint64_t)lane + 64 * i;
+        gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
+    }
+    // ---- the prefix
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t q = (uint64_t)lane + 64 * i;
+        all += gs[i];
+        if (q < g) before += gs[i];
+    }
+    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) {
+        const uint32_t v = ws.gsum[q];
+        all += v;
+        if (q < g) before += v;
+    }
+    // the wave totals: lane 63 of DPP inclusive scans (no LDS round trips)
+    const uint32_t before_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
+    const uint32_t all_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
+    // readlane returns a signed int: through uint32_t, so that an M of 2^31
+    // or more is not sign-extended
+    const uint64_t M = all_w;
+#pragma unroll
+    for (int i = 0; i < kPlaceT; i++) {
+        if (i >= (int)nt) break;
+        const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(m_l, i);
+        const uint32_t P = before_w + (uint32_t)__builtin_amdgcn_readlane(tp_l, i);
+        place_tile(ws, out, p, tile0 + i, m, P, M, in[i], s_pos[wv]);
+    }
+    if (tile0 != 0) return;
+    const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
+    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // header: template + M + total_bytes
     const uint64_t total = off_val + M;
     uint32_t w = reinterpret_cast<const uint32_t *>(hp.tmpl)[lane];
@@ -2562,7 +2597,7 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
     UZIP_LAUNCH_CHECK("k_group_sums");
     int rc = ev.record(ev0);
     if (rc) return rc;
-    k_place_escapes<<<(unsigned)((ep.ntiles + kThreads / 64 - 1) / (kThreads / 64)), kThreads, 0, s>>>(ws, out, ep, hp);
+    k_place_escapes<<<(unsigned)((ep.ntiles + kPlaceT * (kThreads / 64) - 1) / (kPlaceT * (kThreads / 64))), kThreads, 0, s>>>(ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
     return ev.record(ev0 + 1);
 }
