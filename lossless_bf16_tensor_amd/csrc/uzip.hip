@@ -550,10 +550,13 @@ __global__ __launch_bounds__(256) void k_top16(const unsigned long long *__restr
 
 // ============================================================== encode ====
 // LDS of the encode back end.
-struct EncShared {
+// (NT threads per workgroup, NG groups of 8 words per thread.)
+template <int NT = kEncThreads, int NG = kEncGroups>
+struct EncSharedT {
     uint8_t lut[256];                       // the code table (one copy: a barrier publishes it)
-    uint32_t wtot[kEncGroups][kEncThreads / 64];
+    uint32_t wtot[NG][NT / 64];
 };
+using EncShared = EncSharedT<>;
 // A tile's escapes in element order (compacted), written out with 16-byte
 // stores: the exponents of all of them, the positions of a tile with at most
 // kPosListMax (a heavier tile's positions go out as its bitmap).
@@ -564,7 +567,8 @@ struct alignas(16) EscBuf {
 
 // Copies the code table to LDS (threads 0..63, 4 bytes each); a workgroup
 // barrier must follow before any wave reads it.
-__device__ __forceinline__ void load_shared_lut(EncShared &sh, const uint8_t *lut)
+template <typename Sh>
+__device__ __forceinline__ void load_shared_lut(Sh &sh, const uint8_t *lut)
 {
     if (threadIdx.x < 64)
         reinterpret_cast<uint32_t *>(sh.lut)[threadIdx.x] = reinterpret_cast<const uint32_t *>(lut)[threadIdx.x];
@@ -650,22 +654,23 @@ __device__ __forceinline__ uint32_t quad_pack3(uint32_t v, uint32_t q)
     return (v >> (8 * q)) | (nxt << (24 - 8 * q));
 }
 
-template <int kCodes = kCodeNib>
-__device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGroups][4], uint64_t t0, uint32_t rem,
+template <int kCodes = kCodeNib, int NT = kEncThreads, int NG = kEncGroups>
+__device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[NG][4], uint64_t t0, uint32_t rem,
                                                       uint8_t *__restrict__ out, const EncParams &p,
-                                                      EncShared &sh, EscBuf &eb, uint32_t cstart[kEncGroups],
+                                                      EncSharedT<NT, NG> &sh, EscBuf &eb, uint32_t cstart[NG],
                                                       uint8_t *__restrict__ aux)
 {
+    static_assert(NT * NG * 8 == kEncTile, "a workgroup encodes one tile");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the tile's bases (scalar); lanes index them with 32-bit offsets
     uint8_t *smt = out + kHeader + t0;
     uint8_t *cdt = out + p.off_codes + t0 / 2;
     const uint32_t t0m = (uint32_t)(t0 & p.Cmask);      // offset of the tile in its chunk
-    uint32_t fl[kEncGroups], sm[kEncGroups][2], cw[kEncGroups];
+    uint32_t fl[NG], sm[NG][2], cw[NG];
     // table lookups and dense values for every group, then all the stores
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < NG; k++) {
+        const uint32_t lo = (uint32_t)(k * (NT * 8) + tid * 8);
         uint32_t L0 = 0, L1 = 0;
         if (lo < rem) {
             L0 = lut4(sh.lut, xw[k][0], xw[k][1]);
@@ -688,8 +693,8 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         else cw[k] = c8.codes;
     }
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < NG; k++) {
+        const uint32_t lo = (uint32_t)(k * (NT * 8) + tid * 8);
         if (lo < rem) {
             u32x2 smv;
             smv.x = sm[k][0];
@@ -715,9 +720,9 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
         }
     }
     // escape count of each group -> exclusive prefix over the wave's lanes
-    uint32_t pre[kEncGroups];
+    uint32_t pre[NG];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
+    for (int k = 0; k < NG; k++) {
         const uint32_t cnt = __builtin_popcount(fl[k]);
         uint32_t wt = 0, pr = 0;
         if (__ballot(cnt != 0) != 0ull) {
@@ -732,19 +737,19 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     // element order inside the tile is (group k, wave, lane, word): each row
     // of 16 lanes takes the exclusive prefix of the group-major totals, and
     // the wave reads its own entries out of it (wave-uniform values)
-    constexpr int kTot = kEncGroups * (kEncThreads / 64);
+    constexpr int kTot = NG * (NT / 64);
     static_assert(kTot <= 16, "the wave totals fit one row of 16 lanes");
     const uint32_t tv = (lane & 15) < kTot ? (&sh.wtot[0][0])[lane & 15] : 0u;
     const uint32_t tinc = row_inclusive_sum(tv), texc = tinc - tv;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t base[kEncGroups];
+    uint32_t base[NG];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++)
-        base[k] = __builtin_amdgcn_readlane(texc, k * (kEncThreads / 64) + wv);
+    for (int k = 0; k < NG; k++)
+        base[k] = __builtin_amdgcn_readlane(texc, k * (NT / 64) + wv);
     const uint32_t run = __builtin_amdgcn_readlane(tinc, kTot - 1);
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < NG; k++) {
+        const uint32_t lo = (uint32_t)(k * (NT * 8) + tid * 8);
         cstart[k] = (lo < rem && ((t0m + lo) & p.Cmask) == 0) ? base[k] + pre[k] : ~0u;
     }
     // the list in LDS: every escape's exponent, and its position as well
@@ -756,12 +761,12 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
     const bool lst = want_pos && run <= (uint32_t)kPosListMax;
     if (want_pos && !lst) {
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++)
-            aux[(uint32_t)(k * (kEncThreads * 8) + tid * 8) >> 3] = (uint8_t)flags_byte(fl[k]);
+        for (int k = 0; k < NG; k++)
+            aux[(uint32_t)(k * (NT * 8) + tid * 8) >> 3] = (uint8_t)flags_byte(fl[k]);
     }
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < NG; k++) {
+        const uint32_t lo = (uint32_t)(k * (NT * 8) + tid * 8);
         uint32_t rank = base[k] + pre[k];
         const uint32_t g0m = (t0m + lo) & p.Cmask;          // a multiple of 8, below C
         uint32_t mask = fl[k];
@@ -789,7 +794,7 @@ __device__ __forceinline__ uint32_t encode_dense_rank(const uint32_t xw[kEncGrou
 // from the Infinity Cache.
 // G groups of GW values per thread (group k of thread tid starts at tile
 // value k*kEncThreads*GW + tid*GW).
-template <int G = kEncGroups, int GW = 8>
+template <int G = kEncGroups, int GW = 8, int NT = kEncThreads>
 __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[G], uint64_t t0,
                                               uint64_t tile, const EncWs &ws, const EncParams &p,
                                               const EscBuf &eb)
@@ -800,7 +805,7 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
         uint32_t *cpt = ws.chunk_pre + (t0 >> p.logC);     // chunks no larger than the tile start at t0
 #pragma unroll
         for (int k = 0; k < G; k++) {
-            const uint32_t lo = (uint32_t)(k * (kEncThreads * GW) + tid * GW);
+            const uint32_t lo = (uint32_t)(k * (NT * GW) + tid * GW);
             if (cstart[k] != ~0u) cpt[lo >> p.logC] = cstart[k];
         }
     }
@@ -809,11 +814,11 @@ __device__ __forceinline__ void stage_escapes(uint32_t m, const uint32_t cstart[
     if (p.posw && m <= (uint32_t)kPosListMax) {
         u32x4 *sp = reinterpret_cast<u32x4 *>(ws.stage_aux + tile * kAux);
         const u32x4 *lp = reinterpret_cast<const u32x4 *>(eb.pos);
-        for (uint32_t q = tid; q < (m + 7) / 8; q += kEncThreads) sp[q] = lp[q];
+        for (uint32_t q = tid; q < (m + 7) / 8; q += NT) sp[q] = lp[q];
     }
     u32x4 *sv = reinterpret_cast<u32x4 *>(ws.stage_val + tile * kEncTile);
     const u32x4 *lv = reinterpret_cast<const u32x4 *>(eb.val);
-    for (uint32_t q = tid; q < (m + 15) / 16; q += kEncThreads) sv[q] = lv[q];
+    for (uint32_t q = tid; q < (m + 15) / 16; q += NT) sv[q] = lv[q];
 }
 
 template <int kCodes>
@@ -1707,19 +1712,21 @@ struct StreamSet {
 
 // Dense loads of one input's part of a tile: per group, 8 sign-mantissa
 // bytes and 4 code bytes.
+template <int NT, int NG>
 struct DenseIn {
-    u32x2 sm[kEncGroups];
-    uint32_t cd[kEncGroups];
+    u32x2 sm[NG];
+    uint32_t cd[NG];
 };
 
+template <int NT, int NG>
 __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint32_t rem, const DecParams &p,
-                                           DenseIn &d)
+                                           DenseIn<NT, NG> &d)
 {
     const int tid = threadIdx.x;
     const uint8_t *smt = s.base + kHeader + t0, *cdt = s.base + p.off_codes + t0 / 2;
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < NG; k++) {
+        const uint32_t lo = (uint32_t)(k * (NT * 8) + tid * 8);
         if (lo < rem) {
             d.sm[k] = ld_stream(reinterpret_cast<const u32x2 *>(smt + lo));
             d.cd[k] = ld_stream(reinterpret_cast<const uint32_t *>(cdt + lo / 2));
@@ -1730,27 +1737,31 @@ __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint3
     }
 }
 
-// One tile of the k-input reduce. Each thread keeps binary32 sums of its
-// 4 groups of 8 words. The inputs are taken two at a time: both are loaded
-// and decoded, their escapes are patched through the two LDS exponent tiles
-// between one pair of barriers (half the barriers of one input at a time),
-// and they are added to the sums in input order. The sums start at -0.0
-// (-0.0 + x is x for every binary32 x but a NaN, which stays a NaN: the
-// first add sets them exactly). They are rounded once to BF16 and encoded
-// like k_reduce_tile.
-__global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uint8_t *__restrict__ out,
-                                                               EncWs ws, EncParams ep, DecParams dp)
+constexpr int kRkThreads = kEncThreads;
+constexpr int kRkGroups = kEncTile / (kRkThreads * 8);
+static_assert(kRkThreads * kRkGroups * 8 == kEncTile && kRkGroups * (kRkThreads / 64) <= 16, "k-input reduce tile shape");
+
+// One tile of the k-input reduce, kRkThreads threads per tile, each keeping
+// binary32 sums of its kRkGroups groups of 8 words. The inputs are taken two
+// at a time: both are loaded and decoded, their escapes are patched through
+// the two LDS exponent tiles between one pair of barriers (half the barriers
+// of one input at a time), and they are added to the sums in input order.
+// The sums start at -0.0 (-0.0 + x is x for every binary32 x but a NaN,
+// which stays a NaN: the first add sets them exactly). They are rounded once
+// to BF16 and encoded like k_reduce_tile.
+__global__ __launch_bounds__(kRkThreads) void k_reduce_k_tile(StreamSet ss, uint8_t *__restrict__ out,
+                                                              EncWs ws, EncParams ep, DecParams dp)
 {
-    __shared__ EncShared esh;
+    __shared__ EncSharedT<kRkThreads, kRkGroups> esh;
     __shared__ ReduceLds lds;
     const int tid = threadIdx.x;
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
     const uint32_t rem = enc_tile_words(t0, ep);
     uint32_t dec[4] = {dp.dec[0], dp.dec[1], dp.dec[2], dp.dec[3]};
-    float acc[kEncGroups][8];
+    float acc[kRkGroups][8];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++)
+    for (int k = 0; k < kRkGroups; k++)
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
     bool synced = false;                                // a barrier has published the code table
@@ -1758,22 +1769,22 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         const bool two = i + 1 < ss.k;                  // the same in every thread
         const StreamIn s0 = ss.in[i];
         const StreamIn s1 = ss.in[two ? i + 1 : i];
-        const PatchHead h0 = patch_begin<kEncTile, kEncThreads>(s0, t0, dp);
+        const PatchHead h0 = patch_begin<kEncTile, kRkThreads>(s0, t0, dp);
         PatchHead h1 = h0;
-        DenseIn d0, d1;
+        DenseIn<kRkThreads, kRkGroups> d0, d1;
         load_dense(s0, t0, rem, dp, d0);
         if (two) {
-            h1 = patch_begin<kEncTile, kEncThreads>(s1, t0, dp);
+            h1 = patch_begin<kEncTile, kRkThreads>(s1, t0, dp);
             load_dense(s1, t0, rem, dp, d1);
         }
         if (i == 0) load_shared_lut(esh, ep.lut);   // after the first data loads are in flight
-        const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kEncThreads, kRedFetch>(s0, t0, dp, h0);
+        const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s0, t0, dp, h0);
         PatchFetch<kRedFetch> f1 = f0;
         f1.live = false;
-        if (two) f1 = patch_fetch<kEncTile, kEncThreads, kRedFetch>(s1, t0, dp, h1);
-        uint32_t e0[kEncGroups][2], e1[kEncGroups][2];
+        if (two) f1 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1);
+        uint32_t e0[kRkGroups][2], e1[kRkGroups][2];
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) {
+        for (int k = 0; k < kRkGroups; k++) {
             decode8_e(d0.cd[k], dec, e0[k]);
             if (two) decode8_e(d1.cd[k], dec, e1[k]);
         }
@@ -1781,20 +1792,20 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
             // each thread rewrites only its own bytes here, which no thread
             // reads after the previous pair's second barrier but itself
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++) {
-                const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            for (int k = 0; k < kRkGroups; k++) {
+                const uint32_t lo = (uint32_t)(k * (kRkThreads * 8) + tid * 8);
                 if (f0.live) ex_put8(lds.ex.a, lo, e0[k]);
                 if (f1.live) ex_put8(lds.ex.b, lo, e1[k]);
             }
             if (f0.live) patch_put_offs(t0, dp, h0, f0, lds.ex.a);
             if (f1.live) patch_put_offs(t0, dp, h1, f1, lds.ex.b);
             __syncthreads();
-            if (f0.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(s0, t0, dp, h0, f0, lds.ex.a);
-            if (f1.live) patch_scatter<kEncTile, kEncThreads, kRedFetch>(s1, t0, dp, h1, f1, lds.ex.b);
+            if (f0.live) patch_scatter<kEncTile, kRkThreads, kRedFetch>(s0, t0, dp, h0, f0, lds.ex.a);
+            if (f1.live) patch_scatter<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1, f1, lds.ex.b);
             __syncthreads();
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++) {
-                const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+            for (int k = 0; k < kRkGroups; k++) {
+                const uint32_t lo = (uint32_t)(k * (kRkThreads * 8) + tid * 8);
                 if (f0.live) ex_get8(lds.ex.a, lo, e0[k]);
                 if (f1.live) ex_get8(lds.ex.b, lo, e1[k]);
             }
@@ -1802,7 +1813,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         }
         // inputs i, then i + 1: the sums keep the input order
 #pragma unroll
-        for (int k = 0; k < kEncGroups; k++) {
+        for (int k = 0; k < kRkGroups; k++) {
             float f[8];
             floats8(d0.sm[k].x, d0.sm[k].y, e0[k], f);
 #pragma unroll
@@ -1810,7 +1821,7 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
         }
         if (two) {
 #pragma unroll
-            for (int k = 0; k < kEncGroups; k++) {
+            for (int k = 0; k < kRkGroups; k++) {
                 float f[8];
                 floats8(d1.sm[k].x, d1.sm[k].y, e1[k], f);
 #pragma unroll
@@ -1818,10 +1829,10 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
             }
         }
     }
-    uint32_t r[kEncGroups][4];
+    uint32_t r[kRkGroups][4];
 #pragma unroll
-    for (int k = 0; k < kEncGroups; k++) {
-        const uint32_t lo = (uint32_t)(k * (kEncThreads * 8) + tid * 8);
+    for (int k = 0; k < kRkGroups; k++) {
+        const uint32_t lo = (uint32_t)(k * (kRkThreads * 8) + tid * 8);
         bool nan = false;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
@@ -1838,10 +1849,10 @@ __global__ __launch_bounds__(kEncThreads) void k_reduce_k_tile(StreamSet ss, uin
             if (lo >= rem) r[k][q] = 0u;
     }
     if (!synced) __syncthreads();
-    uint32_t cstart[kEncGroups];
-    const uint32_t m = encode_dense_rank<kCodeNib>(r, t0, rem, out, ep, esh, lds.esc, cstart,
+    uint32_t cstart[kRkGroups];
+    const uint32_t m = encode_dense_rank<kCodeNib, kRkThreads, kRkGroups>(r, t0, rem, out, ep, esh, lds.esc, cstart,
                                                    ws.stage_aux + tile * kAux);
-    stage_escapes(m, cstart, t0, tile, ws, ep, lds.esc);
+    stage_escapes<kRkGroups, 8, kRkThreads>(m, cstart, t0, tile, ws, ep, lds.esc);
 }
 
 // ============================================================ FP8 E5M2 ====
@@ -3329,7 +3340,7 @@ int uzip_reduce_k_ex(const void *const *d_in, const uint64_t *in_bytes, uint32_t
     const EncWs ws = make_ws(d_ws, n, chunk);
     const Events ev{opts, s};
     if ((rc = ev.record(0))) return rc;
-    k_reduce_k_tile<<<(unsigned)ep.ntiles, kEncThreads, 0, s>>>(ss, static_cast<uint8_t *>(d_out), ws, ep, dp);
+    k_reduce_k_tile<<<(unsigned)ep.ntiles, kRkThreads, 0, s>>>(ss, static_cast<uint8_t *>(d_out), ws, ep, dp);
     UZIP_LAUNCH_CHECK("k_reduce_k_tile");
     if ((rc = ev.record(1))) return rc;
     return finish_encode(L, cb, ep, ws, static_cast<uint8_t *>(d_out), ev, s);
