@@ -352,7 +352,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the codec shards by chunk with no cross-GPU exchange; see the design notes)",
+              "(the codec shards by chunk with no cross-GPU exchange)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1042,12 +1042,74 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v)
 #endif
 constexpr int kPlaceT = UZIP_PLACE_T;              // consecutive tiles per placement wave
 static_assert(kPlaceT >= 1 && 64 % kPlaceT == 0, "a wave's tiles lie in one group of 2^gshift >= 64 tiles");
+#ifndef UZIP_PLACE_DIRECT
+#define UZIP_PLACE_DIRECT 2
+#endif
+// A tile with at most 64 * kDirectR escapes is placed one escape per lane
+// (a 2-byte and a 1-byte store each, coalesced across the wave) instead of
+// by shifted 16-byte blocks.
+constexpr int kDirectR = UZIP_PLACE_DIRECT;
+static_assert(kDirectR >= 1 && 64 * kDirectR <= kPosListMax, "a directly placed tile has its positions listed");
 
 // What the first load round fetches for one tile.
 struct PlaceIn {
     u32x4 ap, vp;                                  // the slot's first KiB of each part, 16 bytes per lane
     uint32_t cp[2];                                // in-tile prefixes of the chunks starting in the tile
+    uint32_t dp, dv;                               // entry `lane` of the slot's position list and exponents
 };
+
+// The offsets of the chunks that start in a tile whose first escape goes to
+// global index P.
+__device__ __forceinline__ void place_offsets(uint8_t *__restrict__ out, const EncParams &p, uint64_t tile,
+                                              uint32_t P, const PlaceIn &in)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t t0 = tile * kEncTile;
+    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
+    if (p.Cmask + 1 < (uint32_t)kEncTile) {
+        const uint64_t c0 = t0 >> p.logC;
+        uint64_t cn = (uint64_t)kEncTile >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + in.cp[i];
+    } else if ((t0 & p.Cmask) == 0 && lane == 0) {
+        offs[t0 >> p.logC] = P;
+    }
+}
+
+// A tile with m <= 64 * kDirectR escapes (its positions listed in the slot,
+// when the format has them): escape k is written by lane k mod 64, its
+// position to pos[P + k] and its exponent to val[P + k]; entry `lane` came
+// with the first load round, the others are loaded here.
+__device__ __forceinline__ void place_direct(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
+                                             uint64_t tile, uint32_t m, uint32_t P, uint64_t M, const PlaceIn &in)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
+    uint16_t *dpos = reinterpret_cast<uint16_t *>(out + p.off_pos) + P;
+    uint8_t *dval = out + off_val + P;
+    const uint16_t *spos = reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux);
+    const uint8_t *sval = ws.stage_val + tile * kEncTile;
+    uint32_t ps[kDirectR], vs[kDirectR];
+    ps[0] = in.dp;
+    vs[0] = in.dv;
+#pragma unroll
+    for (int r = 1; r < kDirectR; r++) {
+        const uint32_t k = lane + 64u * r;
+        ps[r] = (p.posw && k < m) ? spos[k] : 0u;
+        vs[r] = k < m ? sval[k] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kDirectR; r++) {
+        const uint32_t k = lane + 64u * r;
+        if (k < m) {
+            if (p.posw) st_stream((uint16_t)ps[r], dpos + k);
+            st_stream((uint8_t)vs[r], dval + k);
+        }
+    }
+    place_offsets(out, p, tile, P, in);
+}
 
 __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
                                            uint64_t tile, uint32_t m, uint32_t P, uint64_t M, const PlaceIn &in,
@@ -1163,17 +1225,7 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
         uint8_t *edst = is_p ? qp.dst : qv.dst;
         edst[ej] = (uint8_t)eb;
     }
-    // offsets of the chunks that start in the tile
-    if (C < (uint32_t)kEncTile) {
-        const uint64_t c0 = t0 >> p.logC;
-        uint64_t cn = (uint64_t)kEncTile >> p.logC;
-        if (c0 + cn > p.nch) cn = p.nch - c0;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + in.cp[i];
-    } else if ((t0 & p.Cmask) == 0 && lane == 0) {
-        offs[t0 >> p.logC] = P;
-    }
+    place_offsets(out, p, tile, P, in);
 }
 
 __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
@@ -1193,8 +1245,9 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
 #pragma unroll
     for (int i = 0; i < kPlaceT; i++) {
         const uint64_t tile = tile0 + (i < (int)nt ? i : 0);
-        in[i].ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
-        in[i].vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
+        in[i].ap = in[i].vp = u32x4{0u, 0u, 0u, 0u};
+        in[i].dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
+        in[i].dv = ws.stage_val[tile * kEncTile + lane];
         in[i].cp[0] = in[i].cp[1] = 0u;
         if (C < (uint32_t)kEncTile) {
             const uint64_t c0 = (tile * kEncTile) >> p.logC;
@@ -1239,6 +1292,20 @@ __global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *_
         if (i >= (int)nt) break;
         const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(m_l, i);
         const uint32_t P = before_w + (uint32_t)__builtin_amdgcn_readlane(tp_l, i);
+        const uint64_t tile = tile0 + i;
+        if (m <= 64u * kDirectR) {
+            place_direct(ws, out, p, tile, m, P, M, in[i]);
+            continue;
+        }
+        {
+            // the slot's first KiB of each part, as far as the count says it is used
+            const uint32_t need_a = p.posw ? (m <= (uint32_t)kPosListMax ? 2 * m : (uint32_t)kAux) : 0u;
+            const uint32_t need_v = m < (uint32_t)kAux ? m : (uint32_t)kAux;
+            if (16u * (uint32_t)lane < need_a)
+                in[i].ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
+            if (16u * (uint32_t)lane < need_v)
+                in[i].vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
+        }
         place_tile(ws, out, p, tile0 + i, m, P, M, in[i], s_pos[wv]);
     }
     if (tile0 != 0) return;

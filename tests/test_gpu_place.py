@@ -1,0 +1,119 @@
+"""Escape placement across every per-tile escape count regime.
+
+The placement writes a tile's escapes either one per lane (light tiles) or
+as shifted 16-byte blocks from a position list or an escape bitmap (heavier
+tiles), and neighbouring tiles share the 16-byte blocks at their edges. Here
+consecutive 8192-value tiles carry escape counts on both sides of each
+boundary (0, 1, 63-65, 127-130, 255-257, 511-513, a few thousand, all), in
+mixed order and with the escapes spread out, bunched at the tile's start or
+bunched at its end, plus a ragged last tile. The streams must equal the
+oracle's byte for byte and decode to the input, for the BF16 format, the
+Top-15 + sentinel format (no position array) and the FP8 E5M2 format.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_bf16_tensor_amd import uzip
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TILE = 8192
+COUNTS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 130, 1, 255, 256, 257, 511, 512, 513, 128, 129, 0,
+          1000, 64, 8192, 127, 3, 129, 4096, 128, 65, 512, 513, 7]
+LAST = (5000, 100)             # the ragged last tile: values, escapes
+
+
+def escape_mask(seed):
+    """A boolean mask over the whole input with COUNTS[i] escapes in tile i."""
+    rng = np.random.default_rng(seed)
+    n = TILE * len(COUNTS) + LAST[0]
+    mask = np.zeros(n, dtype=bool)
+    for i, c in enumerate(COUNTS + [LAST[1]]):
+        size = TILE if i < len(COUNTS) else LAST[0]
+        t0 = i * TILE
+        where = i % 3                              # spread, at the start, at the end
+        if where == 0:
+            idx = rng.choice(size, c, replace=False)
+        elif where == 1:
+            idx = np.arange(c)
+        else:
+            idx = np.arange(size - c, size)
+        mask[t0 + idx] = True
+    return mask
+
+
+def bf16_input(seed, k=16):
+    """Words whose exponents are 120..120+k-1 (the codebook's) except at the
+    mask's escapes (exponents 200..215)."""
+    rng = np.random.default_rng(seed)
+    mask = escape_mask(seed)
+    n = mask.size
+    sm = rng.integers(0, 256, n).astype(np.uint16)
+    e = np.where(mask, rng.integers(200, 216, n), rng.integers(120, 120 + k, n)).astype(np.uint16)
+    x = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)
+    hist = np.zeros(256, np.uint64)
+    hist[120:136] = np.arange(16, 0, -1, dtype=np.uint64) * 100
+    return x.astype(np.uint16), hist, int(mask.sum())
+
+
+def to_dev(x_np, dtype=np.int16):
+    return torch.from_numpy(np.ascontiguousarray(x_np).view(dtype)).to(DEV)
+
+
+def compare(got, want, label):
+    assert got.size == want.size, f"{label}: size {got.size} != {want.size}"
+    if not np.array_equal(got, want):
+        bad = np.nonzero(got != want)[0]
+        pytest.fail(f"{label}: {bad.size} bytes differ, first at {bad[:8].tolist()}")
+
+
+@pytest.mark.parametrize("C", [64, 1024, 8192, 65536])
+def test_bf16_escape_counts(C):
+    x, hist, m_want = bf16_input(C)
+    ocb = oracle.top16(hist)
+    cb = uzip.codebook_from_hist(hist)
+    buf = uzip.encode(to_dev(x), cb, C)
+    total, m = uzip.stream_bytes(buf)
+    assert m == m_want
+    compare(buf[:total].cpu().numpy(), oracle.encode(x, C, ocb.dec), f"bf16 C={C}")
+    y = uzip.decode(buf, cb, x.size, C, in_bytes=total).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("C", [64, 1024, 4096])      # the format's largest chunk is 4096
+def test_sentinel_escape_counts(C):
+    x, hist, m_want = bf16_input(C + 1, k=15)       # the sentinel format codes 15 exponents
+    ocb = oracle.calibrate(np.repeat(np.array([oracle.merge(0, e) for e in range(120, 136)], np.uint16),
+                                     np.arange(16, 0, -1)))
+    cb = uzip.codebook_from_hist(ocb.hist)
+    buf = uzip.s15_encode(to_dev(x), cb, C)
+    total, m = uzip.stream_bytes(buf)
+    assert m == m_want
+    compare(buf[:total].cpu().numpy(), oracle.s15_encode(x, C, ocb.dec), f"s15 C={C}")
+    y = uzip.s15_decode(buf, cb, x.size, C, in_bytes=total).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("C", [64, 1024, 8192])
+def test_fp8_escape_counts(C):
+    rng = np.random.default_rng(C + 2)
+    mask = escape_mask(C + 2)
+    n = mask.size
+    a = rng.integers(0, 8, n)
+    e = np.where(mask, rng.integers(16, 32, n), rng.integers(0, 16, n))
+    # the merge for every value, vectorised: sign (bit 2 of a) to bit 7,
+    # the exponent to bits 2..6, the mantissa (bits 0..1 of a) to bits 0..1
+    x = (((a >> 2) & 1) << 7 | (e & 0x1F) << 2 | (a & 3)).astype(np.uint8)
+    assert all(int(x[i]) == oracle.fp8_merge(int(a[i]), int(e[i])) for i in range(64))
+    ocb = oracle.fp8_calibrate(np.repeat(np.array([oracle.fp8_merge(0, k) for k in range(16)], np.uint8),
+                                         np.arange(16, 0, -1)))
+    cb = uzip.codebook_from_hist(ocb.hist)
+    buf = uzip.fp8_encode(torch.from_numpy(x).to(DEV), cb, C)
+    total, m = uzip.stream_bytes(buf)
+    assert m == int(mask.sum())
+    compare(buf[:total].cpu().numpy(), oracle.fp8_encode(x, C, ocb.dec), f"fp8 C={C}")
+    y = uzip.fp8_decode(buf, cb, n, C, in_bytes=total).cpu().numpy()
+    assert np.array_equal(y, x)
