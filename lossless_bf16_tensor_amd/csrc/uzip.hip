@@ -1037,11 +1037,20 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v)
                  (uint32_t)__shfl(v.w, nl, 64)};
 }
 
-#ifndef UZIP_PLACE_T
-#define UZIP_PLACE_T 1
+#ifndef UZIP_PLACE_LIGHT_T
+#define UZIP_PLACE_LIGHT_T 16
 #endif
-constexpr int kPlaceT = UZIP_PLACE_T;              // consecutive tiles per placement wave
-static_assert(kPlaceT >= 1 && 64 % kPlaceT == 0, "a wave's tiles lie in one group of 2^gshift >= 64 tiles");
+// When the escapes average at most kLightAvg per tile, one placement wave
+// takes kLightT consecutive tiles (the rest of the grid exits at once), so
+// that their escapes and chunk offsets go out from one wave in runs rather
+// than as short pieces from many; otherwise one wave takes one tile.
+constexpr int kLightT = UZIP_PLACE_LIGHT_T;
+constexpr uint32_t kLightAvg = 64;
+static_assert(kLightT >= 1 && kLightT <= 64 && 64 % kLightT == 0, "a wave's tiles lie in one group of 2^gshift >= 64 tiles");
+#ifndef UZIP_PLACE_WAVES
+#define UZIP_PLACE_WAVES 4
+#endif
+constexpr int kPlaceThreads = 64 * UZIP_PLACE_WAVES;  // one wave per tile, UZIP_PLACE_WAVES per workgroup
 #ifndef UZIP_PLACE_DIRECT
 #define UZIP_PLACE_DIRECT 2
 #endif
@@ -1108,7 +1117,6 @@ __device__ __forceinline__ void place_direct(const EncWs &ws, uint8_t *__restric
             st_stream((uint8_t)vs[r], dval + k);
         }
     }
-    place_offsets(out, p, tile, P, in);
 }
 
 __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
@@ -1117,12 +1125,10 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
 {
     const int lane = threadIdx.x & 63;
     const uint64_t t0 = tile * kEncTile;
-    const uint32_t C = p.Cmask + 1;
     const u32x4 ap = in.ap, vp = in.vp;
     const uint8_t *src_v = ws.stage_val + tile * kEncTile;
     const u32x4 *sv4 = reinterpret_cast<const u32x4 *>(src_v);
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
-    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // ---- positions
     const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, (p.posw && m <= kPosListMax) ? 2 * (uint64_t)m : 0);
     if (qp.nblk) {                                  // a short list, from the prefetched bytes
@@ -1225,90 +1231,164 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
         uint8_t *edst = is_p ? qp.dst : qv.dst;
         edst[ej] = (uint8_t)eb;
     }
-    place_offsets(out, p, tile, P, in);
 }
 
-__global__ __launch_bounds__(kThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
-                                                            HeaderParams hp)
+// The first KiB of each staged part of a heavy tile (16 bytes per lane), as
+// far as its count says it is used.
+__device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncParams &p, uint64_t tile, uint32_t m,
+                                                  PlaceIn &in)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t need_a = p.posw ? (m <= (uint32_t)kPosListMax ? 2 * m : (uint32_t)kAux) : 0u;
+    const uint32_t need_v = m < (uint32_t)kAux ? m : (uint32_t)kAux;
+    in.ap = in.vp = u32x4{0u, 0u, 0u, 0u};
+    if (16u * lane < need_a) in.ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
+    if (16u * lane < need_v) in.vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
+}
+
+// One wave, nt <= kLightT consecutive tiles of one group (few escapes):
+// every tile's count, prefix and first 64 staged entries in one load round;
+// a tile with at most 64 escapes is stored from those (one with more is
+// placed by its own wave); the chunk offsets of all the tiles go out
+// together, 64 per store.
+__device__ __forceinline__ void place_run(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
+                                              uint64_t tile0, uint32_t nt, uint32_t before_w, uint64_t M)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t m_l = lane < nt ? ws.counts[tile0 + lane] : 0u;
+    const uint32_t P_l = before_w + (lane < nt ? ws.tpre[tile0 + lane] : 0u);
+    uint32_t e[kLightT];                    // entry `lane` of tile j: exponent << 16 | position
+#pragma unroll
+    for (int j = 0; j < kLightT; j++) {
+        const uint64_t t = tile0 + ((uint32_t)j < nt ? (uint32_t)j : 0u);
+        const uint32_t ps = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + t * kAux)[lane] : 0u;
+        e[j] = (uint32_t)ws.stage_val[t * kEncTile + lane] << 16 | ps;
+    }
+    // the chunks that start in these tiles, lane-strided: the first 256 of
+    // their in-tile prefixes come with the same round
+    const bool small_c = p.Cmask + 1 < (uint32_t)kEncTile;
+    uint64_t c0 = 0, cn = 0;
+    uint32_t cp[4] = {0u, 0u, 0u, 0u};
+    if (small_c) {
+        c0 = (tile0 * kEncTile) >> p.logC;
+        cn = ((uint64_t)nt * kEncTile) >> p.logC;
+        if (c0 + cn > p.nch) cn = p.nch - c0;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (lane + 64u * r < cn) cp[r] = ws.chunk_pre[c0 + lane + 64u * r];
+    }
+    const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
+    uint16_t *dpos = reinterpret_cast<uint16_t *>(out + p.off_pos);
+    uint8_t *dval = out + off_val;
+#pragma unroll
+    for (int j = 0; j < kLightT; j++) {
+        // lanes past nt hold m = 0
+        const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(m_l, j);
+        const uint32_t P = (uint32_t)__builtin_amdgcn_readlane(P_l, j);
+        if (m <= 64u && lane < m) {
+            if (p.posw) st_stream((uint16_t)e[j], dpos + P + lane);
+            st_stream((uint8_t)(e[j] >> 16), dval + P + lane);
+        }
+    }
+    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
+    if (small_c) {
+        // chunk c's tile is c >> (13 - logC) (2^13 words per tile); its
+        // prefix is read from that tile's lane with every lane active
+        static_assert(kEncTile == 1 << 13, "chunks per tile as a shift");
+        const uint32_t sh = 13u - p.logC;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const uint64_t c = lane + 64u * r;
+            if (64u * r >= cn) break;
+            const uint32_t jt = (uint32_t)(c >> sh);
+            const uint32_t Pj = (uint32_t)__shfl((int)P_l, (int)(jt < nt ? jt : 0u), 64);
+            if (c < cn) offs[c0 + c] = Pj + cp[r];
+        }
+        for (uint64_t b = 256; b < cn; b += 64) {
+            const uint64_t c = b + lane;
+            const uint32_t jt = (uint32_t)(c >> sh);
+            const uint32_t Pj = (uint32_t)__shfl((int)P_l, (int)(jt < nt ? jt : 0u), 64);
+            if (c < cn) offs[c0 + c] = Pj + ws.chunk_pre[c0 + c];
+        }
+    } else if (lane < nt) {
+        const uint64_t t0 = (tile0 + lane) * kEncTile;
+        if ((t0 & p.Cmask) == 0) offs[t0 >> p.logC] = P_l;
+    }
+}
+
+// Sum of the group sums before group g (lane-strided over the first 256 in
+// gs, the rest loaded), as a wave total.
+__device__ __forceinline__ uint32_t groups_before(const EncWs &ws, const EncParams &p, const uint32_t gs[4],
+                                                  uint64_t g)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t before = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        if ((uint64_t)lane + 64 * i < g) before += gs[i];
+    for (uint64_t q = (uint64_t)lane + 256; q < g; q += 64) before += ws.gsum[q];
+    return (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
+}
+
+__global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
+                                                                 HeaderParams hp)
 {
     // one buffer of positions per wave: a pass, plus the carried partial block
-    __shared__ __attribute__((aligned(16))) uint16_t s_pos[kThreads / 64][kPassVals + 16];
+    __shared__ __attribute__((aligned(16))) uint16_t s_pos[kPlaceThreads / 64][kPassVals + 16];
     // wave-uniform values are moved to scalar registers (readfirstlane)
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t tile0 = ((uint64_t)blockIdx.x * (kThreads / 64) + wv) * kPlaceT;
-    if (tile0 >= p.ntiles) return;
-    const uint32_t nt = (uint32_t)((p.ntiles - tile0 < (uint64_t)kPlaceT) ? p.ntiles - tile0 : (uint64_t)kPlaceT);
-    const uint32_t C = p.Cmask + 1;
-    // ---- the one load round, for all the wave's tiles
-    PlaceIn in[kPlaceT];
-#pragma unroll
-    for (int i = 0; i < kPlaceT; i++) {
-        const uint64_t tile = tile0 + (i < (int)nt ? i : 0);
-        in[i].ap = in[i].vp = u32x4{0u, 0u, 0u, 0u};
-        in[i].dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
-        in[i].dv = ws.stage_val[tile * kEncTile + lane];
-        in[i].cp[0] = in[i].cp[1] = 0u;
-        if (C < (uint32_t)kEncTile) {
-            const uint64_t c0 = (tile * kEncTile) >> p.logC;
-            uint64_t cn = (uint64_t)kEncTile >> p.logC;
-            if (c0 + cn > p.nch) cn = p.nch - c0;
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-                if ((uint64_t)lane + 64 * j < cn) in[i].cp[j] = ws.chunk_pre[c0 + lane + 64 * j];
-        }
-    }
-    // lane i < nt: tile i's count and in-group prefix
-    const uint32_t m_l = (lane < (int)nt) ? ws.counts[tile0 + lane] : 0u;
-    const uint32_t tp_l = (lane < (int)nt) ? ws.tpre[tile0 + lane] : 0u;
-    const uint64_t g = tile0 >> p.gshift;
+    const uint64_t wave = (uint64_t)blockIdx.x * (kPlaceThreads / 64) + wv;
+    // ---- first round: the group sums (L2-resident) and the count of tile `wave`
     uint32_t gs[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const uint64_t q = (uint64_t)lane + 64 * i;
         gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
     }
-    // ---- the prefix
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint64_t q = (uint64_t)lane + 64 * i;
-        all += gs[i];
-        if (q < g) before += gs[i];
-    }
-    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) {
-        const uint32_t v = ws.gsum[q];
-        all += v;
-        if (q < g) before += v;
-    }
-    // the wave totals: lane 63 of DPP inclusive scans (no LDS round trips)
-    const uint32_t before_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
-    const uint32_t all_w = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
+    const uint32_t m_own = wave < p.ntiles ? ws.counts[wave] : 0u;
+    uint32_t all = gs[0] + gs[1] + gs[2] + gs[3];
+    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) all += ws.gsum[q];
     // readlane returns a signed int: through uint32_t, so that an M of 2^31
     // or more is not sign-extended
-    const uint64_t M = all_w;
-#pragma unroll
-    for (int i = 0; i < kPlaceT; i++) {
-        if (i >= (int)nt) break;
-        const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(m_l, i);
-        const uint32_t P = before_w + (uint32_t)__builtin_amdgcn_readlane(tp_l, i);
-        const uint64_t tile = tile0 + i;
-        if (m <= 64u * kDirectR) {
-            place_direct(ws, out, p, tile, m, P, M, in[i]);
-            continue;
-        }
-        {
-            // the slot's first KiB of each part, as far as the count says it is used
-            const uint32_t need_a = p.posw ? (m <= (uint32_t)kPosListMax ? 2 * m : (uint32_t)kAux) : 0u;
-            const uint32_t need_v = m < (uint32_t)kAux ? m : (uint32_t)kAux;
-            if (16u * (uint32_t)lane < need_a)
-                in[i].ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
-            if (16u * (uint32_t)lane < need_v)
-                in[i].vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
-        }
-        place_tile(ws, out, p, tile0 + i, m, P, M, in[i], s_pos[wv]);
+    const uint64_t M = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
+    // With few escapes, wave w places the tiles of run w (kLightT tiles) that
+    // have at most 64 escapes and all their chunk offsets, and tile w if it
+    // has more; otherwise wave w places tile w.
+    const bool light = M <= (uint64_t)kLightAvg * p.ntiles;
+    const bool run = light && wave * kLightT < p.ntiles;
+    const bool own = wave < p.ntiles && (!light || m_own > 64u);
+    if (!run && !own && wave != 0) return;
+    if (run) {
+        const uint64_t tile0 = wave * kLightT;
+        const uint32_t nt = (uint32_t)((p.ntiles - tile0 < (uint64_t)kLightT) ? p.ntiles - tile0 : (uint64_t)kLightT);
+        place_run(ws, out, p, tile0, nt, groups_before(ws, p, gs, tile0 >> p.gshift), M);
     }
-    if (tile0 != 0) return;
+    if (own) {
+        const uint64_t tile = wave;
+        PlaceIn in;
+        in.cp[0] = in.cp[1] = 0u;
+        if (!light && p.Cmask + 1 < (uint32_t)kEncTile) {
+            const uint64_t c0 = (tile * kEncTile) >> p.logC;
+            uint64_t cn = (uint64_t)kEncTile >> p.logC;
+            if (c0 + cn > p.nch) cn = p.nch - c0;
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                if ((uint64_t)lane + 64 * j < cn) in.cp[j] = ws.chunk_pre[c0 + lane + 64 * j];
+        }
+        in.dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
+        in.dv = ws.stage_val[tile * kEncTile + lane];
+        const uint32_t P = groups_before(ws, p, gs, tile >> p.gshift) + ws.tpre[tile];
+        const uint32_t m = m_own;
+        if (m <= 64u * kDirectR) {
+            place_direct(ws, out, p, tile, m, P, M, in);
+        } else {
+            place_load_blocks(ws, p, tile, m, in);
+            place_tile(ws, out, p, tile, m, P, M, in, s_pos[wv]);
+        }
+        if (!light) place_offsets(out, p, tile, P, in);
+    }
+    if (wave != 0) return;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
     // header: template + M + total_bytes
@@ -1804,6 +1884,9 @@ __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint3
     }
 }
 
+#ifndef UZIP_RK_PIPE
+#define UZIP_RK_PIPE 0
+#endif
 constexpr int kRkThreads = kEncThreads;
 constexpr int kRkGroups = kEncTile / (kRkThreads * 8);
 static_assert(kRkThreads * kRkGroups * 8 == kEncTile && kRkGroups * (kRkThreads / 64) <= 16, "k-input reduce tile shape");
@@ -1832,10 +1915,42 @@ __global__ __launch_bounds__(kRkThreads) void k_reduce_k_tile(StreamSet ss, uint
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
     bool synced = false;                                // a barrier has published the code table
+#if UZIP_RK_PIPE
+    // pair 0's chunk offsets and dense bytes; each pair then issues the next
+    // pair's right after its own escape loads, so that they are in flight
+    // during its patch (whose barriers wait for LDS traffic only) and adds
+    PatchHead nh0 = patch_begin<kEncTile, kRkThreads>(ss.in[0], t0, dp), nh1 = nh0;
+    DenseIn<kRkThreads, kRkGroups> nd0, nd1;
+    load_dense(ss.in[0], t0, rem, dp, nd0);
+    nd1 = nd0;
+    if (ss.k > 1) {
+        nh1 = patch_begin<kEncTile, kRkThreads>(ss.in[1], t0, dp);
+        load_dense(ss.in[1], t0, rem, dp, nd1);
+    }
+    load_shared_lut(esh, ep.lut);
+#endif
     for (uint32_t i = 0; i < ss.k; i += 2) {
         const bool two = i + 1 < ss.k;                  // the same in every thread
         const StreamIn s0 = ss.in[i];
         const StreamIn s1 = ss.in[two ? i + 1 : i];
+#if UZIP_RK_PIPE
+        const PatchHead h0 = nh0, h1 = nh1;
+        const DenseIn<kRkThreads, kRkGroups> d0 = nd0, d1 = nd1;
+        const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s0, t0, dp, h0);
+        PatchFetch<kRedFetch> f1 = f0;
+        f1.live = false;
+        if (two) f1 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1);
+        if (i + 2 < ss.k) {
+            const StreamIn n0 = ss.in[i + 2];
+            nh0 = patch_begin<kEncTile, kRkThreads>(n0, t0, dp);
+            load_dense(n0, t0, rem, dp, nd0);
+            if (i + 3 < ss.k) {
+                const StreamIn n1 = ss.in[i + 3];
+                nh1 = patch_begin<kEncTile, kRkThreads>(n1, t0, dp);
+                load_dense(n1, t0, rem, dp, nd1);
+            }
+        }
+#else
         const PatchHead h0 = patch_begin<kEncTile, kRkThreads>(s0, t0, dp);
         PatchHead h1 = h0;
         DenseIn<kRkThreads, kRkGroups> d0, d1;
@@ -1849,6 +1964,7 @@ __global__ __launch_bounds__(kRkThreads) void k_reduce_k_tile(StreamSet ss, uint
         PatchFetch<kRedFetch> f1 = f0;
         f1.live = false;
         if (two) f1 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1);
+#endif
         uint32_t e0[kRkGroups][2], e1[kRkGroups][2];
 #pragma unroll
         for (int k = 0; k < kRkGroups; k++) {
@@ -2675,7 +2791,8 @@ int finish_encode(const Layout &L, const uzip_codebook_t *cb, const EncParams &e
     UZIP_LAUNCH_CHECK("k_group_sums");
     int rc = ev.record(ev0);
     if (rc) return rc;
-    k_place_escapes<<<(unsigned)((ep.ntiles + kPlaceT * (kThreads / 64) - 1) / (kPlaceT * (kThreads / 64))), kThreads, 0, s>>>(ws, out, ep, hp);
+    k_place_escapes<<<(unsigned)((ep.ntiles + kPlaceThreads / 64 - 1) / (kPlaceThreads / 64)), kPlaceThreads, 0, s>>>(
+        ws, out, ep, hp);
     UZIP_LAUNCH_CHECK("k_place_escapes");
     return ev.record(ev0 + 1);
 }

@@ -6,9 +6,12 @@ tiles), and neighbouring tiles share the 16-byte blocks at their edges. Here
 consecutive 8192-value tiles carry escape counts on both sides of each
 boundary (0, 1, 63-65, 127-130, 255-257, 511-513, a few thousand, all), in
 mixed order and with the escapes spread out, bunched at the tile's start or
-bunched at its end, plus a ragged last tile. The streams must equal the
-oracle's byte for byte and decode to the input, for the BF16 format, the
-Top-15 + sentinel format (no position array) and the FP8 E5M2 format.
+bunched at its end, plus a ragged last tile. With `pad` escape-free tiles
+added, the average falls to under 64 escapes per tile, where each placement
+wave takes a run of consecutive tiles and the heavier ones are placed by
+their own waves; both regimes run here. The streams must equal the oracle's
+byte for byte and decode to the input, for the BF16 format, the Top-15 +
+sentinel format (no position array) and the FP8 E5M2 format.
 """
 import numpy as np
 import pytest
@@ -26,13 +29,18 @@ COUNTS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 130, 1, 255, 256, 257, 511, 512, 5
 LAST = (5000, 100)             # the ragged last tile: values, escapes
 
 
-def escape_mask(seed):
-    """A boolean mask over the whole input with COUNTS[i] escapes in tile i."""
+PADS = [0, 300]                # escape-free tiles added: 300 brings the average under 64
+
+
+def escape_mask(seed, pad=0):
+    """A boolean mask over the whole input with COUNTS[i] escapes in tile i,
+    then `pad` tiles without escapes and the ragged last tile."""
     rng = np.random.default_rng(seed)
-    n = TILE * len(COUNTS) + LAST[0]
+    counts = COUNTS + [0] * pad
+    n = TILE * len(counts) + LAST[0]
     mask = np.zeros(n, dtype=bool)
-    for i, c in enumerate(COUNTS + [LAST[1]]):
-        size = TILE if i < len(COUNTS) else LAST[0]
+    for i, c in enumerate(counts + [LAST[1]]):
+        size = TILE if i < len(counts) else LAST[0]
         t0 = i * TILE
         where = i % 3                              # spread, at the start, at the end
         if where == 0:
@@ -45,11 +53,11 @@ def escape_mask(seed):
     return mask
 
 
-def bf16_input(seed, k=16):
+def bf16_input(seed, k=16, pad=0):
     """Words whose exponents are 120..120+k-1 (the codebook's) except at the
     mask's escapes (exponents 200..215)."""
     rng = np.random.default_rng(seed)
-    mask = escape_mask(seed)
+    mask = escape_mask(seed, pad)
     n = mask.size
     sm = rng.integers(0, 256, n).astype(np.uint16)
     e = np.where(mask, rng.integers(200, 216, n), rng.integers(120, 120 + k, n)).astype(np.uint16)
@@ -70,9 +78,11 @@ def compare(got, want, label):
         pytest.fail(f"{label}: {bad.size} bytes differ, first at {bad[:8].tolist()}")
 
 
+@pytest.mark.parametrize("pad", PADS)
 @pytest.mark.parametrize("C", [64, 1024, 8192, 65536])
-def test_bf16_escape_counts(C):
-    x, hist, m_want = bf16_input(C)
+def test_bf16_escape_counts(C, pad):
+    x, hist, m_want = bf16_input(C, pad=pad)
+    assert (m_want <= 64 * ((x.size + TILE - 1) // TILE)) == (pad > 0)
     ocb = oracle.top16(hist)
     cb = uzip.codebook_from_hist(hist)
     buf = uzip.encode(to_dev(x), cb, C)
@@ -83,9 +93,10 @@ def test_bf16_escape_counts(C):
     assert np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("pad", PADS)
 @pytest.mark.parametrize("C", [64, 1024, 4096])      # the format's largest chunk is 4096
-def test_sentinel_escape_counts(C):
-    x, hist, m_want = bf16_input(C + 1, k=15)       # the sentinel format codes 15 exponents
+def test_sentinel_escape_counts(C, pad):
+    x, hist, m_want = bf16_input(C + 1, k=15, pad=pad)   # the sentinel format codes 15 exponents
     ocb = oracle.calibrate(np.repeat(np.array([oracle.merge(0, e) for e in range(120, 136)], np.uint16),
                                      np.arange(16, 0, -1)))
     cb = uzip.codebook_from_hist(ocb.hist)
@@ -97,10 +108,11 @@ def test_sentinel_escape_counts(C):
     assert np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("pad", PADS)
 @pytest.mark.parametrize("C", [64, 1024, 8192])
-def test_fp8_escape_counts(C):
+def test_fp8_escape_counts(C, pad):
     rng = np.random.default_rng(C + 2)
-    mask = escape_mask(C + 2)
+    mask = escape_mask(C + 2, pad)
     n = mask.size
     a = rng.integers(0, 8, n)
     e = np.where(mask, rng.integers(16, 32, n), rng.integers(0, 16, n))
