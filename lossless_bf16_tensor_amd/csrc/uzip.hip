@@ -249,6 +249,17 @@ __device__ __forceinline__ void st_stream(T v, T *p)
 }
 
 // --------------------------------------------------------- bit helpers -----
+#ifndef UZIP_PLACE_NT
+#define UZIP_PLACE_NT 1
+#endif
+// Stores of the escape placement (non-temporal unless UZIP_PLACE_NT is 0).
+template <typename T>
+__device__ __forceinline__ void st_place(T v, T *p)
+{
+    if constexpr (UZIP_PLACE_NT != 0) st_stream(v, p);
+    else *p = v;
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     return __builtin_amdgcn_perm(hi, lo, sel);
@@ -984,7 +995,7 @@ __device__ __forceinline__ uint64_t edge_offset(uint64_t head, uint64_t tail0, u
 // Whole destination block k of a plan from source blocks lo = k, hi = k + 1.
 __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 lo, u32x4 hi)
 {
-    st_stream(q.r == 0 ? lo : extract16(lo, hi, q.r), q.d4 + k);
+    st_place(q.r == 0 ? lo : extract16(lo, hi, q.r), q.d4 + k);
 }
 
 // One wave per encode tile. Its escape prefix P = (group sums before the
@@ -1113,8 +1124,8 @@ __device__ __forceinline__ void place_direct(const EncWs &ws, uint8_t *__restric
     for (int r = 0; r < kDirectR; r++) {
         const uint32_t k = lane + 64u * r;
         if (k < m) {
-            if (p.posw) st_stream((uint16_t)ps[r], dpos + k);
-            st_stream((uint8_t)vs[r], dval + k);
+            if (p.posw) st_place((uint16_t)ps[r], dpos + k);
+            st_place((uint8_t)vs[r], dval + k);
         }
     }
 }
@@ -1133,7 +1144,7 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
     const ShiftPlan qp = shift_plan(out + p.off_pos + 2 * (uint64_t)P, (p.posw && m <= kPosListMax) ? 2 * (uint64_t)m : 0);
     if (qp.nblk) {                                  // a short list, from the prefetched bytes
         const u32x4 nxt = next_lane(ap);
-        if ((uint64_t)lane < qp.nblk) st_stream(qp.r == 0 ? ap : extract16(ap, nxt, qp.r), qp.d4 + lane);
+        if ((uint64_t)lane < qp.nblk) st_place(qp.r == 0 ? ap : extract16(ap, nxt, qp.r), qp.d4 + lane);
     }
     if (p.posw && m > (uint32_t)kPosListMax) {      // from the bitmap
         const uint32_t t0m = (uint32_t)(t0 & p.Cmask);
@@ -1168,7 +1179,7 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
                     for (uint32_t b = 2 * phantom; b < 16; b++)
                         dst[b] = (uint8_t)((b < 8 ? (b < 4 ? blk.x : blk.y) : (b < 12 ? blk.z : blk.w)) >> (8 * (b & 3)));
                 } else {
-                    st_stream(blk, reinterpret_cast<u32x4 *>(dst));
+                    st_place(blk, reinterpret_cast<u32x4 *>(dst));
                 }
             }
             const uint32_t left = ntot & 7u;        // entries of a partial last block
@@ -1196,7 +1207,7 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
     const uint64_t nreg = qv.nblk < 63 ? qv.nblk : 63;
     {
         const u32x4 nxt = next_lane(vp);
-        if ((uint64_t)lane < nreg) st_stream(qv.r == 0 ? vp : extract16(vp, nxt, qv.r), qv.d4 + lane);
+        if ((uint64_t)lane < nreg) st_place(qv.r == 0 ? vp : extract16(vp, nxt, qv.r), qv.d4 + lane);
     }
     // edge bytes: this lane's byte (lanes 0..31: a short position list's,
     // 32..63: the exponents'), from the prefetched bytes or else loaded
@@ -1286,8 +1297,8 @@ __device__ __forceinline__ void place_run(const EncWs &ws, uint8_t *__restrict__
         const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(m_l, j);
         const uint32_t P = (uint32_t)__builtin_amdgcn_readlane(P_l, j);
         if (m <= 64u && lane < m) {
-            if (p.posw) st_stream((uint16_t)e[j], dpos + P + lane);
-            st_stream((uint8_t)(e[j] >> 16), dval + P + lane);
+            if (p.posw) st_place((uint16_t)e[j], dpos + P + lane);
+            st_place((uint8_t)(e[j] >> 16), dval + P + lane);
         }
     }
     uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
