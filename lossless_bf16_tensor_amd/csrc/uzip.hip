@@ -2079,6 +2079,7 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     __shared__ uint32_t wtot[kEncThreads / 64];
     __shared__ EscBuf eb;
     __shared__ uint32_t s_lut[8];          // the 32 code-table bytes
+    __shared__ __attribute__((aligned(16))) uint8_t s_exb[kEncThreads * k8Vals];   // each lane's exponents
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t tile = blockIdx.x;
     const uint64_t t0 = tile * kEncTile;
@@ -2177,20 +2178,24 @@ __global__ __launch_bounds__(kEncThreads) void k8_encode_tile(const uint8_t *__r
     // positions listed for a tile with at most kPosListMax escapes, else the
     // tile's escape bitmap: this lane's 32 values are its bytes 4 tid..4 tid + 3
     const bool lst = m <= (uint32_t)kPosListMax;
-    if (!lst)
-        reinterpret_cast<uint32_t *>(ws.stage_aux + tile * kAux)[tid] =
-            flags_byte(c8[0].flags) | (flags_byte(c8[1].flags) << 8) | (flags_byte(c8[2].flags) << 16) |
-            (flags_byte(c8[3].flags) << 24);
-#pragma unroll
-    for (int q = 0; q < 8; q += 2) {               // 8 values per loop, in value order
-        uint32_t mask = c8[q / 2].flags;
-        while (mask) {
-            const uint32_t j = __builtin_ctz(mask) >> 2;       // value 4q + j
-            if (lst) eb.pos[rank] = (uint16_t)(g0m + 4 * q + j);
-            eb.val[rank] = (uint8_t)perm(E[q + 1], E[q], j);
-            rank++;
-            mask &= mask - 1;
-        }
+    // the lane's escape flags, bit j for value j
+    uint32_t fm = flags_byte(c8[0].flags) | (flags_byte(c8[1].flags) << 8) | (flags_byte(c8[2].flags) << 16) |
+                  (flags_byte(c8[3].flags) << 24);
+    if (!lst) reinterpret_cast<uint32_t *>(ws.stage_aux + tile * kAux)[tid] = fm;
+    // one loop over the lane's 32 values (as often as the wave's busiest
+    // lane has escapes), each exponent read back from the lane's own 32
+    // exponent bytes in LDS
+    if (fm) {
+        u32x4 *mine = reinterpret_cast<u32x4 *>(&s_exb[tid * k8Vals]);
+        mine[0] = u32x4{E[0], E[1], E[2], E[3]};
+        mine[1] = u32x4{E[4], E[5], E[6], E[7]};
+    }
+    while (fm) {
+        const uint32_t j = __builtin_ctz(fm);
+        if (lst) eb.pos[rank] = (uint16_t)(g0m + j);
+        eb.val[rank] = s_exb[tid * k8Vals + j];
+        rank++;
+        fm &= fm - 1;
     }
     stage_escapes<1, k8Vals>(m, cstart, t0, tile, ws, p, eb);
 }
