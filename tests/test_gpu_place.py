@@ -32,11 +32,12 @@ LAST = (5000, 100)             # the ragged last tile: values, escapes
 PADS = [0, 300]                # escape-free tiles added: 300 brings the average under 64
 
 
-def escape_mask(seed, pad=0):
+def escape_mask(seed, pad=0, extra=0):
     """A boolean mask over the whole input with COUNTS[i] escapes in tile i,
-    then `pad` tiles without escapes and the ragged last tile."""
+    then `pad` tiles without escapes (the first of them with `extra`) and
+    the ragged last tile."""
     rng = np.random.default_rng(seed)
-    counts = COUNTS + [0] * pad
+    counts = COUNTS + ([extra] + [0] * (pad - 1) if pad else [])
     n = TILE * len(counts) + LAST[0]
     mask = np.zeros(n, dtype=bool)
     for i, c in enumerate(counts + [LAST[1]]):
@@ -53,11 +54,11 @@ def escape_mask(seed, pad=0):
     return mask
 
 
-def bf16_input(seed, k=16, pad=0):
+def bf16_input(seed, k=16, pad=0, extra=0):
     """Words whose exponents are 120..120+k-1 (the codebook's) except at the
     mask's escapes (exponents 200..215)."""
     rng = np.random.default_rng(seed)
-    mask = escape_mask(seed, pad)
+    mask = escape_mask(seed, pad, extra)
     n = mask.size
     sm = rng.integers(0, 256, n).astype(np.uint16)
     e = np.where(mask, rng.integers(200, 216, n), rng.integers(120, 120 + k, n)).astype(np.uint16)
@@ -90,6 +91,22 @@ def test_bf16_escape_counts(C, pad):
     assert m == m_want
     compare(buf[:total].cpu().numpy(), oracle.encode(x, C, ocb.dec), f"bf16 C={C}")
     y = uzip.decode(buf, cb, x.size, C, in_bytes=total).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("extra", [33, 34])
+def test_bf16_at_the_run_threshold(extra):
+    # 285 tiles: M = 64 * 285 = 18,240 (the largest M placed in runs) and one more
+    x, hist, m_want = bf16_input(11, pad=252, extra=extra)
+    ntiles = (x.size + TILE - 1) // TILE
+    assert ntiles == 285 and m_want == 18207 + extra and (m_want <= 64 * ntiles) == (extra == 33)
+    ocb = oracle.top16(hist)
+    cb = uzip.codebook_from_hist(hist)
+    buf = uzip.encode(to_dev(x), cb, 1024)
+    total, m = uzip.stream_bytes(buf)
+    assert m == m_want
+    compare(buf[:total].cpu().numpy(), oracle.encode(x, 1024, ocb.dec), f"bf16 extra={extra}")
+    y = uzip.decode(buf, cb, x.size, 1024, in_bytes=total).cpu().numpy().view(np.uint16)
     assert np.array_equal(y, x)
 
 
