@@ -126,6 +126,9 @@ def cpu_baseline(x_np, calib_np, C, budget_s=12.0, sample=1 << 24):
         sp, rp, ep, dp, vp = timed(lambda: parallel.encode_parallel(xs, C, cb.dec, threads, pool),
                                    lambda s: parallel.decode_parallel(s, n, C, cb.dec, threads, pool))
     assert np.array_equal(sp, s1), "chunk-parallel oracle stream differs from the one-thread stream"
+    t0 = time.perf_counter()
+    oracle.histogram(xs)                                                 # calibration's first step, one thread
+    hist_gbps = 2 * n / (time.perf_counter() - t0) / 1e9
     m = int(np.frombuffer(s1[24:32].tobytes(), dtype="<u8")[0])         # header: M, then total bytes
     total = int(np.frombuffer(s1[32:40].tobytes(), dtype="<u8")[0])
     return {
@@ -136,7 +139,7 @@ def cpu_baseline(x_np, calib_np, C, budget_s=12.0, sample=1 << 24):
                   f"one thread: {r1} round trips, encode {e1:.4f} GB/s, decode {d1:.4f} GB/s",
         "encode_GBps": round(ep, 4), "decode_GBps": round(dp, 4),
         "one_thread": {"value": round(v1, 4), "encode_GBps": round(e1, 4), "decode_GBps": round(d1, 4),
-                       "cores": 1},
+                       "histogram_GBps": round(hist_gbps, 4), "cores": 1},
         "streams_identical": True,
         "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__,
         "sample_sha256": hashlib.sha256(xs.tobytes()).hexdigest()[:16],
@@ -263,8 +266,18 @@ def table(uzip, torch, reps=10, flush_mib=1024):
             t1 = time.perf_counter()
             oracle.decode(st, sample, C, ocb.dec)
             t2 = time.perf_counter()
+            oracle.histogram(xs_np)
+            t3 = time.perf_counter()
             row.update({"oracle_sample": sample, "oracle_encode_GBps": round(2 * sample / (t1 - t0) / 1e9, 4),
-                        "oracle_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4), "oracle_cores": 1})
+                        "oracle_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4),
+                        "oracle_histogram_GBps": round(2 * sample / (t3 - t2) / 1e9, 4), "oracle_cores": 1})
+            if len(xs) == 2:
+                # the oracle's fused reduce on the same sample of both inputs
+                stb = oracle.encode(np.ascontiguousarray(xs[1][:sample]), C, ocb.dec)
+                t4 = time.perf_counter()
+                oracle.reduce_add(st, stb, sample, C, ocb.dec)
+                t5 = time.perf_counter()
+                row["oracle_reduce_GBps_uncompressed_in"] = round(2 * 2 * sample / (t5 - t4) / 1e9, 4)
             print("TABLE " + json.dumps(row), flush=True)
             del out, ws, y
         del x

@@ -81,6 +81,7 @@ def test_cpu_baseline_leg():
     assert r["cores"] == min(16, len(os.sched_getaffinity(0))) and r["one_thread"]["cores"] == 1
     assert r["streams_identical"] is True
     assert r["value"] > 0 and r["one_thread"]["value"] > 0 and "65536 values" in r["sample"]
+    assert r["one_thread"]["histogram_GBps"] > 0
     # the round-trip rate is the harmonic combination of the two legs
     # (each figure is rounded to 4 decimals)
     assert r["value"] == pytest.approx(1 / (1 / r["encode_GBps"] + 1 / r["decode_GBps"]), abs=2e-4)
