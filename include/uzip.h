@@ -194,9 +194,10 @@ int uzip_encode_ex(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_c
  * that are rejected with UZIP_ESCRATCH before anything is enqueued. Every call
  * on one GPU uses that GPU's array, so calls that overlap on one GPU (two
  * streams, or two host threads) race and must be serialised by the caller.
- * The array keeps the last call's contents; the encode reads no workspace
- * byte it has not written in the same call. Output, arguments and the other
- * errors are those of uzip_encode (the device is the current one). */
+ * The array keeps the last call's contents; the result does not depend on
+ * them (the encode may load stale bytes past a tile's staged escapes, but
+ * never uses them). Output, arguments and the other errors are those of
+ * uzip_encode (the device is the current one). */
 #define UZIP_NOALLOC_SCRATCH_BYTES (64ull << 20)
 int uzip_encode_noalloc(const uint16_t *d_x, uint64_t n, uint32_t chunk, const uzip_codebook_t *cb,
                         void *d_out, uint64_t out_cap, hipStream_t s);
