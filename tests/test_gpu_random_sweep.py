@@ -8,8 +8,9 @@ mix and the stream's average lands on either side of the placement's run
 threshold. Every format the library encodes is checked against the oracle
 byte for byte (BF16, Top-15 + sentinel and Top-7 + zero-point where the chunk
 size allows them, Top-8 3-bit, FP8 E5M2), with the decode equal to the input;
-every third case adds the fused reduce of two such inputs and every fourth the
-k-input reduce of up to four.
+every fifth case adds online calibration (whole input or a block sample),
+every third the fused reduce of two such inputs and every fourth the k-input
+reduce of up to four.
 """
 import numpy as np
 import pytest
@@ -111,6 +112,22 @@ def test_random_case(case):
     t8, _ = uzip.stream_bytes(b8)
     compare(b8[:t8].cpu().numpy(), oracle.fp8_encode(x8, C, o8.dec), f"{label} fp8")
     assert np.array_equal(uzip.fp8_decode(b8, c8, n, C, in_bytes=t8).cpu().numpy(), x8), f"{label} fp8 decode"
+    if case % 5 == 0:
+        # online calibration: the whole input, or the first `sample` words of every `block`
+        if rng.random() < 0.5:
+            block = sample = 0
+            ocal = x
+        else:
+            block = int(8 * 2 ** rng.integers(0, 15))
+            sample = int(8 * rng.integers(1, block // 8 + 1))
+            ocal = oracle.sample_words(x, block, sample)
+        bo = uzip.encode_online(words_dev(x), C, block, sample)
+        to, _ = uzip.stream_bytes(bo)
+        compare(bo[:to].cpu().numpy(), oracle.encode(x, C, oracle.calibrate(ocal).dec),
+                f"{label} online block={block} sample={sample}")
+        rcb = uzip.codebook_from_dec(uzip.parse_header(bo[:256].cpu().numpy().tobytes())["dec"])
+        y = uzip.decode(bo, rcb, n, C, in_bytes=to).cpu().numpy().view(np.uint16)
+        assert np.array_equal(y, x), f"{label} online decode"
     if case % 3 == 0:
         xb = bf16_words(rng, n, escape_mask(rng, n))
         bb = uzip.encode(words_dev(xb), cb, C)
