@@ -1130,9 +1130,11 @@ __device__ __forceinline__ void place_direct(const EncWs &ws, uint8_t *__restric
     }
 }
 
+// buf: the wave's LDS position buffer (a pass plus the carried block); bm:
+// its 1 KiB LDS copy of a heavy tile's escape bitmap.
 __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
                                            uint64_t tile, uint32_t m, uint32_t P, uint64_t M, const PlaceIn &in,
-                                           uint16_t *buf)
+                                           uint16_t *buf, uint32_t *bm)
 {
     const int lane = threadIdx.x & 63;
     const uint64_t t0 = tile * kEncTile;
@@ -1152,13 +1154,14 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
         uint8_t *base = out + (d0 & ~15ull);        // destination of buffer entry 0
         const uint32_t phantom = (uint32_t)((d0 & 15u) >> 1);   // entries of the tile before
         uint32_t carry = phantom, done = 0;         // entries waiting at the buffer's start; blocks stored
+        // the bitmap to LDS once (16 bytes per lane), read a dword per lane and pass
+        reinterpret_cast<u32x4 *>(bm)[lane] = ap;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         for (int c = 0; c < kEncTile / kPassVals; c++) {
-            // this lane's 32 values: dword (lane & 3) of lane 16c + lane / 4
-            const int sl = 16 * c + (lane >> 2);
-            const uint32_t bx = __shfl(ap.x, sl, 64), by = __shfl(ap.y, sl, 64);
-            const uint32_t bz = __shfl(ap.z, sl, 64), bw = __shfl(ap.w, sl, 64);
-            const uint32_t q = (uint32_t)lane & 3u;
-            uint32_t bits = q == 0 ? bx : q == 1 ? by : q == 2 ? bz : bw;
+            // this lane's 32 values: dword 64c + lane of the bitmap
+            uint32_t bits = bm[64 * c + lane];
             const uint32_t cnt = __builtin_popcount(bits);
             const uint32_t inc = wave_inclusive_sum(cnt);
             const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane(inc, 63);
@@ -1346,6 +1349,7 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
 {
     // one buffer of positions per wave: a pass, plus the carried partial block
     __shared__ __attribute__((aligned(16))) uint16_t s_pos[kPlaceThreads / 64][kPassVals + 16];
+    __shared__ __attribute__((aligned(16))) uint32_t s_bm[kPlaceThreads / 64][kAux / 4];
     // wave-uniform values are moved to scalar registers (readfirstlane)
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1395,7 +1399,7 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
             place_direct(ws, out, p, tile, m, P, M, in);
         } else {
             place_load_blocks(ws, p, tile, m, in);
-            place_tile(ws, out, p, tile, m, P, M, in, s_pos[wv]);
+            place_tile(ws, out, p, tile, m, P, M, in, s_pos[wv], s_bm[wv]);
         }
         if (!light) place_offsets(out, p, tile, P, in);
     }
