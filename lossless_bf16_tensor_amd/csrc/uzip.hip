@@ -23,11 +23,13 @@
 //                   stages each tile's escapes (position, exponent) compactly
 //                   in the workspace.
 //   k_group_sums    sums the per-tile escape counts of each group of tiles.
-//   k_place_escapes one wave per tile: its escape prefix (group sums before
-//                   its group + tile counts before it in its group), then its
-//                   staged escapes -> final position and value slots by
-//                   16-byte shifted block copies, and the offsets of its
-//                   chunks. Tile 0 also writes the header, the last chunk
+//   k_place_escapes each wave takes a run of consecutive tiles: their escape
+//                   prefixes (group sums before their group + tile counts
+//                   before each in the group), the chunk offsets, and the
+//                   escapes of the tiles with few of them; a heavier tile's
+//                   staged escapes go to their final position and value
+//                   slots from a wave of its own, by 16-byte shifted block
+//                   copies. Wave 0 also writes the header, the last chunk
 //                   offset and the zero padding.
 //   k_decode_tile   one pass: 8-byte sign-mantissa loads, 4-byte code loads,
 //                   16-entry lookup in registers (v_perm). A tile with
@@ -998,11 +1000,13 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
     st_place(q.r == 0 ? lo : extract16(lo, hi, q.r), q.d4 + k);
 }
 
-// One wave per encode tile. Its escape prefix P = (group sums before the
-// tile's group) + (the tile's prefix inside its group). Every load goes out
-// in one first round: the count, the sums, the tile's chunk prefixes, and
-// the first KiB of each part of its staging slot (its position list or
-// bitmap, and its exponents; 16 bytes per lane). Then:
+// A tile with more than 64 escapes is placed by a wave of its own. Its
+// escape prefix P = (group sums before the tile's group) + (the tile's
+// prefix inside its group); the count, the sums and entry `lane` of its
+// staged list come in one first load round. With at most 64 * kDirectR
+// escapes it is written one escape per lane (place_direct); otherwise the
+// first KiB of each part of its staging slot (its position list or bitmap,
+// and its exponents; 16 bytes per lane) is loaded, and then:
 //  - positions, a tile with at most kPosListMax escapes: its list is all in
 //    the prefetched bytes. Each whole 16-byte destination block of pos[P..]
 //    is built from two lanes' bytes (a cross-lane read and a byte funnel)
@@ -1021,12 +1025,10 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
 //    each round issued before the stores of the round before it (a wait for
 //    a load also waits for every store issued before it).
 // Lanes 0..31 store a short list's edge bytes, lanes 32..63 the exponents'.
-// It writes the tile's chunk offsets. Tile 0's wave also writes the header,
-// offsets[nch] = M and every padding byte.
+// The tile's chunk offsets are written by the wave of its run (place_run).
 constexpr int kPassVals = 2048;                    // values per bitmap pass: 32 per lane
 static_assert(kEncTile % kPassVals == 0 && kAux == 16 * 64, "the slot's first KiB is 16 bytes per lane");
 static_assert(kEncTile >= 16 * 65, "placement reads at most 65 blocks past a round start");
-static_assert(kEncTile / 64 <= 128, "placement loads at most two chunk prefixes per lane");
 
 // Byte j (j < 1024) of the bytes held 16 per lane in pf (lane l: bytes
 // 16l..16l + 15); every lane must call it (cross-lane reads).
@@ -1051,12 +1053,12 @@ __device__ __forceinline__ u32x4 next_lane(u32x4 v)
 #ifndef UZIP_PLACE_LIGHT_T
 #define UZIP_PLACE_LIGHT_T 16
 #endif
-// When the escapes average at most kLightAvg per tile, one placement wave
-// takes kLightT consecutive tiles (the rest of the grid exits at once), so
-// that their escapes and chunk offsets go out from one wave in runs rather
-// than as short pieces from many; otherwise one wave takes one tile.
+// One placement wave takes a run of kLightT consecutive tiles: their chunk
+// offsets, and the escapes of those with at most 64, go out from one wave in
+// runs rather than as short pieces from many. A tile with more escapes is
+// placed by the wave of its own index; the other waves past the runs exit at
+// once.
 constexpr int kLightT = UZIP_PLACE_LIGHT_T;
-constexpr uint32_t kLightAvg = 64;
 static_assert(kLightT >= 1 && kLightT <= 64 && 64 % kLightT == 0, "a wave's tiles lie in one group of 2^gshift >= 64 tiles");
 #ifndef UZIP_PLACE_WAVES
 #define UZIP_PLACE_WAVES 4
@@ -1074,29 +1076,8 @@ static_assert(kDirectR >= 1 && 64 * kDirectR <= kPosListMax, "a directly placed 
 // What the first load round fetches for one tile.
 struct PlaceIn {
     u32x4 ap, vp;                                  // the slot's first KiB of each part, 16 bytes per lane
-    uint32_t cp[2];                                // in-tile prefixes of the chunks starting in the tile
     uint32_t dp, dv;                               // entry `lane` of the slot's position list and exponents
 };
-
-// The offsets of the chunks that start in a tile whose first escape goes to
-// global index P.
-__device__ __forceinline__ void place_offsets(uint8_t *__restrict__ out, const EncParams &p, uint64_t tile,
-                                              uint32_t P, const PlaceIn &in)
-{
-    const int lane = threadIdx.x & 63;
-    const uint64_t t0 = tile * kEncTile;
-    uint32_t *offs = reinterpret_cast<uint32_t *>(out + p.off_offs);
-    if (p.Cmask + 1 < (uint32_t)kEncTile) {
-        const uint64_t c0 = t0 >> p.logC;
-        uint64_t cn = (uint64_t)kEncTile >> p.logC;
-        if (c0 + cn > p.nch) cn = p.nch - c0;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-            if ((uint64_t)lane + 64 * i < cn) offs[c0 + lane + 64 * i] = P + in.cp[i];
-    } else if ((t0 & p.Cmask) == 0 && lane == 0) {
-        offs[t0 >> p.logC] = P;
-    }
-}
 
 // A tile with m <= 64 * kDirectR escapes (its positions listed in the slot,
 // when the format has them): escape k is written by lane k mod 64, its
@@ -1260,7 +1241,7 @@ __device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncPara
     if (16u * lane < need_v) in.vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
 }
 
-// One wave, nt <= kLightT consecutive tiles of one group (few escapes):
+// One wave, nt <= kLightT consecutive tiles of one group:
 // every tile's count, prefix and first 64 staged entries in one load round;
 // a tile with at most 64 escapes is stored from those (one with more is
 // placed by its own wave); the chunk offsets of all the tiles go out
@@ -1367,12 +1348,10 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
     // readlane returns a signed int: through uint32_t, so that an M of 2^31
     // or more is not sign-extended
     const uint64_t M = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
-    // With few escapes, wave w places the tiles of run w (kLightT tiles) that
-    // have at most 64 escapes and all their chunk offsets, and tile w if it
-    // has more; otherwise wave w places tile w.
-    const bool light = M <= (uint64_t)kLightAvg * p.ntiles;
-    const bool run = light && wave * kLightT < p.ntiles;
-    const bool own = wave < p.ntiles && (!light || m_own > 64u);
+    // Wave w places the tiles of run w (kLightT tiles) that have at most 64
+    // escapes and all their chunk offsets, and tile w if it has more.
+    const bool run = wave * kLightT < p.ntiles;
+    const bool own = wave < p.ntiles && m_own > 64u;
     if (!run && !own && wave != 0) return;
     if (run) {
         const uint64_t tile0 = wave * kLightT;
@@ -1382,15 +1361,6 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
     if (own) {
         const uint64_t tile = wave;
         PlaceIn in;
-        in.cp[0] = in.cp[1] = 0u;
-        if (!light && p.Cmask + 1 < (uint32_t)kEncTile) {
-            const uint64_t c0 = (tile * kEncTile) >> p.logC;
-            uint64_t cn = (uint64_t)kEncTile >> p.logC;
-            if (c0 + cn > p.nch) cn = p.nch - c0;
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-                if ((uint64_t)lane + 64 * j < cn) in.cp[j] = ws.chunk_pre[c0 + lane + 64 * j];
-        }
         in.dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
         in.dv = ws.stage_val[tile * kEncTile + lane];
         const uint32_t P = groups_before(ws, p, gs, tile >> p.gshift) + ws.tpre[tile];
@@ -1401,7 +1371,6 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
             place_load_blocks(ws, p, tile, m, in);
             place_tile(ws, out, p, tile, m, P, M, in, s_pos[wv], s_bm[wv]);
         }
-        if (!light) place_offsets(out, p, tile, P, in);
     }
     if (wave != 0) return;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);

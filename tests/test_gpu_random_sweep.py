@@ -3,9 +3,8 @@
 Each case draws n (log-uniform up to 3 million), a chunk size (a power of two
 in [64, 65536]) and, per 8192-word tile, an escape density from {0, 0.1 %,
 1 %, 5 %, 20 %, all} (escapes include zeros, subnormals, infinities and
-NaNs, so the reduces meet them too), so that light and heavy tiles sit side by side in every
-mix and the stream's average lands on either side of the placement's run
-threshold. Every format the library encodes is checked against the oracle
+NaNs, so the reduces meet them too), so that light and heavy tiles sit side
+by side in the placement's runs of consecutive tiles. Every format the library encodes is checked against the oracle
 byte for byte (BF16, Top-15 + sentinel and Top-7 + zero-point where the chunk
 size allows them, Top-8 3-bit, FP8 E5M2), with the decode equal to the input;
 every fifth case adds online calibration (whole input or a block sample),
