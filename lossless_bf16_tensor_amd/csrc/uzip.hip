@@ -1027,6 +1027,11 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
 // Lanes 0..31 store a short list's edge bytes, lanes 32..63 the exponents'.
 // The tile's chunk offsets are written by the wave of its run (place_run).
 constexpr int kPassVals = 2048;                    // values per bitmap pass: 32 per lane
+// With at least this many escapes a tile's exponents span more than 64 whole
+// 16-byte destination blocks wherever they start, so the copy's first round
+// past the prefetched KiB reads source blocks 63 + lane and 64 + lane.
+constexpr uint32_t kValPre = 16 * 64 + 30;
+static_assert(kEncTile >= 16 * 128, "the preloaded exponent blocks lie in the slot");
 static_assert(kEncTile % kPassVals == 0 && kAux == 16 * 64, "the slot's first KiB is 16 bytes per lane");
 static_assert(kEncTile >= 16 * 65, "placement reads at most 65 blocks past a round start");
 
@@ -1076,6 +1081,7 @@ static_assert(kDirectR >= 1 && 64 * kDirectR <= kPosListMax, "a directly placed 
 // What the first load round fetches for one tile.
 struct PlaceIn {
     u32x4 ap, vp;                                  // the slot's first KiB of each part, 16 bytes per lane
+    u32x4 bl, bh;                                  // exponent blocks 63 + lane and 64 + lane (m >= kValPre)
     uint32_t dp, dv;                               // entry `lane` of the slot's position list and exponents
 };
 
@@ -1202,9 +1208,10 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
     const uint32_t bp = byte_from_lanes(ap, jj), bv = byte_from_lanes(vp, jj);
     uint32_t eb = is_p ? bp : bv;
     if (!is_p && ej != ~0ull && ej >= (uint64_t)kAux) eb = src_v[ej];
-    // the rest of the exponents, 64 blocks per round from the slot
-    u32x4 blo = {}, bhi = {};
-    {
+    // the rest of the exponents, 64 blocks per round from the slot (the
+    // first round came with the slot's first KiB when m >= kValPre)
+    u32x4 blo = in.bl, bhi = in.bh;
+    if (m < kValPre) {
         const uint64_t k = nreg + lane;
         if (k < qv.nblk) {
             blo = sv4[k];
@@ -1236,9 +1243,30 @@ __device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncPara
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t need_a = p.posw ? (m <= (uint32_t)kPosListMax ? 2 * m : (uint32_t)kAux) : 0u;
     const uint32_t need_v = m < (uint32_t)kAux ? m : (uint32_t)kAux;
-    in.ap = in.vp = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 *sv4 = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile);
+    in.ap = in.vp = in.bl = in.bh = u32x4{0u, 0u, 0u, 0u};
     if (16u * lane < need_a) in.ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
-    if (16u * lane < need_v) in.vp = reinterpret_cast<const u32x4 *>(ws.stage_val + tile * kEncTile)[lane];
+    if (16u * lane < need_v) in.vp = sv4[lane];
+    if (m >= kValPre) {
+        in.bl = sv4[63 + lane];
+        in.bh = sv4[64 + lane];
+    }
+}
+
+// What a tile's own wave loads before it knows its prefix: the tile's
+// prefix in its group, and entry `lane` of its staged list and exponents or
+// the first KiB of each staged part.
+__device__ __forceinline__ void place_own_loads(const EncWs &ws, const EncParams &p, uint64_t tile, uint32_t m,
+                                                PlaceIn &in, uint32_t &tp)
+{
+    const uint32_t lane = threadIdx.x & 63;
+    tp = ws.tpre[tile];
+    if (m <= 64u * kDirectR) {
+        in.dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
+        in.dv = ws.stage_val[tile * kEncTile + lane];
+    } else {
+        place_load_blocks(ws, p, tile, m, in);
+    }
 }
 
 // One wave, nt <= kLightT consecutive tiles of one group:
@@ -1325,6 +1353,33 @@ __device__ __forceinline__ uint32_t groups_before(const EncWs &ws, const EncPara
     return (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(before), 63);
 }
 
+// The group sums, the first 256 of them 4 per lane in gs, and their total M.
+__device__ __forceinline__ uint64_t place_sums(const EncWs &ws, const EncParams &p, uint32_t gs[4])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint64_t q = (uint64_t)lane + 64 * i;
+        gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
+    }
+    uint32_t all = gs[0] + gs[1] + gs[2] + gs[3];
+    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) all += ws.gsum[q];
+    // readlane returns a signed int: through uint32_t, so that an M of 2^31
+    // or more is not sign-extended
+    return (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
+}
+
+// A tile with more than 64 escapes, from its own wave.
+__device__ __forceinline__ void place_own(const EncWs &ws, uint8_t *__restrict__ out, const EncParams &p,
+                                          uint64_t tile, uint32_t m, uint32_t P, uint64_t M, const PlaceIn &in,
+                                          uint16_t *buf, uint32_t *bm)
+{
+    if (m <= 64u * kDirectR)
+        place_direct(ws, out, p, tile, m, P, M, in);
+    else
+        place_tile(ws, out, p, tile, m, P, M, in, buf, bm);
+}
+
 __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8_t *__restrict__ out, EncParams p,
                                                                  HeaderParams hp)
 {
@@ -1335,42 +1390,36 @@ __global__ __launch_bounds__(kPlaceThreads) void k_place_escapes(EncWs ws, uint8
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t wave = (uint64_t)blockIdx.x * (kPlaceThreads / 64) + wv;
-    // ---- first round: the group sums (L2-resident) and the count of tile `wave`
-    uint32_t gs[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const uint64_t q = (uint64_t)lane + 64 * i;
-        gs[i] = q < p.ngroups ? ws.gsum[q] : 0u;
-    }
-    const uint32_t m_own = wave < p.ntiles ? ws.counts[wave] : 0u;
-    uint32_t all = gs[0] + gs[1] + gs[2] + gs[3];
-    for (uint64_t q = (uint64_t)lane + 256; q < p.ngroups; q += 64) all += ws.gsum[q];
-    // readlane returns a signed int: through uint32_t, so that an M of 2^31
-    // or more is not sign-extended
-    const uint64_t M = (uint32_t)__builtin_amdgcn_readlane(wave_inclusive_sum(all), 63);
     // Wave w places the tiles of run w (kLightT tiles) that have at most 64
-    // escapes and all their chunk offsets, and tile w if it has more.
-    const bool run = wave * kLightT < p.ntiles;
-    const bool own = wave < p.ntiles && m_own > 64u;
-    if (!run && !own && wave != 0) return;
-    if (run) {
+    // escapes and all their chunk offsets, and tile w if it has more. A wave
+    // past the runs reads its tile's count alone and, with a tile to place,
+    // issues that tile's loads together with the group sums'.
+    if (wave * kLightT >= p.ntiles) {
+        const uint32_t m = wave < p.ntiles ? ws.counts[wave] : 0u;
+        if (m <= 64u) return;
+        PlaceIn in;
+        uint32_t tp;
+        place_own_loads(ws, p, wave, m, in, tp);
+        uint32_t gs[4];
+        const uint64_t M = place_sums(ws, p, gs);
+        place_own(ws, out, p, wave, m, groups_before(ws, p, gs, wave >> p.gshift) + tp, M, in, s_pos[wv], s_bm[wv]);
+        return;
+    }
+    // ---- a run: the group sums (L2-resident) and the count of tile `wave`
+    uint32_t gs[4];
+    const uint32_t m_own = ws.counts[wave];
+    const uint64_t M = place_sums(ws, p, gs);
+    {
         const uint64_t tile0 = wave * kLightT;
         const uint32_t nt = (uint32_t)((p.ntiles - tile0 < (uint64_t)kLightT) ? p.ntiles - tile0 : (uint64_t)kLightT);
         place_run(ws, out, p, tile0, nt, groups_before(ws, p, gs, tile0 >> p.gshift), M);
     }
-    if (own) {
-        const uint64_t tile = wave;
+    if (m_own > 64u) {
         PlaceIn in;
-        in.dp = p.posw ? reinterpret_cast<const uint16_t *>(ws.stage_aux + tile * kAux)[lane] : 0u;
-        in.dv = ws.stage_val[tile * kEncTile + lane];
-        const uint32_t P = groups_before(ws, p, gs, tile >> p.gshift) + ws.tpre[tile];
-        const uint32_t m = m_own;
-        if (m <= 64u * kDirectR) {
-            place_direct(ws, out, p, tile, m, P, M, in);
-        } else {
-            place_load_blocks(ws, p, tile, m, in);
-            place_tile(ws, out, p, tile, m, P, M, in, s_pos[wv], s_bm[wv]);
-        }
+        uint32_t tp;
+        place_own_loads(ws, p, wave, m_own, in, tp);
+        place_own(ws, out, p, wave, m_own, groups_before(ws, p, gs, wave >> p.gshift) + tp, M, in, s_pos[wv],
+                  s_bm[wv]);
     }
     if (wave != 0) return;
     const uint64_t off_val = p.off_pos + (p.posw ? align256(2 * M) : 0);
