@@ -129,3 +129,43 @@ def test_fp8_escape_counts(C, pad):
     compare(buf[:total].cpu().numpy(), oracle.fp8_encode(x, C, ocb.dec), f"fp8 C={C}")
     y = uzip.fp8_decode(buf, cb, n, C, in_bytes=total).cpu().numpy()
     assert np.array_equal(y, x)
+
+
+def dirty(nbytes, fill, seed):
+    """A device buffer of nbytes holding `fill` in every byte, or random bytes
+    when fill is None."""
+    if fill is None:
+        rng = np.random.default_rng(seed)
+        return torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).to(DEV)
+    return torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, None])
+def test_dirty_workspace(fill):
+    # The placement loads staged bytes past a tile's escapes (each light
+    # tile's entry `lane`, whole 16-byte blocks at a list's end, the copy's
+    # first round of exponent blocks) but never uses them: streams written
+    # with a workspace and output buffer full of other bytes equal the
+    # oracle's, for encode and both reduces.
+    C = 1024
+    x, hist, _ = bf16_input(21, pad=40)
+    x2, _, _ = bf16_input(22, pad=40)
+    n = x.size
+    ocb = oracle.top16(hist)
+    cb = uzip.codebook_from_hist(hist)
+    wsb = uzip.workspace_bytes(n, C)
+    cap = uzip.max_bytes(n, C)
+    a = uzip.encode(to_dev(x), cb, C, out=dirty(cap, fill, 1), ws=dirty(wsb, fill, 2))
+    ta, _ = uzip.stream_bytes(a)
+    oa = oracle.encode(x, C, ocb.dec)
+    compare(a[:ta].cpu().numpy(), oa, f"encode fill={fill}")
+    b = uzip.encode(to_dev(x2), cb, C, out=dirty(cap, fill, 3), ws=dirty(wsb, fill, 4))
+    tb, _ = uzip.stream_bytes(b)
+    ob = oracle.encode(x2, C, ocb.dec)
+    compare(b[:tb].cpu().numpy(), ob, f"encode 2 fill={fill}")
+    r = uzip.reduce_add(a[:ta], b[:tb], cb, n, C, out=dirty(cap, fill, 5), ws=dirty(wsb, fill, 6))
+    tr, _ = uzip.stream_bytes(r)
+    compare(r[:tr].cpu().numpy(), oracle.reduce_add(oa, ob, n, C, ocb.dec), f"reduce_add fill={fill}")
+    rk = uzip.reduce_k([a[:ta], b[:tb], a[:ta]], cb, n, C, out=dirty(cap, fill, 7), ws=dirty(wsb, fill, 8))
+    tk, _ = uzip.stream_bytes(rk)
+    compare(rk[:tk].cpu().numpy(), oracle.reduce_k([oa, ob, oa], n, C, ocb.dec), f"reduce_k fill={fill}")
