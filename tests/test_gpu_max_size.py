@@ -226,6 +226,80 @@ def test_maximum_size_reduce():
     say("reduce checked")
 
 
+def test_maximum_size_reduce_k():
+    """The k-input reduce at n = 2^32 - 1 with three inputs of uniformly
+    random words (the sum's escapes number more than 2^31). Checked: the
+    output's M against a count over its decoded words, sampled chunks of the
+    output stream against the oracle's reduce of the same chunks of the
+    inputs, and 2^20 sampled sums against the oracle's in-order sums."""
+    k = 3
+    say(f"reduce_k k={k} n={N} C={C}: generating the inputs on the device")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(123)
+    xs = [torch.randint(-32768, 32768, (N,), dtype=torch.int16, device=DEV, generator=g) for _ in range(k)]
+    ocb = oracle.calibrate(*[x[: 1 << 20].cpu().numpy().view(np.uint16) for x in xs])
+    cb = uzip.codebook_from_hist(ocb.hist)
+    member = torch.zeros(256, dtype=torch.bool, device=DEV)
+    member[torch.from_numpy(ocb.dec.astype(np.int64)).to(DEV)] = True
+    nch = (N + C - 1) // C
+    chunks = (0, (1 << 31) // C - 1, (1 << 31) // C, nch - 1)
+    # the words the checks need, kept on the host before the inputs are freed
+    words = {c: [x[c * C:c * C + min(C, N - c * C)].cpu().numpy().view(np.uint16) for x in xs] for c in chunks}
+    idx = torch.randint(0, N, (1 << 20,), device=DEV, generator=g)
+    rows = np.stack([x[idx].cpu().numpy().view(np.uint16) for x in xs])
+
+    say("encode the inputs, reduce")
+    streams = []
+    for i in range(k):
+        si = uzip.encode(xs[i], cb, C)
+        streams.append(si[:uzip.stream_bytes(si)[0]])
+        xs[i] = None
+    del xs
+    torch.cuda.empty_cache()
+    out = uzip.reduce_k(streams, cb, N, C)
+    del streams
+    torch.cuda.empty_cache()
+    total, m = uzip.stream_bytes(out)
+    say(f"M={m} total={total}")
+    off_codes = 256 + A(N)
+    off_offs = off_codes + A((N + 1) // 2)
+    off_pos = off_offs + A(4 * (nch + 1))
+    off_val = off_pos + A(2 * m)
+    assert total == off_val + m
+    assert (1 << 31) < m < (1 << 32)
+
+    say("sampled chunks against the oracle's reduce")
+    for c in chunks:
+        lo = c * C
+        ln = min(C, N - lo)
+        mini = oracle.reduce_k([oracle.encode(w, C, ocb.dec) for w in words[c]], ln, C, ocb.dec)
+        sec = oracle.sections(mini)
+        sm = out[256 + lo:256 + lo + ln].cpu().numpy()
+        codes = out[off_codes + lo // 2:off_codes + lo // 2 + (ln + 1) // 2].cpu().numpy()
+        o = out[off_offs + 4 * c:off_offs + 4 * (c + 2)].cpu().numpy().view(np.uint32).astype(np.int64)
+        pos = out[off_pos + 2 * o[0]:off_pos + 2 * o[1]].cpu().numpy().view(np.uint16)
+        val = out[off_val + o[0]:off_val + o[1]].cpu().numpy()
+        assert np.array_equal(sm, sec["sm"]), f"chunk {c}: sign-mantissa bytes"
+        assert np.array_equal(codes, sec["codes"]), f"chunk {c}: codes"
+        assert np.array_equal(pos, sec["pos"]), f"chunk {c}: positions"
+        assert np.array_equal(val, sec["val"]), f"chunk {c}: exponents"
+
+    say("decode, M over the decoded sums, sampled sums against the oracle")
+    y = uzip.decode(out, cb, N, C, in_bytes=total)
+    del out
+    want_m = 0
+    step = 1 << 28
+    for i in range(0, N, step):
+        e = (y[i:i + step].to(torch.int32) >> 7) & 0xFF
+        want_m += int((~member[e.long()]).sum().item())
+    assert m == want_m
+    got = y[idx].cpu().numpy().view(np.uint16)
+    del y
+    torch.cuda.empty_cache()
+    assert np.array_equal(got, oracle.sum_words(rows))
+    say("reduce_k checked")
+
+
 @pytest.mark.parametrize("fmt,kept", [("s15", 15), ("z7", 7), ("t8", 8)])
 def test_maximum_size_ablation_formats(fmt, kept):
     """The ablation formats at n = 2^32 - 1 uniformly random words: the
