@@ -172,10 +172,13 @@ def make_flush(torch, dev, mib):
 def table(uzip, torch, reps=10, flush_mib=1024):
     """One JSON line per (config, chunk): encode/decode (and, for the
     gradient-reduce config, fused reduce) throughput, ratio, escape rate, and
-    the CPU oracle on a bounded sample. Every row is gated on a bit-exact
-    round trip."""
+    the CPU oracle on a bounded sample, on one thread and on every core.
+    Every row is gated on a bit-exact round trip."""
+    import concurrent.futures as cf
+
     import oracle
     import workloads
+    from oracle import parallel as oparallel
     dev = torch.device("cuda:0")
     flush = make_flush(torch, dev, flush_mib)   # evicts the Infinity Cache before each timed call
 
@@ -271,13 +274,30 @@ def table(uzip, torch, reps=10, flush_mib=1024):
             row.update({"oracle_sample": sample, "oracle_encode_GBps": round(2 * sample / (t1 - t0) / 1e9, 4),
                         "oracle_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4),
                         "oracle_histogram_GBps": round(2 * sample / (t3 - t2) / 1e9, 4), "oracle_cores": 1})
-            if len(xs) == 2:
-                # the oracle's fused reduce on the same sample of both inputs
-                stb = oracle.encode(np.ascontiguousarray(xs[1][:sample]), C, ocb.dec)
-                t4 = time.perf_counter()
-                oracle.reduce_add(st, stb, sample, C, ocb.dec)
-                t5 = time.perf_counter()
-                row["oracle_reduce_GBps_uncompressed_in"] = round(2 * 2 * sample / (t5 - t4) / 1e9, 4)
+            # the same sample with its chunks shared out over every core this
+            # process may use; the streams must equal the one-thread ones
+            threads = oparallel.default_threads()
+            with cf.ThreadPoolExecutor(threads) as pool:
+                t0 = time.perf_counter()
+                sp = oparallel.encode_parallel(xs_np, C, ocb.dec, threads, pool)
+                t1 = time.perf_counter()
+                yp = oparallel.decode_parallel(st, sample, C, ocb.dec, threads, pool)
+                t2 = time.perf_counter()
+                assert np.array_equal(sp, st) and np.array_equal(yp, xs_np), "all-core oracle differs"
+                row.update({"oracle_allcore_encode_GBps": round(2 * sample / (t1 - t0) / 1e9, 4),
+                            "oracle_allcore_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4),
+                            "oracle_allcore_cores": threads})
+                if len(xs) == 2:
+                    # the oracle's fused reduce on the same sample of both inputs
+                    stb = oracle.encode(np.ascontiguousarray(xs[1][:sample]), C, ocb.dec)
+                    t4 = time.perf_counter()
+                    r1 = oracle.reduce_add(st, stb, sample, C, ocb.dec)
+                    t5 = time.perf_counter()
+                    rp = oparallel.reduce_add_parallel(st, stb, sample, C, ocb.dec, threads, pool)
+                    t6 = time.perf_counter()
+                    assert np.array_equal(rp, r1), "all-core oracle reduce differs"
+                    row["oracle_reduce_GBps_uncompressed_in"] = round(2 * 2 * sample / (t5 - t4) / 1e9, 4)
+                    row["oracle_allcore_reduce_GBps_uncompressed_in"] = round(2 * 2 * sample / (t6 - t5) / 1e9, 4)
             print("TABLE " + json.dumps(row), flush=True)
             del out, ws, y
         del x

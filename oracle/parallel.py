@@ -21,7 +21,7 @@ import os
 
 import numpy as np
 
-from . import decode, encode, sections
+from . import decode, encode, reduce_add, sections
 
 
 def _a256(v: int) -> int:
@@ -134,3 +134,23 @@ def decode_parallel(stream, n: int, chunk: int, dec, threads: int | None = None,
     else:
         list(pool.map(one, bounds))
     return y
+
+
+def reduce_add_parallel(sa, sb, n: int, chunk: int, dec, threads: int | None = None, pool=None) -> np.ndarray:
+    """oracle.reduce_add(sa, sb, n, chunk, dec), with the chunks shared out
+    over threads: each thread cuts the same chunk range out of both streams
+    and reduces that pair of pieces; the results are joined."""
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    bounds = piece_bounds(n, chunk, threads or default_threads())
+
+    def one(b):
+        e0, e1 = b[0] * chunk, min(b[1] * chunk, n)
+        return reduce_add(split(sa, *b), split(sb, *b), e1 - e0, chunk, dec)
+
+    if pool is None:
+        with cf.ThreadPoolExecutor(len(bounds)) as p:
+            pieces = list(p.map(one, bounds))
+    else:
+        pieces = list(pool.map(one, bounds))
+    return join(pieces, n, chunk)

@@ -1,7 +1,8 @@
 """The chunk-parallel CPU baseline driver (oracle/parallel.py) is the same
 computation as the one-thread oracle: its joined stream equals the oracle's
-stream byte for byte, and its decode returns the input, for ragged sizes,
-every chunk size, all-escape input and more threads than chunks."""
+stream byte for byte, its decode returns the input, and its fused reduce
+equals the oracle's, for ragged sizes, every chunk size, all-escape input
+and more threads than chunks."""
 import numpy as np
 import pytest
 
@@ -53,3 +54,17 @@ def test_split_then_join_is_identity():
     for (c0, c1), p in zip(bounds, pieces):
         assert np.array_equal(p, oracle.encode(x[c0 * chunk:min(c1 * chunk, n)], chunk, cb.dec))
     assert np.array_equal(parallel.join(pieces, n, chunk), s)
+
+
+@pytest.mark.parametrize("n,chunk,threads", [
+    (1, 64, 4), (1000, 64, 7), (4097, 1024, 3), (200_003, 1024, 8), (65_536 * 3 + 5, 65_536, 5), (50_000, 256, 1),
+])
+def test_parallel_reduce_equals_oracle(n, chunk, threads):
+    a = _input(n, seed=2 * n + 1)
+    b = _input(n, seed=2 * n + 2, escapes=0.2)
+    cb = oracle.calibrate(a[: max(1, n // 4)], b[: max(1, n // 4)])
+    sa, sb = oracle.encode(a, chunk, cb.dec), oracle.encode(b, chunk, cb.dec)
+    want = oracle.reduce_add(sa, sb, n, chunk, cb.dec)
+    got = parallel.reduce_add_parallel(sa, sb, n, chunk, cb.dec, threads=threads)
+    assert got.size == want.size and np.array_equal(got, want)
+
