@@ -283,9 +283,13 @@ def table(uzip, torch, reps=10, flush_mib=1024):
                 t1 = time.perf_counter()
                 yp = oparallel.decode_parallel(st, sample, C, ocb.dec, threads, pool)
                 t2 = time.perf_counter()
+                hp = oparallel.histogram_parallel(xs_np, threads, pool)
+                t3 = time.perf_counter()
                 assert np.array_equal(sp, st) and np.array_equal(yp, xs_np), "all-core oracle differs"
+                assert np.array_equal(hp, oracle.histogram(xs_np)), "all-core oracle histogram differs"
                 row.update({"oracle_allcore_encode_GBps": round(2 * sample / (t1 - t0) / 1e9, 4),
                             "oracle_allcore_decode_GBps": round(2 * sample / (t2 - t1) / 1e9, 4),
+                            "oracle_allcore_histogram_GBps": round(2 * sample / (t3 - t2) / 1e9, 4),
                             "oracle_allcore_cores": threads})
                 if len(xs) == 2:
                     # the oracle's fused reduce on the same sample of both inputs

@@ -21,7 +21,7 @@ import os
 
 import numpy as np
 
-from . import decode, encode, reduce_add, sections
+from . import decode, encode, histogram, reduce_add, sections
 
 
 def _a256(v: int) -> int:
@@ -154,3 +154,19 @@ def reduce_add_parallel(sa, sb, n: int, chunk: int, dec, threads: int | None = N
     else:
         pieces = list(pool.map(one, bounds))
     return join(pieces, n, chunk)
+
+
+def histogram_parallel(x, threads: int | None = None, pool=None) -> np.ndarray:
+    """oracle.histogram(x), with x cut into one piece per thread: the pieces'
+    histograms are counted by the oracle and added."""
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+    parts = max(1, min(threads or default_threads(), x.size))
+    step = (x.size + parts - 1) // parts
+    pieces = [x[i:i + step] for i in range(0, x.size, step)] or [x]
+    if pool is None:
+        with cf.ThreadPoolExecutor(len(pieces)) as p:
+            hists = list(p.map(histogram, pieces))
+    else:
+        hists = list(pool.map(histogram, pieces))
+    return np.sum(hists, axis=0, dtype=np.uint64)
+

@@ -68,3 +68,9 @@ def test_parallel_reduce_equals_oracle(n, chunk, threads):
     got = parallel.reduce_add_parallel(sa, sb, n, chunk, cb.dec, threads=threads)
     assert got.size == want.size and np.array_equal(got, want)
 
+
+@pytest.mark.parametrize("n,threads", [(1, 4), (1000, 7), (200_003, 8), (65_536, 16)])
+def test_parallel_histogram_equals_oracle(n, threads):
+    x = _input(n, seed=3 * n + 1, escapes=0.3)
+    assert np.array_equal(parallel.histogram_parallel(x, threads=threads), oracle.histogram(x))
+
