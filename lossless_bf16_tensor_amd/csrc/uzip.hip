@@ -1917,9 +1917,6 @@ __device__ __forceinline__ void load_dense(const StreamIn &s, uint64_t t0, uint3
     }
 }
 
-#ifndef UZIP_RK_PIPE
-#define UZIP_RK_PIPE 0
-#endif
 constexpr int kRkThreads = kEncThreads;
 constexpr int kRkGroups = kEncTile / (kRkThreads * 8);
 static_assert(kRkThreads * kRkGroups * 8 == kEncTile && kRkGroups * (kRkThreads / 64) <= 16, "k-input reduce tile shape");
@@ -1948,42 +1945,10 @@ __global__ __launch_bounds__(kRkThreads) void k_reduce_k_tile(StreamSet ss, uint
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[k][q] = -0.0f;
     bool synced = false;                                // a barrier has published the code table
-#if UZIP_RK_PIPE
-    // pair 0's chunk offsets and dense bytes; each pair then issues the next
-    // pair's right after its own escape loads, so that they are in flight
-    // during its patch (whose barriers wait for LDS traffic only) and adds
-    PatchHead nh0 = patch_begin<kEncTile, kRkThreads>(ss.in[0], t0, dp), nh1 = nh0;
-    DenseIn<kRkThreads, kRkGroups> nd0, nd1;
-    load_dense(ss.in[0], t0, rem, dp, nd0);
-    nd1 = nd0;
-    if (ss.k > 1) {
-        nh1 = patch_begin<kEncTile, kRkThreads>(ss.in[1], t0, dp);
-        load_dense(ss.in[1], t0, rem, dp, nd1);
-    }
-    load_shared_lut(esh, ep.lut);
-#endif
     for (uint32_t i = 0; i < ss.k; i += 2) {
         const bool two = i + 1 < ss.k;                  // the same in every thread
         const StreamIn s0 = ss.in[i];
         const StreamIn s1 = ss.in[two ? i + 1 : i];
-#if UZIP_RK_PIPE
-        const PatchHead h0 = nh0, h1 = nh1;
-        const DenseIn<kRkThreads, kRkGroups> d0 = nd0, d1 = nd1;
-        const PatchFetch<kRedFetch> f0 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s0, t0, dp, h0);
-        PatchFetch<kRedFetch> f1 = f0;
-        f1.live = false;
-        if (two) f1 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1);
-        if (i + 2 < ss.k) {
-            const StreamIn n0 = ss.in[i + 2];
-            nh0 = patch_begin<kEncTile, kRkThreads>(n0, t0, dp);
-            load_dense(n0, t0, rem, dp, nd0);
-            if (i + 3 < ss.k) {
-                const StreamIn n1 = ss.in[i + 3];
-                nh1 = patch_begin<kEncTile, kRkThreads>(n1, t0, dp);
-                load_dense(n1, t0, rem, dp, nd1);
-            }
-        }
-#else
         const PatchHead h0 = patch_begin<kEncTile, kRkThreads>(s0, t0, dp);
         PatchHead h1 = h0;
         DenseIn<kRkThreads, kRkGroups> d0, d1;
@@ -1997,7 +1962,6 @@ __global__ __launch_bounds__(kRkThreads) void k_reduce_k_tile(StreamSet ss, uint
         PatchFetch<kRedFetch> f1 = f0;
         f1.live = false;
         if (two) f1 = patch_fetch<kEncTile, kRkThreads, kRedFetch>(s1, t0, dp, h1);
-#endif
         uint32_t e0[kRkGroups][2], e1[kRkGroups][2];
 #pragma unroll
         for (int k = 0; k < kRkGroups; k++) {
