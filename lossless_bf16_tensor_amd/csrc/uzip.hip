@@ -1002,11 +1002,13 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
 
 // A tile with more than 64 escapes is placed by a wave of its own. Its
 // escape prefix P = (group sums before the tile's group) + (the tile's
-// prefix inside its group); the count, the sums and entry `lane` of its
-// staged list come in one first load round. With at most 64 * kDirectR
-// escapes it is written one escape per lane (place_direct); otherwise the
-// first KiB of each part of its staging slot (its position list or bitmap,
-// and its exponents; 16 bytes per lane) is loaded, and then:
+// prefix inside its group). Once its count is known, the group sums, the
+// in-group prefix and the staged bytes it needs come in one load round:
+// with at most 64 * kDirectR escapes, entry `lane` of its staged list and
+// exponents, and the tile is written one escape per lane (place_direct);
+// otherwise the first KiB of each part of its staging slot (its position
+// list or bitmap, and its exponents; 16 bytes per lane) and, with at least
+// kValPre escapes, the exponent copy's first round of blocks; then:
 //  - positions, a tile with at most kPosListMax escapes: its list is all in
 //    the prefetched bytes. Each whole 16-byte destination block of pos[P..]
 //    is built from two lanes' bytes (a cross-lane read and a byte funnel)
@@ -1021,9 +1023,10 @@ __device__ __forceinline__ void put_block(const ShiftPlan &q, uint64_t k, u32x4 
 //    the tile before it, which are not written), and the at most 7 entries
 //    of a partial last block move to the buffer's start for the next pass;
 //  - exponents: like a short position list for the blocks within the
-//    prefetched KiB, then 64 blocks per round from the slot, the loads of
-//    each round issued before the stores of the round before it (a wait for
-//    a load also waits for every store issued before it).
+//    prefetched KiB, then 64 blocks per round from the slot (the first
+//    round preloaded as above), the loads of each round issued before the
+//    stores of the round before it (a wait for a load also waits for every
+//    store issued before it).
 // Lanes 0..31 store a short list's edge bytes, lanes 32..63 the exponents'.
 // The tile's chunk offsets are written by the wave of its run (place_run).
 constexpr int kPassVals = 2048;                    // values per bitmap pass: 32 per lane
@@ -1236,7 +1239,8 @@ __device__ __forceinline__ void place_tile(const EncWs &ws, uint8_t *__restrict_
 }
 
 // The first KiB of each staged part of a heavy tile (16 bytes per lane), as
-// far as its count says it is used.
+// far as its count says it is used, and with at least kValPre escapes the
+// exponent copy's first round of blocks past that KiB.
 __device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncParams &p, uint64_t tile, uint32_t m,
                                                   PlaceIn &in)
 {
@@ -1255,7 +1259,7 @@ __device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncPara
 
 // What a tile's own wave loads before it knows its prefix: the tile's
 // prefix in its group, and entry `lane` of its staged list and exponents or
-// the first KiB of each staged part.
+// (place_load_blocks) the first KiB of each staged part and more.
 __device__ __forceinline__ void place_own_loads(const EncWs &ws, const EncParams &p, uint64_t tile, uint32_t m,
                                                 PlaceIn &in, uint32_t &tp)
 {
