@@ -247,3 +247,18 @@ def test_config5_full_reduce():
     check_encode(B, 1024, cb, ocb, "config 5 B")
     print("config 5: inputs encoded", flush=True)
     check_reduce(A, B, 1024, cb, ocb, "config 5 reduce (2 x 2^29)")
+
+
+def test_worked_example_stream():
+    # the stream worked out by hand from the stream layout
+    # (tests/golden/stream_worked_example.txt), through the C-ABI
+    from test_oracle_format import CHUNK, WORDS, golden_hist, golden_stream
+    cb = uzip.codebook_from_hist(golden_hist())
+    want = golden_stream()
+    buf = uzip.encode(to_dev(WORDS), cb, CHUNK)
+    total, m = uzip.stream_bytes(buf)
+    assert (total, m) == (want.size, 1)
+    assert np.array_equal(buf[:total].cpu().numpy(), want)
+    y = uzip.decode(buf, cb, WORDS.size, CHUNK, in_bytes=total).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y, WORDS)
+    assert uzip.validate(buf[:total], cb) == 0

@@ -320,3 +320,18 @@ def test_noalloc_rejects_inputs_beyond_its_scratch_on_the_host():
         rc = L.uzip_encode_noalloc(None, n, C, ctypes.byref(cb), None, 0, None)
         assert rc == -6
         assert b"UZIP_NOALLOC_SCRATCH_BYTES" in L.uzip_strerror(rc)
+
+
+def test_host_side_reads_the_worked_example():
+    # the library's header parser and host validator on the stream worked
+    # out by hand from the stream layout
+    from test_oracle_format import CHUNK, WORDS, golden_hist, golden_stream
+    s = golden_stream()
+    cb = uzip.codebook_from_hist(golden_hist())
+    h = uzip.parse_header(s.tobytes())
+    assert h == {"n": WORDS.size, "chunk": CHUNK, "m": 1, "total_bytes": 1281,
+                 "dec": [127, 128, 0] + list(range(1, 14))}
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    bad = s.copy()
+    bad[1024] = 64                      # the escape's position past its chunk
+    assert uzip.validate_host(bad.tobytes(), cb) != 0
