@@ -102,3 +102,17 @@ def test_kv_cache_full():
     ocb = oracle.fp8_calibrate(w.calib)
     assert list(cb.dec) == ocb.dec.tolist()
     check(w.x, 1024, cb, ocb, "e5m2 kv cache 2^28")
+
+
+def test_worked_example_stream():
+    # the FP8 stream worked out by hand (tests/golden/stream_fp8_worked_example.txt)
+    from test_oracle_format import BYTES_FP8, CHUNK, GOLDEN_FP8, golden_stream
+    calib = np.repeat(np.array([0x3C, 0x40, 0x00], dtype=np.uint8), [10, 5, 3])
+    cb = uzip.codebook_from_hist(oracle.fp8_calibrate(calib).hist)
+    want = golden_stream(GOLDEN_FP8)
+    buf = uzip.fp8_encode(torch.from_numpy(BYTES_FP8).to(DEV), cb, CHUNK)
+    total, m = uzip.stream_bytes(buf)
+    assert (total, m) == (want.size, 1)
+    assert np.array_equal(buf[:total].cpu().numpy(), want)
+    y = uzip.fp8_decode(buf, cb, BYTES_FP8.size, CHUNK, in_bytes=total).cpu().numpy()
+    assert np.array_equal(y, BYTES_FP8)

@@ -335,3 +335,14 @@ def test_host_side_reads_the_worked_example():
     bad = s.copy()
     bad[1024] = 64                      # the escape's position past its chunk
     assert uzip.validate_host(bad.tobytes(), cb) != 0
+
+
+def test_host_validator_reads_the_fp8_worked_example():
+    from test_oracle_format import GOLDEN_FP8, golden_stream
+    s = golden_stream(GOLDEN_FP8)
+    calib = np.repeat(np.array([0x3C, 0x40, 0x00], dtype=np.uint8), [10, 5, 3])
+    cb = uzip.codebook_from_hist(oracle.fp8_calibrate(calib).hist)
+    assert uzip.validate_host(s.tobytes(), cb) == 0
+    bad = s.copy()
+    bad[1280] = 15                      # an escape whose exponent is in the codebook
+    assert uzip.validate_host(bad.tobytes(), cb) != 0

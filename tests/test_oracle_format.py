@@ -1,8 +1,9 @@
-"""The stream layout pinned by a stream worked out by hand
-(tests/golden/stream_worked_example.txt): five words, one escape, chunk 64.
-The oracle's stream must equal it byte for byte, and its decode must return
-the words. The GPU encode is checked against the same bytes in
-tests/test_gpu_parity.py."""
+"""The stream layout pinned by streams worked out by hand: five BF16 words
+with one escape (tests/golden/stream_worked_example.txt) and five FP8 E5M2
+values with one escape (tests/golden/stream_fp8_worked_example.txt), chunk
+64. The oracle's streams must equal them byte for byte, and its decodes must
+return the inputs. The GPU encodes are checked against the same bytes in
+tests/test_gpu_parity.py and tests/test_gpu_fp8.py."""
 import os
 
 import numpy as np
@@ -10,13 +11,15 @@ import numpy as np
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_worked_example.txt")
+GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "stream_fp8_worked_example.txt")
 WORDS = np.array([0x3F80, 0x4000, 0xBF80, 0x7F80, 0x0001], dtype=np.uint16)
+BYTES_FP8 = np.array([0x3C, 0x40, 0xBC, 0x7C, 0x01], dtype=np.uint8)
 CHUNK = 64
 
 
-def golden_stream():
+def golden_stream(path=GOLDEN):
     total, runs = None, []
-    for line in open(GOLDEN):
+    for line in open(path):
         line = line.split("#", 1)[0].strip()
         if not line:
             continue
@@ -50,3 +53,23 @@ def test_oracle_stream_equals_the_worked_example():
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
     assert np.array_equal(oracle.decode(want, WORDS.size, CHUNK, cb.dec), WORDS)
     assert oracle.validate(want, cb.dec) == 0
+
+
+def golden_hist_fp8():
+    h = np.zeros(32, dtype=np.uint64)
+    h[15], h[16], h[0] = 10, 5, 3
+    return h
+
+
+def test_oracle_fp8_stream_equals_the_worked_example():
+    calib = np.repeat(np.array([0x3C, 0x40, 0x00], dtype=np.uint8), [10, 5, 3])   # e 15, 16, 0
+    cb = oracle.fp8_calibrate(calib)
+    assert np.array_equal(cb.hist[:32], golden_hist_fp8())
+    assert cb.dec.tolist() == [15, 16, 0] + list(range(1, 14))
+    got = oracle.fp8_encode(BYTES_FP8, CHUNK, cb.dec)
+    want = golden_stream(GOLDEN_FP8)
+    assert got.size == want.size == 1281
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
+    assert np.array_equal(oracle.fp8_decode(want, BYTES_FP8.size, CHUNK, cb.dec), BYTES_FP8)
+    assert oracle.fp8_validate(want, cb.dec) == 0
+
