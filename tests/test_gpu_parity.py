@@ -262,3 +262,17 @@ def test_worked_example_stream():
     y = uzip.decode(buf, cb, WORDS.size, CHUNK, in_bytes=total).cpu().numpy().view(np.uint16)
     assert np.array_equal(y, WORDS)
     assert uzip.validate(buf[:total], cb) == 0
+
+
+@pytest.mark.parametrize("fmt", ["s15", "z7"])
+def test_worked_example_ablation_streams(fmt):
+    # the Top-15 + sentinel and Top-7 + zero-point streams worked out by hand
+    from test_oracle_format import CHUNK, GOLDEN_S15, GOLDEN_Z7, WORDS, golden_hist, golden_stream
+    cb = uzip.codebook_from_hist(golden_hist())
+    want = golden_stream({"s15": GOLDEN_S15, "z7": GOLDEN_Z7}[fmt])
+    buf = getattr(uzip, f"{fmt}_encode")(to_dev(WORDS), cb, CHUNK)
+    total, m = uzip.stream_bytes(buf)
+    assert (total, m) == (want.size, 1)
+    assert np.array_equal(buf[:total].cpu().numpy(), want)
+    y = getattr(uzip, f"{fmt}_decode")(buf, cb, WORDS.size, CHUNK, in_bytes=total).cpu().numpy().view(np.uint16)
+    assert np.array_equal(y, WORDS)

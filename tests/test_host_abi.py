@@ -346,3 +346,14 @@ def test_host_validator_reads_the_fp8_worked_example():
     bad = s.copy()
     bad[1280] = 15                      # an escape whose exponent is in the codebook
     assert uzip.validate_host(bad.tobytes(), cb) != 0
+
+
+def test_host_validator_reads_the_ablation_worked_examples():
+    from test_oracle_format import GOLDEN_S15, GOLDEN_Z7, golden_hist, golden_stream
+    cb = uzip.codebook_from_hist(golden_hist())
+    for path in (GOLDEN_S15, GOLDEN_Z7):
+        s = golden_stream(path)
+        assert uzip.validate_host(s.tobytes(), cb) == 0, path
+        bad = s.copy()
+        bad[-1] = 128                   # a stored exponent that is in the codebook
+        assert uzip.validate_host(bad.tobytes(), cb) != 0, path

@@ -1,17 +1,22 @@
 """The stream layout pinned by streams worked out by hand: five BF16 words
-with one escape (tests/golden/stream_worked_example.txt) and five FP8 E5M2
-values with one escape (tests/golden/stream_fp8_worked_example.txt), chunk
-64. The oracle's streams must equal them byte for byte, and its decodes must
+with one escape (tests/golden/stream_worked_example.txt), the same words in
+the Top-15 + sentinel and Top-7 + zero-point formats
+(stream_s15_worked_example.txt, stream_z7_worked_example.txt), and five FP8
+E5M2 values with one escape (tests/golden/stream_fp8_worked_example.txt),
+chunk 64. The oracle's streams must equal them byte for byte, and its decodes must
 return the inputs. The GPU encodes are checked against the same bytes in
 tests/test_gpu_parity.py and tests/test_gpu_fp8.py."""
 import os
 
 import numpy as np
+import pytest
 
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_worked_example.txt")
 GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "stream_fp8_worked_example.txt")
+GOLDEN_S15 = os.path.join(os.path.dirname(__file__), "golden", "stream_s15_worked_example.txt")
+GOLDEN_Z7 = os.path.join(os.path.dirname(__file__), "golden", "stream_z7_worked_example.txt")
 WORDS = np.array([0x3F80, 0x4000, 0xBF80, 0x7F80, 0x0001], dtype=np.uint16)
 BYTES_FP8 = np.array([0x3C, 0x40, 0xBC, 0x7C, 0x01], dtype=np.uint8)
 CHUNK = 64
@@ -72,4 +77,15 @@ def test_oracle_fp8_stream_equals_the_worked_example():
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
     assert np.array_equal(oracle.fp8_decode(want, BYTES_FP8.size, CHUNK, cb.dec), BYTES_FP8)
     assert oracle.fp8_validate(want, cb.dec) == 0
+
+
+@pytest.mark.parametrize("fmt,path", [("s15", GOLDEN_S15), ("z7", GOLDEN_Z7)])
+def test_oracle_ablation_streams_equal_the_worked_examples(fmt, path):
+    cb = oracle.top16(golden_hist())
+    got = getattr(oracle, f"{fmt}_encode")(WORDS, CHUNK, cb.dec)
+    want = golden_stream(path)
+    assert got.size == want.size
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
+    assert np.array_equal(getattr(oracle, f"{fmt}_decode")(want, WORDS.size, CHUNK, cb.dec), WORDS)
+    assert getattr(oracle, f"{fmt}_validate")(want, cb.dec) == 0
 
