@@ -276,3 +276,20 @@ def test_worked_example_ablation_streams(fmt):
     assert np.array_equal(buf[:total].cpu().numpy(), want)
     y = getattr(uzip, f"{fmt}_decode")(buf, cb, WORDS.size, CHUNK, in_bytes=total).cpu().numpy().view(np.uint16)
     assert np.array_equal(y, WORDS)
+
+
+def test_worked_example_reduce():
+    # the fused reduce worked out by hand (tests/golden/stream_reduce_worked_example.txt),
+    # through both reduce entry points
+    from test_oracle_format import CHUNK, GOLDEN_REDUCE, WORDS, WORDS_B, golden_hist, golden_stream
+    cb = uzip.codebook_from_hist(golden_hist())
+    want = golden_stream(GOLDEN_REDUCE)
+    a = uzip.encode(to_dev(WORDS), cb, CHUNK)
+    b = uzip.encode(to_dev(WORDS_B), cb, CHUNK)
+    ta, _ = uzip.stream_bytes(a)
+    tb, _ = uzip.stream_bytes(b)
+    for r in (uzip.reduce_add(a[:ta], b[:tb], cb, WORDS.size, CHUNK),
+              uzip.reduce_k([a[:ta], b[:tb]], cb, WORDS.size, CHUNK)):
+        total, m = uzip.stream_bytes(r)
+        assert (total, m) == (want.size, 1)
+        assert np.array_equal(r[:total].cpu().numpy(), want)

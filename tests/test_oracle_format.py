@@ -1,10 +1,11 @@
-"""The stream layout pinned by streams worked out by hand: five BF16 words
-with one escape (tests/golden/stream_worked_example.txt), the same words in
-the Top-15 + sentinel and Top-7 + zero-point formats
-(stream_s15_worked_example.txt, stream_z7_worked_example.txt), and five FP8
-E5M2 values with one escape (tests/golden/stream_fp8_worked_example.txt),
-chunk 64. The oracle's streams must equal them byte for byte, and its decodes must
-return the inputs. The GPU encodes are checked against the same bytes in
+"""The stream layouts pinned by streams worked out by hand, chunk 64: five
+BF16 words with one escape (tests/golden/stream_worked_example.txt), the
+same words in the Top-15 + sentinel and Top-7 + zero-point formats
+(stream_s15_worked_example.txt, stream_z7_worked_example.txt), five FP8
+E5M2 values with one escape (stream_fp8_worked_example.txt), and the fused
+reduce of the five BF16 words with five ones (stream_reduce_worked_example.txt).
+The oracle's streams must equal them byte for byte and its decodes return
+the inputs; the GPU paths are checked against the same bytes in
 tests/test_gpu_parity.py and tests/test_gpu_fp8.py."""
 import os
 
@@ -17,6 +18,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_worked_exampl
 GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "stream_fp8_worked_example.txt")
 GOLDEN_S15 = os.path.join(os.path.dirname(__file__), "golden", "stream_s15_worked_example.txt")
 GOLDEN_Z7 = os.path.join(os.path.dirname(__file__), "golden", "stream_z7_worked_example.txt")
+GOLDEN_REDUCE = os.path.join(os.path.dirname(__file__), "golden", "stream_reduce_worked_example.txt")
+WORDS_B = np.full(5, 0x3F80, dtype=np.uint16)
 WORDS = np.array([0x3F80, 0x4000, 0xBF80, 0x7F80, 0x0001], dtype=np.uint16)
 BYTES_FP8 = np.array([0x3C, 0x40, 0xBC, 0x7C, 0x01], dtype=np.uint8)
 CHUNK = 64
@@ -88,4 +91,16 @@ def test_oracle_ablation_streams_equal_the_worked_examples(fmt, path):
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
     assert np.array_equal(getattr(oracle, f"{fmt}_decode")(want, WORDS.size, CHUNK, cb.dec), WORDS)
     assert getattr(oracle, f"{fmt}_validate")(want, cb.dec) == 0
+
+
+def test_oracle_reduce_equals_the_worked_example():
+    cb = oracle.top16(golden_hist())
+    sa, sb = oracle.encode(WORDS, CHUNK, cb.dec), oracle.encode(WORDS_B, CHUNK, cb.dec)
+    want = golden_stream(GOLDEN_REDUCE)
+    for got in (oracle.reduce_add(sa, sb, WORDS.size, CHUNK, cb.dec),
+                oracle.reduce_k([sa, sb], WORDS.size, CHUNK, cb.dec)):
+        assert got.size == want.size
+        assert np.array_equal(got, want), np.nonzero(got != want)[0][:16].tolist()
+    sums = oracle.decode(want, WORDS.size, CHUNK, cb.dec)
+    assert sums.tolist() == [0x4000, 0x4040, 0x0000, 0x7F80, 0x3F80]
 
