@@ -4,7 +4,8 @@ The placement writes a tile's escapes either one per lane (light tiles) or
 as shifted 16-byte blocks from a position list or an escape bitmap (heavier
 tiles), and neighbouring tiles share the 16-byte blocks at their edges. Here
 consecutive 8192-value tiles carry escape counts on both sides of each
-boundary (0, 1, 63-65, 127-130, 255-257, 511-513, a few thousand, all), in
+boundary (0, 1, 63-65, 127-130, 255-257, 511-513, 1053-1055 where the
+exponent copy's first round is loaded ahead, a few thousand, all), in
 mixed order and with the escapes spread out, bunched at the tile's start or
 bunched at its end, plus a ragged last tile. Each placement wave writes the
 chunk offsets of a run of 16 consecutive tiles and the escapes of those with
@@ -26,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TILE = 8192
 COUNTS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 130, 1, 255, 256, 257, 511, 512, 513, 128, 129, 0,
-          1000, 64, 8192, 127, 3, 129, 4096, 128, 65, 512, 513, 7]
+          1000, 64, 8192, 127, 3, 129, 4096, 128, 65, 512, 513, 7, 1053, 1054, 1055, 5, 1054, 2047, 2048]
 LAST = (5000, 100)             # the ragged last tile: values, escapes
 
 
