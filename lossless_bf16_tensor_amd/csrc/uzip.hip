@@ -252,9 +252,11 @@ __device__ __forceinline__ void st_stream(T v, T *p)
 
 // --------------------------------------------------------- bit helpers -----
 #ifndef UZIP_PLACE_NT
-#define UZIP_PLACE_NT 1
+#define UZIP_PLACE_NT 0
 #endif
-// Stores of the escape placement (non-temporal unless UZIP_PLACE_NT is 0).
+// Stores of the escape placement: ordinary write-back stores (non-temporal
+// ones with UZIP_PLACE_NT = 1). The L2 merges the partial lines that
+// neighbouring tiles' waves write at their edges, so HBM sees each line once.
 template <typename T>
 __device__ __forceinline__ void st_place(T v, T *p)
 {
@@ -1251,9 +1253,11 @@ __device__ __forceinline__ void place_load_blocks(const EncWs &ws, const EncPara
     in.ap = in.vp = in.bl = in.bh = u32x4{0u, 0u, 0u, 0u};
     if (16u * lane < need_a) in.ap = reinterpret_cast<const u32x4 *>(ws.stage_aux + tile * kAux)[lane];
     if (16u * lane < need_v) in.vp = sv4[lane];
+    // only blocks that start before the last exponent (a whole destination
+    // block never takes bytes from a source block past it)
     if (m >= kValPre) {
-        in.bl = sv4[63 + lane];
-        in.bh = sv4[64 + lane];
+        if (16u * (63u + lane) < m) in.bl = sv4[63 + lane];
+        if (16u * (64u + lane) < m) in.bh = sv4[64 + lane];
     }
 }
 
