@@ -252,11 +252,13 @@ __device__ __forceinline__ void st_stream(T v, T *p)
 
 // --------------------------------------------------------- bit helpers -----
 #ifndef UZIP_PLACE_NT
-#define UZIP_PLACE_NT 0
+#define UZIP_PLACE_NT 1
 #endif
-// Stores of the escape placement: ordinary write-back stores (non-temporal
-// ones with UZIP_PLACE_NT = 1). The L2 merges the partial lines that
-// neighbouring tiles' waves write at their edges, so HBM sees each line once.
+// Stores of the escape placement: non-temporal (ordinary write-back stores
+// with UZIP_PLACE_NT = 0). Write-back stores make the kernel itself finish
+// sooner, but part of what it writes then stays dirty in the memory-side
+// cache and is written back during the next operation, which costs more
+// than it saved.
 template <typename T>
 __device__ __forceinline__ void st_place(T v, T *p)
 {
