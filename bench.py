@@ -530,6 +530,34 @@ def main():
     t_enc = float(np.mean(enc_list))
     t_dec = float(np.mean(dec_list))
     ab = algorithmic_bytes(n, C, m)
+
+    # --- work a call leaves behind: lines it leaves dirty in the memory-side
+    # cache are written back during the next operation, outside the call's
+    # own time (the encode's staging, written with ordinary stores so that
+    # the placement finds it in that cache). Measured as the extra time of a
+    # cache-evicting read right after one call, against the same read after
+    # another such read; the round-trip value above already includes it ---
+    def left_behind(call, reps=10):
+        if args.flush_mib <= 0:
+            return 0.0
+        t = {"clean": [], "after": []}
+        for r in range(reps + 2):
+            for what in ("clean", "after"):
+                flush()
+                call() if what == "after" else flush()
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ea.record()
+                flush()
+                eb.record()
+                torch.cuda.synchronize()
+                if r >= 2:
+                    t[what].append(ea.elapsed_time(eb))
+        return max(0.0, float(np.median(t["after"]) - np.median(t["clean"])))
+
+    behind = {"encode": left_behind(lambda: uzip.encode(x, cb, C, out=out, ws=ws)),
+              "decode": left_behind(lambda: uzip.decode(out, cb, n, C, out=y, in_bytes=total))}
+    op_frac_full = {"encode": ab["encode"] / ((t_enc + behind["encode"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "decode": ab["decode"] / ((t_dec + behind["decode"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     # roofline per op: each op's whole-call fraction and its dominant
     # (longest) kernel's own fraction; the line's roofline is the slower op's
     op_frac = {"encode": ab["encode"] / (t_enc * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -795,10 +823,15 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "encode_ms_stats": stats_ms(enc_list), "decode_ms_stats": stats_ms(dec_list),
         "op_roofline_frac": {k: round(v, 4) for k, v in op_frac.items()},
+        "left_behind_ms": {**{k: round(v, 4) for k, v in behind.items()},
+                           "what": "extra time of the next cache-evicting read after one call: the lines the call "
+                                   "left dirty in the memory-side cache, written back then (median of 10)"},
+        "op_roofline_frac_incl_left_behind": {k: round(v, 4) for k, v in op_frac_full.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dom), "algorithmic_bytes": ab[dom],
-                     "op": slow_op, "op_frac": round(op_frac[slow_op], 4)},
+                     "op": slow_op, "op_frac": round(op_frac[slow_op], 4),
+                     "op_frac_incl_left_behind": round(op_frac_full[slow_op], 4)},
         "roofline_ops": roofline_ops,
         "copy_kernel_GBps": {"value": round(copy_gbps, 1), "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                              "what": "torch copy_ of 1 GiB to 1 GiB (2 GiB moved), median of 5 after a cache-evicting read"},
